@@ -1,0 +1,181 @@
+"""Pins of the oracle's masked softmax attention (prefill and decode).
+
+References other than the oracle itself: a pure-Python triple loop with
+``math.exp``; PyTorch's float64 CPU scaled_dot_product_attention on the
+special cases where the Sep-Attention mask is the causal triangle or a
+sliding-window band; SciPy's softmax/logsumexp on the visible entries of a
+row; and invariants (weights sum to 1, outputs inside the convex hull of the
+visible values, invariance under a joint permutation of keys and mask
+columns).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import oracle
+
+
+def rand_case(rng, Hq, Hkv, S, D, a, n, p_sep):
+    q = rng.standard_normal((Hq, S, D))
+    k = rng.standard_normal((Hkv, S, D))
+    v = rng.standard_normal((Hkv, S, D))
+    flags = rng.random(S) < p_sep
+    return q, k, v, flags
+
+
+def loop_attention(q, k, v, flags, a, n, scale):
+    Hq, S, D = q.shape
+    G = Hq // k.shape[0]
+    out = np.zeros_like(q)
+    for h in range(Hq):
+        g = h // G
+        for i in range(S):
+            js = [j for j in range(i + 1) if j < a or i - j < n or flags[j]]
+            sc = [scale * sum(q[h, i, d] * k[g, j, d] for d in range(D)) for j in js]
+            m = max(sc)
+            e = [math.exp(x - m) for x in sc]
+            z = sum(e)
+            for d in range(D):
+                out[h, i, d] = sum(e[t] * v[g, js[t], d] for t in range(len(js))) / z
+    return out
+
+
+def test_triple_loop_brute_force():
+    rng = np.random.default_rng(21)
+    for (Hq, Hkv, S, D, a, n, ps) in [(2, 1, 17, 4, 2, 3, 0.3), (4, 2, 23, 3, 0, 1, 0.5),
+                                      (1, 1, 12, 5, 4, 20, 0.0), (2, 2, 19, 2, 1, 4, 1.0)]:
+        q, k, v, flags = rand_case(rng, Hq, Hkv, S, D, a, n, ps)
+        scale = 1.0 / math.sqrt(D)
+        M = oracle.sep_mask(flags, a, n)
+        o, _ = oracle.attention(q, k, v, M, scale)
+        assert np.allclose(o, loop_attention(q, k, v, flags, a, n, scale), atol=1e-12, rtol=0)
+
+
+def _sdpa(q, k, v, scale, causal=False, mask=None):
+    G = q.shape[0] // k.shape[0]
+    kk = torch.from_numpy(np.repeat(k, G, axis=0))
+    vv = torch.from_numpy(np.repeat(v, G, axis=0))
+    qq = torch.from_numpy(q)
+    am = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        qq, kk, vv, attn_mask=am, is_causal=causal, scale=scale).numpy()
+
+
+def test_long_window_is_causal_attention():
+    rng = np.random.default_rng(23)
+    for (Hq, Hkv, S, D) in [(4, 2, 64, 16), (2, 2, 96, 8), (8, 2, 33, 32)]:
+        q, k, v, flags = rand_case(rng, Hq, Hkv, S, D, 4, S, 0.2)
+        scale = 1 / math.sqrt(D)
+        o, _ = oracle.attention(q, k, v, oracle.sep_mask(flags, 4, S), scale)
+        assert np.allclose(o, _sdpa(q, k, v, scale, causal=True), atol=1e-12, rtol=0)
+
+
+def test_no_separators_no_initial_is_sliding_window():
+    rng = np.random.default_rng(29)
+    S, D = 80, 16
+    q, k, v, _ = rand_case(rng, 2, 1, S, D, 0, 1, 0.0)
+    for n in (1, 7, 33):
+        band = np.tri(S, S, 0, dtype=bool) & ~np.tri(S, S, -n, dtype=bool)
+        o, _ = oracle.attention(q, k, v, oracle.sep_mask(np.zeros(S, bool), 0, n), 0.25)
+        assert np.allclose(o, _sdpa(q, k, v, 0.25, mask=band), atol=1e-12, rtol=0)
+
+
+def test_weights_rows_sum_to_one_and_match_scipy():
+    rng = np.random.default_rng(31)
+    S, D, a, n = 70, 8, 3, 9
+    q, k, v, flags = rand_case(rng, 2, 1, S, D, a, n, 0.15)
+    M = oracle.sep_mask(flags, a, n)
+    o, lse, w = oracle.attention(q, k, v, M, 0.5, return_weights=True)
+    assert np.all(np.abs(w.sum(-1) - 1.0) < 1e-12)
+    assert np.all(w[:, ~M] == 0.0)
+    for h in range(2):
+        for i in range(S):
+            js = np.flatnonzero(M[i])
+            sc = 0.5 * (k[0, js] @ q[h, i])
+            assert np.allclose(w[h, i, js], softmax(sc), atol=1e-14, rtol=0)
+            assert abs(lse[h, i] - logsumexp(sc)) < 1e-12
+
+
+def test_outputs_in_convex_hull_of_visible_values():
+    rng = np.random.default_rng(37)
+    S, D, a, n = 90, 6, 4, 5
+    q, k, v, flags = rand_case(rng, 3, 1, S, D, a, n, 0.1)
+    q *= 4.0  # sharp softmax
+    M = oracle.sep_mask(flags, a, n)
+    o, _ = oracle.attention(q, k, v, M, 1.0)
+    for i in range(S):
+        vis = v[0, M[i]]
+        assert np.all(o[:, i] <= vis.max(0) + 1e-12) and np.all(o[:, i] >= vis.min(0) - 1e-12)
+
+
+def test_joint_key_permutation_invariance():
+    rng = np.random.default_rng(41)
+    S, D, a, n = 50, 8, 2, 6
+    q, k, v, flags = rand_case(rng, 2, 2, S, D, a, n, 0.2)
+    M = oracle.sep_mask(flags, a, n)
+    o, _ = oracle.attention(q, k, v, M, 0.3)
+    perm = rng.permutation(S)
+    # permute keys/values and mask columns only (queries stay in place)
+    o2 = np.empty_like(o)
+    for h in range(2):
+        x = 0.3 * q[h] @ k[h][perm].T
+        x[~M[:, perm]] = -np.inf
+        o2[h] = softmax(x, axis=1) @ v[h][perm]
+    assert np.allclose(o, o2, atol=1e-12, rtol=0)
+
+
+def test_attention_rows_equals_full():
+    rng = np.random.default_rng(43)
+    S, D, a, n = 120, 16, 4, 10
+    q, k, v, flags = rand_case(rng, 4, 2, S, D, a, n, 0.1)
+    M = oracle.sep_mask(flags, a, n)
+    o, lse = oracle.attention(q, k, v, M, 0.25)
+    rows = [0, 1, 5, 63, 119]
+    o2, lse2 = oracle.attention_rows(q[:, rows], k, v, oracle.mask_rows(flags, a, n, rows), 0.25,
+                                     kv_head_of=[h // 2 for h in range(4)])
+    assert np.allclose(o[:, rows], o2, atol=1e-13, rtol=0)
+    assert np.allclose(lse[:, rows], lse2, atol=1e-13, rtol=0)
+
+
+def test_decode_over_full_prefix_is_causal_row():
+    rng = np.random.default_rng(47)
+    S, D = 40, 8
+    q, k, v, flags = rand_case(rng, 4, 2, S, D, 0, S, 0.0)
+    ref = _sdpa(q, k, v, 0.2, causal=True)
+    for t in (0, 1, 17, S - 1):
+        o, _ = oracle.decode_attention(q[:, t], k[:, :t + 1], v[:, :t + 1], 0.2)
+        assert np.allclose(o, ref[:, t], atol=1e-12, rtol=0)
+
+
+# ----------------------------------------------------------- planted mistakes
+def _mut_no_scale(q, k, v, M, scale):
+    return oracle.attention(q, k, v, M, 1.0)[0]
+
+
+def _mut_wrong_gqa(q, k, v, M, scale):
+    Hq = q.shape[0]
+    Hkv = k.shape[0]
+    out = np.empty_like(q)
+    for h in range(Hq):
+        g = h % Hkv                        # interleaved instead of grouped
+        x = scale * q[h] @ k[g].T
+        x[~M] = -np.inf
+        out[h] = softmax(x, axis=1) @ v[g]
+    return out
+
+
+def _mut_transposed_mask(q, k, v, M, scale):
+    Mt = M.T | np.eye(M.shape[0], dtype=bool)
+    return oracle.attention(q, k, v, Mt, scale)[0]
+
+
+@pytest.mark.parametrize("mutant", [_mut_no_scale, _mut_wrong_gqa, _mut_transposed_mask])
+def test_planted_attention_mistakes_fail_the_pin(mutant):
+    rng = np.random.default_rng(53)
+    q, k, v, flags = rand_case(rng, 4, 2, 14, 3, 2, 3, 0.3)
+    M = oracle.sep_mask(flags, 2, 3)
+    ref = loop_attention(q, k, v, flags, 2, 3, 1 / math.sqrt(3))
+    assert not np.allclose(mutant(q, k, v, M, 1 / math.sqrt(3)), ref, atol=1e-9)
