@@ -1,0 +1,237 @@
+/*
+ * sepattn.h - C ABI of the Sep-Attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Sep-Attention (SepLLM): a causal query i attends key j only when j is one of
+ * the first `a` tokens (initial tokens), or j is among the `n` most recent
+ * positions (0 <= i - j < n, the neighbouring window), or token j is a
+ * separator, i.e. its id belongs to a given separator id set. Streaming
+ * inference keeps a four-block KV cache (initial / separator / past window /
+ * local window) and compacts the overflowing past window down to its
+ * separators.
+ *
+ * Sources (web pages on SepLLM):
+ *   [P1] "HKUDS047: SepLLM 作为 Long-Context Compression、KV Cache Efficiency 与
+ *        Research OS Memory Compression Layer" - sections "核心机制",
+ *        "SepCache", "Streaming-SepLLM", "KV Cache Manager",
+ *        "Streaming 参数约束", "SepAttention", "Flex Attention Kernel".
+ *   [P2] jieyibu.net SepLLM explainer - §1.2 (mask matrix, masked scaled
+ *        softmax) and §1.3 (the four cache blocks).
+ *   [P3] "用句号提速大模型？华为新算法SepLLM让AI推理快50%！" - §3.1 (kept
+ *        tokens) and §3.3 (four-block eviction table).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or synchronises, and keeps no mutable
+ *     global state. Tensors are dense, row-major, in the layouts stated, and
+ *     16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the null stream). Calls on one stream execute in order.
+ *   - Arguments are validated on the host before anything is launched. An
+ *     invalid argument returns a negative sep_status and enqueues nothing.
+ *     After enqueueing, a failed launch returns SEP_ERR_HIP. No exceptions
+ *     cross this boundary and nothing calls exit().
+ *   - Valid inputs cannot fail on the device: ids outside every separator
+ *     set are simply not separators.
+ *   - Names follow the pages: a = init_cache_size (= init_tok_max_idx + 1),
+ *     n = prefill/generate_local_window_size, s = sep_cache_size,
+ *     w = local_size, c = cache_size = a + s + p + w, with p the past window.
+ */
+#ifndef SEPATTN_H
+#define SEPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SEP_OK = 0,
+  SEP_ERR_NULL = -1,      /* a required pointer is NULL                    */
+  SEP_ERR_SHAPE = -2,     /* a size is out of range or inconsistent        */
+  SEP_ERR_PARAM = -3,     /* a, n, s, p, w, scale break the contract       */
+  SEP_ERR_DTYPE = -4,     /* dtype not supported by this entry point       */
+  SEP_ERR_WORKSPACE = -5, /* workspace missing or too small                */
+  SEP_ERR_HIP = -6,       /* the HIP runtime reported a launch failure     */
+  SEP_ERR_ALIGN = -7      /* a tensor pointer is not 16-byte aligned       */
+} sep_status;
+
+typedef enum { SEP_F32 = 0, SEP_BF16 = 1 } sep_dtype;
+
+/* Largest separator set accepted (ids are compared one by one). */
+#define SEP_MAX_SEP_IDS 64
+/* Largest S for which sep_mask_build writes the dense mask. */
+#define SEP_MAX_DENSE_S 8192
+
+/*
+ * sep_mask_build - separator flags, block classes and (optionally) the dense
+ * 0/1 mask of each sequence.  [P1 "Separator Tokens", "SepAttention"
+ * (build_prefill_mask); P2 §1.2 (mask matrix M); P1 "Flex Attention Kernel"
+ * (block-sparse map, the role of create_block_mask)]
+ *
+ *   ids        [B, S] int32   token ids.
+ *   sep_ids    [n_sep_ids] int32 device array, 0 <= n_sep_ids <= 64
+ *              (NULL allowed when n_sep_ids == 0; duplicates allowed).
+ *   a, n       initial-token count (a >= 0) and window (n >= 1).
+ *   is_sep     [B, S] uint8 out (required): 1 iff ids[b,j] is in sep_ids.
+ *   tile_class [B, ceil(S/tq), ceil(S/tk)] uint8 out, or NULL: for each
+ *              block of tq query rows x tk key columns, 0 = no pair visible,
+ *              1 = every pair visible, 2 = mixed. Edge blocks count only
+ *              rows/columns < S. tq, tk in [1, 4096] when tile_class != NULL.
+ *   dense_mask [B, S, S] uint8 out, or NULL: M[b,i,j] = 1 iff j <= i and
+ *              (j < a or i - j < n or is_sep[b,j]). Requires S <= 8192.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_HIP.
+ */
+int sep_mask_build(const int32_t* ids, int B, int S, const int32_t* sep_ids, int n_sep_ids,
+                   int a, int n, uint8_t* is_sep, uint8_t* tile_class, int tq, int tk,
+                   uint8_t* dense_mask, hipStream_t stream);
+
+/*
+ * sep_index_compact - prefix-sum stream compaction of the separator flags.
+ * [P1 "KV Cache Manager" (compress_past_win_2_seps keeps the separator
+ * entries of a window, in order); P3 §3.3 (the past window keeps only its
+ * separators)]
+ *
+ *   is_sep  [B, S] uint8 (0/1; any non-zero byte counts as 1).
+ *   rank    [B, S+1] int32 out: rank[b,j] = number of separators at
+ *           positions < j; rank[b,S] is the separator count.
+ *   sep_pos [B, S] int32 out: sep_pos[b,r] = position of the r-th separator
+ *           in increasing order for r < count; -1 for r >= count.
+ *   count   [B] int32 out, or NULL.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_HIP.
+ */
+int sep_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank, int32_t* sep_pos,
+                      int32_t* count, hipStream_t stream);
+
+/*
+ * sep_attn_prefill - Sep-Attention over a whole sequence.  [P2 §1.2 (scores
+ * scaled, masked entries set to -inf, softmax, weighted sum of V); P1
+ * "SepAttention" (initial OR window OR separator, AND causal); P1
+ * "Flex Attention Kernel" (only a kernel that sees the sparsity saves work)]
+ *
+ *   q        [B, Hq, S, D]; k, v [B, Hkv, S, D]; dtype SEP_BF16 or SEP_F32
+ *            (the same for q, k, v and out). Query head h reads key/value
+ *            head h / (Hq / Hkv). Hq % Hkv == 0, Hq / Hkv <= 16, D in {64, 128}.
+ *   is_sep   [B, S] uint8 from sep_mask_build.
+ *   rank     [B, S+1], sep_pos [B, S] int32 from sep_index_compact on the
+ *            same is_sep.
+ *   a >= 0, n >= 1; scale > 0 multiplies q.k (1/sqrt(D) is the usual value).
+ *   out      [B, Hq, S, D] out, same dtype as q.
+ *   lse      [B, Hq, S] float32 out, or NULL: natural-log softmax
+ *            normaliser (row max + log of the row sum of exponentials).
+ * Arithmetic: fp32 accumulation and online softmax; in bf16 mode the
+ * softmax weights are rounded to bf16 for the P.V product.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                     int Hkv, int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                     const int32_t* sep_pos, int a, int n, float scale, void* out, float* lse,
+                     hipStream_t stream);
+
+/*
+ * sep_cache - a batch of four-block KV caches in caller-owned device memory.
+ * [P2 §1.3 and P3 §3.3 (initial / separator / past window / local window);
+ * P1 "SepCache" (parameter names)]
+ *
+ * Slot layout per sequence, c = a + s + p + w slots:
+ *   [0, a)       initial block: position x < a lives in slot x.
+ *   [a, a+s)     separator ring (FIFO, cap s).
+ *   [a+s, c)     recent ring R = past window ++ local window (cap p + w):
+ *                position x >= a lives in slot a + s + (x - a) mod (p + w).
+ * Device arrays:
+ *   k, v   [B, Hkv, c, D] in `dtype`.
+ *   pos    [B, c] int32: absolute position held by each slot, -1 if empty.
+ *   tok    [B, c] int32: token id held by each slot, -1 if empty.
+ *   state  [B, 4] int64 per sequence:
+ *          [0] n_seen        tokens inserted so far (t);
+ *          [1] n_compact     compactions so far (K); the compacted prefix
+ *                            is [a, a + K (p + 1)) and R holds
+ *                            positions [a + K (p + 1), t);
+ *          [2] sep_head      separator-ring slot the next separator takes;
+ *          [3] sep_count     separators held (<= s).
+ *          The ring's entries, oldest first, are the slots
+ *          a + (sep_head - sep_count + i) mod s, i = 0 .. sep_count-1.
+ * An empty cache is state all zero and pos/tok all -1 (sep_cache_reset).
+ * K/V rows of empty slots are never read.
+ * Contract [P1 "Streaming 参数约束"]: a >= 0, w >= 1, and either s >= 1 and
+ * p >= 1 (SepLLM: a + s + w < c) or s == 0 and p == 0 (StreamingLLM: the
+ * local window is c - a).
+ */
+typedef struct {
+  int32_t a, s, p, w;
+  int32_t B, Hkv, D, dtype;
+  void* k;
+  void* v;
+  int32_t* pos;
+  int32_t* tok;
+  int64_t* state;
+} sep_cache;
+
+/*
+ * sep_cache_reset - make every sequence of the cache empty (state = 0,
+ * pos = tok = -1). K/V contents are left as they are.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_HIP.
+ */
+int sep_cache_reset(const sep_cache* cache, hipStream_t stream);
+
+/*
+ * sep_cache_update - append T tokens to every sequence of the cache.
+ * [P1 "KV Cache Manager" (compress_past_win_2_seps, keep the last
+ * sep_cache_size separators, K/V and token ids move together); P3 §3.3
+ * (initial fixed; local window overflows into the past window; a full past
+ * window keeps its separators and drops the rest; the separator cache
+ * evicts its oldest entry beyond s)]
+ *
+ *   k_new, v_new [B, Hkv, T, D] in cache->dtype; ids_new [B, T] int32.
+ *   sep_ids [n_sep_ids] int32 device array (0..64 ids).
+ * Rule, per token (positions t = n_seen, n_seen+1, ...): if fewer than a
+ * tokens are held in the initial block, the token goes there. Otherwise it
+ * joins R; when R would hold p + w + 1 entries, its oldest p + 1 entries are
+ * compacted first: each separator among them, oldest first, is copied into
+ * the separator ring (overwriting the oldest entry once the ring holds s),
+ * the rest are dropped. T > 1 gives exactly the state of T calls with T = 1.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_cache_update(const sep_cache* cache, const void* k_new, const void* v_new,
+                     const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep_ids,
+                     hipStream_t stream);
+
+/*
+ * sep_attn_decode - one decode step of Sep-Attention over the cache.
+ * [P1 "SepAttention" (build_generate_mask: the same keep rule for one query);
+ * P1 "Streaming-SepLLM" (each token: forward with the cache, then update
+ * and compress); P2 §1.3 (only the retained KV are read)]
+ *
+ *   q      [B, Hq, D] in cache->dtype (SEP_BF16 only).
+ *   k_new, v_new [B, Hkv, D]: the current token's key/value. It attends the
+ *          cache as it is (tokens before it) plus itself; call
+ *          sep_cache_update afterwards to insert it.
+ *   scale  > 0; out [B, Hq, D] (bf16); lse [B, Hq] float32 out or NULL.
+ *   ws     device workspace of at least sep_decode_workspace_bytes(...)
+ *          bytes, zero-filled before its first use; every call leaves it
+ *          zero-filled again. Calls that overlap in time must not share it.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_WORKSPACE, SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
+                    int Hq, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Workspace bytes sep_attn_decode needs for this cache shape and Hq. */
+size_t sep_decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D);
+
+/* Static description of a status code. */
+const char* sep_status_string(int status);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int sep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEPATTN_H */

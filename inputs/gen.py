@@ -16,6 +16,8 @@ exactly.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Sequence
 
 import numpy as np
@@ -114,10 +116,40 @@ def prefill_ids(cfg, b: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- tensors
+BLOCK_ROWS = 16384
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def normal_rows(seed: int, key: Sequence[int], rows: int, D: int, dtype: str) -> np.ndarray:
-    """rows x D values ~ N(0,1) in float64, rounded once to the storage dtype."""
-    x = _rng(seed, *key).standard_normal((rows, D))
-    return round_storage(x, dtype)
+    """rows x D values ~ N(0,1) in float64, rounded once to the storage dtype.
+
+    Rows come in blocks of BLOCK_ROWS; block j is drawn from its own stream
+    seeded by (seed, *key, j), so blocks are generated in parallel threads
+    and the result does not depend on the thread count."""
+    st = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((rows, D), dtype=st)
+    nblk = -(-rows // BLOCK_ROWS)
+
+    def fill(j):
+        r0 = j * BLOCK_ROWS
+        r1 = min(rows, r0 + BLOCK_ROWS)
+        x = _rng(seed, *key, j).standard_normal((r1 - r0, D))
+        out[r0:r1] = round_storage(x, dtype)
+
+    if nblk <= 1:
+        for j in range(nblk):
+            fill(j)
+    else:
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out
 
 
 def prefill_head(cfg, b: int, tag: int, h: int) -> np.ndarray:

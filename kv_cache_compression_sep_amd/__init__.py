@@ -1,0 +1,218 @@
+"""Sep-Attention hot path for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libsepattn.so`` (C ABI in ``include/sepattn.h``). The
+functions carry the C entry points' names and take PyTorch tensors on the
+GPU; the binding only checks tensor properties, allocates outputs when the
+caller does not pass them, and hands raw pointers and the current HIP
+stream to the library. All computation happens in the HIP kernels.
+
+    is_sep, tiles, dense = sep_mask_build(ids, sep_ids, a, n, ...)
+    rank, sep_pos, count = sep_index_compact(is_sep)
+    out, lse             = sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a, n)
+    cache = SepCache(B, Hkv, D, a, s, p, w)     # four-block KV cache
+    o, lse = sep_attn_decode(q, k_new, v_new, cache)
+    sep_cache_update(cache, k_new, v_new, ids_new, sep_ids)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
+
+__all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_decode",
+           "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version"]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return SEP_BF16
+    if t.dtype == torch.float32:
+        return SEP_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def library_version() -> int:
+    return _lib.load().sep_version()
+
+
+def sep_mask_build(ids, sep_ids, a: int, n: int, *, is_sep=None, tiles: tuple | None = None,
+                   tile_class=None, dense: bool = False, dense_mask=None):
+    """Separator flags [B,S] u8; optional tile classes for ``tiles=(tq, tk)``
+    and the dense mask [B,S,S] u8 (S <= 8192)."""
+    lib = _lib.load()
+    _need(ids, "ids", torch.int32, 2)
+    _need(sep_ids, "sep_ids", torch.int32, 1)
+    B, S = ids.shape
+    dev = ids.device
+    if is_sep is None:
+        is_sep = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    tq = tk = 0
+    if tiles is not None:
+        tq, tk = tiles
+        if tile_class is None:
+            tile_class = torch.empty((B, -(-S // tq), -(-S // tk)), dtype=torch.uint8, device=dev)
+    if dense and dense_mask is None:
+        dense_mask = torch.empty((B, S, S), dtype=torch.uint8, device=dev)
+    code = lib.sep_mask_build(ids.data_ptr(), B, S, _ptr(sep_ids) if sep_ids.numel() else None,
+                              sep_ids.numel(), a, n, is_sep.data_ptr(), _ptr(tile_class), tq, tk,
+                              _ptr(dense_mask), _stream())
+    _lib.check("sep_mask_build", code)
+    return is_sep, tile_class, dense_mask
+
+
+def sep_index_compact(is_sep, *, rank=None, sep_pos=None, count=None):
+    """rank [B,S+1] i32, sep_pos [B,S] i32, count [B] i32."""
+    lib = _lib.load()
+    _need(is_sep, "is_sep", torch.uint8, 2)
+    B, S = is_sep.shape
+    dev = is_sep.device
+    rank = torch.empty((B, S + 1), dtype=torch.int32, device=dev) if rank is None else rank
+    sep_pos = torch.empty((B, S), dtype=torch.int32, device=dev) if sep_pos is None else sep_pos
+    count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
+    code = lib.sep_index_compact(is_sep.data_ptr(), B, S, rank.data_ptr(), sep_pos.data_ptr(),
+                                 count.data_ptr(), _stream())
+    _lib.check("sep_index_compact", code)
+    return rank, sep_pos, count
+
+
+def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: float | None = None, *,
+                     out=None, return_lse: bool = False, lse=None):
+    """Sep-Attention prefill: q [B,Hq,S,D], k/v [B,Hkv,S,D] (bf16 or fp32)."""
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, None, 4)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError("k/v must be [B, Hkv, S, D] matching q")
+    _need(is_sep, "is_sep", torch.uint8, 2)
+    _need(rank, "rank", torch.int32, 2)
+    _need(sep_pos, "sep_pos", torch.int32, 2)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    code = lib.sep_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, Hq,
+                                Hkv, S, D, is_sep.data_ptr(), rank.data_ptr(), sep_pos.data_ptr(),
+                                a, n, float(scale), out.data_ptr(), _ptr(lse), _stream())
+    _lib.check("sep_attn_prefill", code)
+    return (out, lse) if return_lse else out
+
+
+class SepCache:
+    """A batch of four-block caches in device memory (layout: see sep_cache
+    in include/sepattn.h). Also owns the decode workspace."""
+
+    def __init__(self, B: int, Hkv: int, D: int, a: int, s: int, p: int, w: int,
+                 dtype=torch.bfloat16, device="cuda", Hq: int | None = None):
+        self.B, self.Hkv, self.D = B, Hkv, D
+        self.a, self.s, self.p, self.w = a, s, p, w
+        self.c = a + s + p + w
+        self.dtype = dtype
+        dev = torch.device(device)
+        self.k = torch.zeros((B, Hkv, self.c, D), dtype=dtype, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.pos = torch.full((B, self.c), -1, dtype=torch.int32, device=dev)
+        self.tok = torch.full((B, self.c), -1, dtype=torch.int32, device=dev)
+        self.state = torch.zeros((B, 4), dtype=torch.int64, device=dev)
+        self._ws = None
+        self._ws_hq = None
+        if Hq is not None:
+            self.workspace(Hq)
+
+    def struct(self) -> _lib.SepCacheStruct:
+        return _lib.SepCacheStruct(self.a, self.s, self.p, self.w, self.B, self.Hkv, self.D,
+                                   _dtype_code(self.k), self.k.data_ptr(), self.v.data_ptr(),
+                                   self.pos.data_ptr(), self.tok.data_ptr(), self.state.data_ptr())
+
+    def workspace(self, Hq: int):
+        if self._ws is None or self._ws_hq != Hq:
+            nbytes = _lib.load().sep_decode_workspace_bytes(self.B, Hq, self.Hkv, self.c, self.D)
+            if nbytes == 0:
+                raise ValueError("invalid decode shape")
+            self._ws = torch.zeros((nbytes,), dtype=torch.uint8, device=self.k.device)
+            self._ws_hq = Hq
+        return self._ws
+
+    def reset(self):
+        sep_cache_reset(self)
+
+    def n_seen(self):
+        return self.state[:, 0]
+
+
+def sep_cache_reset(cache: SepCache):
+    st = cache.struct()
+    _lib.check("sep_cache_reset", _lib.load().sep_cache_reset(ctypes.byref(st), _stream()))
+
+
+def sep_cache_update(cache: SepCache, k_new, v_new, ids_new, sep_ids):
+    """Append T tokens per sequence: k_new/v_new [B,Hkv,T,D], ids_new [B,T] i32."""
+    lib = _lib.load()
+    _need(k_new, "k_new", cache.dtype, 4)
+    _need(v_new, "v_new", cache.dtype, 4)
+    _need(ids_new, "ids_new", torch.int32, 2)
+    _need(sep_ids, "sep_ids", torch.int32, 1)
+    B, Hkv, T, D = k_new.shape
+    if (B, Hkv, D) != (cache.B, cache.Hkv, cache.D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, Hkv, T, D] of the cache")
+    if ids_new.shape != (B, T):
+        raise ValueError("ids_new must be [B, T]")
+    st = cache.struct()
+    code = lib.sep_cache_update(ctypes.byref(st), k_new.data_ptr(), v_new.data_ptr(),
+                                ids_new.data_ptr(), T,
+                                _ptr(sep_ids) if sep_ids.numel() else None, sep_ids.numel(),
+                                _stream())
+    _lib.check("sep_cache_update", code)
+
+
+def sep_attn_decode(q, k_new, v_new, cache: SepCache, scale: float | None = None, *, out=None,
+                    return_lse: bool = False, lse=None):
+    """One decode step: q [B,Hq,D], k_new/v_new [B,Hkv,D] (bf16)."""
+    lib = _lib.load()
+    _need(q, "q", cache.dtype, 3)
+    _need(k_new, "k_new", cache.dtype, 3)
+    _need(v_new, "v_new", cache.dtype, 3)
+    B, Hq, D = q.shape
+    if (B, D) != (cache.B, cache.D) or k_new.shape != (B, cache.Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("shapes do not match the cache")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = cache.workspace(Hq)
+    st = cache.struct()
+    code = lib.sep_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ctypes.byref(st),
+                               Hq, float(scale), out.data_ptr(), _ptr(lse), ws.data_ptr(),
+                               ws.numel(), _stream())
+    _lib.check("sep_attn_decode", code)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,156 @@
+// C ABI of libsepattn: host-side validation, then kernel launches.
+// Every check runs before anything is enqueued; a failed check returns a
+// negative sep_status and launches nothing.
+#include <stdint.h>
+
+#include "internal.hpp"
+#include "sepattn.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kMaxSepCache = 8192;   // separator-ring cap (plan list lives in LDS)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SEP_OK : SEP_ERR_HIP; }
+
+int check_cache(const sep_cache* c) {
+  if (c == nullptr) return SEP_ERR_NULL;
+  if (c->pos == nullptr || c->tok == nullptr || c->state == nullptr) return SEP_ERR_NULL;
+  if (c->B <= 0 || c->Hkv <= 0) return SEP_ERR_SHAPE;
+  if (c->D != 64 && c->D != 128) return SEP_ERR_SHAPE;
+  if (c->dtype != SEP_BF16 && c->dtype != SEP_F32) return SEP_ERR_DTYPE;
+  // parameter contract (study notes, "Streaming 参数约束"), with c = a+s+p+w
+  if (c->a < 0 || c->w < 1 || c->s < 0 || c->p < 0) return SEP_ERR_PARAM;
+  const bool sepllm = c->s >= 1 && c->p >= 1;
+  const bool streaming = c->s == 0 && c->p == 0;
+  if (!sepllm && !streaming) return SEP_ERR_PARAM;
+  if (c->s > kMaxSepCache) return SEP_ERR_PARAM;
+  const int64_t cap = static_cast<int64_t>(c->a) + c->s + c->p + c->w;
+  if (cap > (1 << 24)) return SEP_ERR_SHAPE;
+  return SEP_OK;
+}
+
+int check_cache_kv(const sep_cache* c) {
+  if (c->k == nullptr || c->v == nullptr) return SEP_ERR_NULL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return SEP_ERR_ALIGN;
+  return SEP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sep_version(void) { return kVersion; }
+
+const char* sep_status_string(int s) {
+  switch (s) {
+    case SEP_OK: return "ok";
+    case SEP_ERR_NULL: return "a required pointer is NULL";
+    case SEP_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case SEP_ERR_PARAM: return "a parameter breaks the Sep-Attention / cache contract";
+    case SEP_ERR_DTYPE: return "dtype not supported by this entry point";
+    case SEP_ERR_WORKSPACE: return "workspace missing or too small";
+    case SEP_ERR_HIP: return "HIP launch failure";
+    case SEP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int sep_mask_build(const int32_t* ids, int B, int S, const int32_t* sep_ids, int n_sep_ids, int a,
+                   int n, uint8_t* is_sep, uint8_t* tile_class, int tq, int tk,
+                   uint8_t* dense_mask, hipStream_t stream) {
+  if (ids == nullptr || is_sep == nullptr) return SEP_ERR_NULL;
+  if (n_sep_ids < 0 || n_sep_ids > SEP_MAX_SEP_IDS) return SEP_ERR_SHAPE;
+  if (n_sep_ids > 0 && sep_ids == nullptr) return SEP_ERR_NULL;
+  if (B <= 0 || S <= 0) return SEP_ERR_SHAPE;
+  if (a < 0 || n < 1) return SEP_ERR_PARAM;
+  if (tile_class != nullptr && (tq < 1 || tk < 1 || tq > 4096 || tk > 4096)) return SEP_ERR_SHAPE;
+  if (dense_mask != nullptr && S > SEP_MAX_DENSE_S) return SEP_ERR_SHAPE;
+  if (!aligned16(ids)) return SEP_ERR_ALIGN;
+  hipError_t e = sep::launch_is_sep(ids, static_cast<int64_t>(B) * S, sep_ids, n_sep_ids, is_sep,
+                                    stream);
+  if (e != hipSuccess) return SEP_ERR_HIP;
+  if (tile_class != nullptr) {
+    e = sep::launch_tile_class(is_sep, B, S, a, n, tq, tk, tile_class, stream);
+    if (e != hipSuccess) return SEP_ERR_HIP;
+  }
+  if (dense_mask != nullptr) {
+    e = sep::launch_dense_mask(is_sep, B, S, a, n, dense_mask, stream);
+    if (e != hipSuccess) return SEP_ERR_HIP;
+  }
+  return SEP_OK;
+}
+
+int sep_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank, int32_t* sep_pos,
+                      int32_t* count, hipStream_t stream) {
+  if (is_sep == nullptr || rank == nullptr || sep_pos == nullptr) return SEP_ERR_NULL;
+  if (B <= 0 || S <= 0) return SEP_ERR_SHAPE;
+  return hip_status(sep::launch_index_compact(is_sep, B, S, rank, sep_pos, count, stream));
+}
+
+int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
+                     int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                     const int32_t* sep_pos, int a, int n, float scale, void* out, float* lse,
+                     hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return SEP_ERR_NULL;
+  if (is_sep == nullptr || rank == nullptr || sep_pos == nullptr) return SEP_ERR_NULL;
+  if (dtype != SEP_BF16 && dtype != SEP_F32) return SEP_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0) return SEP_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq / Hkv > 16) return SEP_ERR_SHAPE;
+  if (D != 64 && D != 128) return SEP_ERR_SHAPE;
+  if (a < 0 || n < 1) return SEP_ERR_PARAM;
+  if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_prefill(q, k, v, dtype, B, Hq, Hkv, S, D, is_sep, rank, sep_pos, a,
+                                        n, scale, out, lse, stream));
+}
+
+int sep_cache_reset(const sep_cache* cache, hipStream_t stream) {
+  const int st = check_cache(cache);
+  if (st != SEP_OK) return st;
+  return hip_status(sep::launch_cache_reset(*cache, stream));
+}
+
+int sep_cache_update(const sep_cache* cache, const void* k_new, const void* v_new,
+                     const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep_ids,
+                     hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != SEP_OK) return st;
+  st = check_cache_kv(cache);
+  if (st != SEP_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || ids_new == nullptr) return SEP_ERR_NULL;
+  if (T < 1) return SEP_ERR_SHAPE;
+  if (n_sep_ids < 0 || n_sep_ids > SEP_MAX_SEP_IDS) return SEP_ERR_SHAPE;
+  if (n_sep_ids > 0 && sep_ids == nullptr) return SEP_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SEP_ERR_ALIGN;
+  return hip_status(
+      sep::launch_cache_update(*cache, k_new, v_new, ids_new, T, sep_ids, n_sep_ids, stream));
+}
+
+size_t sep_decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
+  return sep::decode_workspace_bytes(B, Hq, Hkv, c, D);
+}
+
+int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
+                    int Hq, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != SEP_OK) return st;
+  st = check_cache_kv(cache);
+  if (st != SEP_OK) return st;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr) return SEP_ERR_NULL;
+  if (cache->dtype != SEP_BF16) return SEP_ERR_DTYPE;
+  if (Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return SEP_ERR_SHAPE;
+  if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
+  const int cap = cache->a + cache->s + cache->p + cache->w;
+  const size_t need = sep::decode_workspace_bytes(cache->B, Hq, cache->Hkv, cap, cache->D);
+  if (ws == nullptr || ws_bytes < need) return SEP_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || !aligned16(ws))
+    return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, out, lse, ws, stream));
+}
+
+}  // extern "C"

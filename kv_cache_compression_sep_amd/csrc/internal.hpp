@@ -1,0 +1,36 @@
+// Internal launchers behind the C ABI (argument checking happens in api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sepattn.h"
+
+#define SEP_MAX_SEP_IDS_ SEP_MAX_SEP_IDS
+
+namespace sep {
+
+hipError_t launch_is_sep(const int32_t* ids, int64_t N, const int32_t* sep_ids, int n_sep,
+                         uint8_t* is_sep, hipStream_t st);
+hipError_t launch_tile_class(const uint8_t* is_sep, int B, int S, int a, int n, int tq, int tk,
+                             uint8_t* tc, hipStream_t st);
+hipError_t launch_dense_mask(const uint8_t* is_sep, int B, int S, int a, int n, uint8_t* M,
+                             hipStream_t st);
+hipError_t launch_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank,
+                                int32_t* sep_pos, int32_t* count, hipStream_t st);
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
+                          int Hkv, int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                          const int32_t* sep_pos, int a, int n, float scale, void* out, float* lse,
+                          hipStream_t st);
+hipError_t launch_cache_reset(const sep_cache& c, hipStream_t st);
+hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void* v_new,
+                               const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,
+                               hipStream_t st);
+hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
+                         int Hq, float scale, void* out, float* lse, void* ws, hipStream_t st);
+
+// Decode split-K geometry shared by the launcher and the workspace query.
+constexpr int kDecodeMaxSplit = 16;
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D);
+
+}  // namespace sep

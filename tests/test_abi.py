@@ -1,0 +1,152 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/sepattn.h declares, and rejects invalid arguments with the documented
+status codes before touching the GPU (validation runs before any HIP call,
+so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_compression_sep_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sepattn.h")
+FAKE = 4096  # a non-NULL, 16-byte aligned host address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libsepattn.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:int|size_t|const char\*)\s+(sep_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_entry_points():
+    names = header_functions()
+    for fn in ("sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_decode",
+               "sep_cache_update"):
+        assert fn in names
+
+
+def test_every_declared_function_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for fn in header_functions():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+    assert set(_lib.SIGNATURES) == set(header_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sep_version() >= 10000
+    for code in range(-7, 1):
+        assert lib.sep_status_string(code)
+    assert lib.sep_status_string(-99) == b"unknown status"
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(_lib.SepCacheStruct) == 8 * 4 + 5 * 8
+    assert _lib.SepCacheStruct.k.offset == 32
+
+
+def test_mask_build_argument_checks(lib):
+    f = lib.sep_mask_build
+    E = _lib
+    assert f(None, 1, 8, FAKE, 1, 4, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_NULL
+    assert f(FAKE, 1, 8, FAKE, 1, 4, 2, None, None, 0, 0, None, None) == E.SEP_ERR_NULL
+    assert f(FAKE, 0, 8, FAKE, 1, 4, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_SHAPE
+    assert f(FAKE, 1, 0, FAKE, 1, 4, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_SHAPE
+    assert f(FAKE, 1, 8, FAKE, 65, 4, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_SHAPE
+    assert f(FAKE, 1, 8, None, 3, 4, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_NULL
+    assert f(FAKE, 1, 8, FAKE, 1, -1, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_PARAM
+    assert f(FAKE, 1, 8, FAKE, 1, 4, 0, FAKE, None, 0, 0, None, None) == E.SEP_ERR_PARAM
+    assert f(FAKE, 1, 8, FAKE, 1, 4, 2, FAKE, FAKE, 0, 8, None, None) == E.SEP_ERR_SHAPE
+    assert f(FAKE, 1, 9000, FAKE, 1, 4, 2, FAKE, None, 0, 0, FAKE, None) == E.SEP_ERR_SHAPE
+    assert f(FAKE + 4, 1, 8, FAKE, 1, 4, 2, FAKE, None, 0, 0, None, None) == E.SEP_ERR_ALIGN
+
+
+def test_index_compact_argument_checks(lib):
+    f = lib.sep_index_compact
+    assert f(None, 1, 8, FAKE, FAKE, None, None) == _lib.SEP_ERR_NULL
+    assert f(FAKE, 1, 8, None, FAKE, None, None) == _lib.SEP_ERR_NULL
+    assert f(FAKE, 0, 8, FAKE, FAKE, None, None) == _lib.SEP_ERR_SHAPE
+
+
+def _prefill(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, B=1, Hq=32, Hkv=8, S=64, D=128, is_sep=FAKE,
+                rank=FAKE, sep_pos=FAKE, a=4, n=16, scale=0.088, out=FAKE, lse=None, st=None)
+    args.update(kw)
+    return lib.sep_attn_prefill(*args.values())
+
+
+def test_prefill_argument_checks(lib):
+    E = _lib
+    assert _prefill(lib, q=None) == E.SEP_ERR_NULL
+    assert _prefill(lib, rank=None) == E.SEP_ERR_NULL
+    assert _prefill(lib, dtype=7) == E.SEP_ERR_DTYPE
+    assert _prefill(lib, Hq=30) == E.SEP_ERR_SHAPE        # not a multiple of Hkv
+    assert _prefill(lib, Hq=8 * 17) == E.SEP_ERR_SHAPE    # group larger than 16
+    assert _prefill(lib, D=96) == E.SEP_ERR_SHAPE
+    assert _prefill(lib, S=0) == E.SEP_ERR_SHAPE
+    assert _prefill(lib, a=-1) == E.SEP_ERR_PARAM
+    assert _prefill(lib, n=0) == E.SEP_ERR_PARAM
+    assert _prefill(lib, scale=0.0) == E.SEP_ERR_PARAM
+    assert _prefill(lib, scale=float("nan")) == E.SEP_ERR_PARAM
+    assert _prefill(lib, out=FAKE + 2) == E.SEP_ERR_ALIGN
+
+
+def _cache(**kw):
+    d = dict(a=4, s=64, p=64, w=256, B=1, Hkv=8, D=128, dtype=1, k=FAKE, v=FAKE, pos=FAKE,
+             tok=FAKE, state=FAKE)
+    d.update(kw)
+    return _lib.SepCacheStruct(*d.values())
+
+
+def test_cache_contract_from_the_pages(lib):
+    """P1 "Streaming 参数约束": cache > 0, init >= 0, local > 0,
+    cache >= init + local; SepLLM: sep > 0 and init + sep + local < cache;
+    StreamingLLM: local == cache - init (here s = p = 0)."""
+    E = _lib
+    upd = lambda c: lib.sep_cache_update(ctypes.byref(c), FAKE, FAKE, FAKE, 1, FAKE, 1, None)
+    assert upd(_cache(w=0)) == E.SEP_ERR_PARAM             # local must be > 0
+    assert upd(_cache(a=-1)) == E.SEP_ERR_PARAM            # init must be >= 0
+    assert upd(_cache(p=0)) == E.SEP_ERR_PARAM             # init + sep + local == cache
+    assert upd(_cache(s=0)) == E.SEP_ERR_PARAM             # sep must be > 0 for SepLLM
+    assert upd(_cache(s=9000)) == E.SEP_ERR_PARAM          # beyond the ring limit
+    assert upd(_cache(D=80)) == E.SEP_ERR_SHAPE
+    assert upd(_cache(dtype=5)) == E.SEP_ERR_DTYPE
+    assert upd(_cache(pos=None)) == E.SEP_ERR_NULL
+    assert upd(_cache(k=FAKE + 8)) == E.SEP_ERR_ALIGN
+    assert lib.sep_cache_update(None, FAKE, FAKE, FAKE, 1, FAKE, 1, None) == E.SEP_ERR_NULL
+    c = _cache()
+    assert lib.sep_cache_update(ctypes.byref(c), FAKE, FAKE, FAKE, 0, FAKE, 1, None) == E.SEP_ERR_SHAPE
+    assert lib.sep_cache_update(ctypes.byref(c), None, FAKE, FAKE, 1, FAKE, 1, None) == E.SEP_ERR_NULL
+    assert lib.sep_cache_reset(ctypes.byref(_cache(w=0)), None) == E.SEP_ERR_PARAM
+
+
+def test_decode_argument_checks(lib):
+    E = _lib
+    c = _cache()
+    need = lib.sep_decode_workspace_bytes(1, 32, 8, 388, 128)
+    assert need > 0
+    assert lib.sep_decode_workspace_bytes(1, 30, 8, 388, 128) == 0
+    dec = lambda cc, **kw: lib.sep_attn_decode(
+        kw.get("q", FAKE), FAKE, FAKE, ctypes.byref(cc), kw.get("Hq", 32), kw.get("scale", 0.1),
+        FAKE, None, kw.get("ws", FAKE), kw.get("ws_bytes", need), None)
+    assert dec(c, ws=None) == E.SEP_ERR_WORKSPACE
+    assert dec(c, ws_bytes=need - 1) == E.SEP_ERR_WORKSPACE
+    assert dec(c, q=None) == E.SEP_ERR_NULL
+    assert dec(c, Hq=12) == E.SEP_ERR_SHAPE
+    assert dec(c, scale=-1.0) == E.SEP_ERR_PARAM
+    assert dec(_cache(dtype=0)) == E.SEP_ERR_DTYPE
+    assert dec(c, q=FAKE + 2) == E.SEP_ERR_ALIGN

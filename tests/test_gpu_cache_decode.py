@@ -1,0 +1,168 @@
+"""GPU parity of sep_cache_update and sep_attn_decode against the oracle.
+
+The cache must match the list-based simulation bit for bit, block by block
+in logical order (initial, separator ring oldest first, recent ring oldest
+first): positions, token ids and K/V bytes; every slot outside the live set
+must read pos = tok = -1. A bulk update of T tokens must leave exactly the
+state (pos, tok, state words, live K/V rows) of T single-token updates.
+Decode outputs must match fp64 attention over the retained keys plus the
+current token within the bf16 tolerance.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from inputs import configs, gen
+from kv_cache_compression_sep_amd import SepCache, sep_attn_decode, sep_cache_update
+
+from .gpu_util import check_close, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+SEP_IDS = list(range(8))
+
+
+class Stream:
+    """A seeded synthetic token stream for one batch of sequences."""
+
+    def __init__(self, seed, B, Hq, Hkv, D, T, p_sep):
+        rng = np.random.default_rng(seed)
+        self.ids = np.where(rng.random((B, T)) < p_sep, rng.integers(0, 8, (B, T)),
+                            rng.integers(8, 1000, (B, T))).astype(np.int32)
+        self.k = gen.round_storage(rng.standard_normal((B, Hkv, T, D)), "bf16")
+        self.v = gen.round_storage(rng.standard_normal((B, Hkv, T, D)), "bf16")
+        self.q = gen.round_storage(rng.standard_normal((B, T, Hq, D)), "bf16")
+        self.B, self.Hq, self.Hkv, self.D, self.T = B, Hq, Hkv, D, T
+
+    def push_gpu(self, cache, t0, t1, d_sep):
+        sep_cache_update(cache, to_dev(np.ascontiguousarray(self.k[:, :, t0:t1]), "bf16"),
+                         to_dev(np.ascontiguousarray(self.v[:, :, t0:t1]), "bf16"),
+                         to_dev(np.ascontiguousarray(self.ids[:, t0:t1])), d_sep)
+
+
+def live_slots(cache, b):
+    t, K, head, cnt = [int(x) for x in cache.state[b].cpu().numpy()]
+    a, s, p, w = cache.a, cache.s, cache.p, cache.w
+    I = list(range(min(a, t)))
+    S = [a + (head - cnt + i) % s for i in range(cnt)] if s > 0 else []
+    cend = a + K * (p + 1)
+    R = [a + s + (x - a) % (p + w) for x in range(max(cend, a), t)] if t > a else []
+    return I, S, R
+
+
+def check_cache(cache, sims, stream):
+    pos = cache.pos.cpu().numpy()
+    tok = cache.tok.cpu().numpy()
+    kc = cache.k.view(torch.int16).cpu().numpy()
+    vc = cache.v.view(torch.int16).cpu().numpy()
+    for b, sim in enumerate(sims):
+        I, S, R = live_slots(cache, b)
+        assert int(cache.state[b, 0]) == sim.t
+        want = sim.positions()
+        for slots, wpos, name in zip((I, S, R), want, "ISR"):
+            assert pos[b, slots].tolist() == wpos, (b, name)
+            assert tok[b, slots].tolist() == [int(stream.ids[b, x]) for x in wpos], (b, name)
+            if wpos:
+                assert np.array_equal(kc[b][:, slots], stream.k[b][:, wpos].view(np.int16)), (b, name)
+                assert np.array_equal(vc[b][:, slots], stream.v[b][:, wpos].view(np.int16)), (b, name)
+        dead = sorted(set(range(cache.c)) - set(I) - set(S) - set(R))
+        assert (pos[b, dead] == -1).all() and (tok[b, dead] == -1).all(), b
+        assert sim.occupancy() == len(I) + len(S) + len(R)
+
+
+PARAMS = [
+    # a, s,  p,  w
+    (4, 6, 5, 9),
+    (0, 3, 1, 4),
+    (2, 1, 3, 1),
+    (4, 64, 64, 256),
+    (3, 10, 70, 20),    # p + 1 > 64: compaction crosses a wavefront
+    (1, 40, 300, 7),    # compaction across several waves
+    (4, 0, 0, 12),      # StreamingLLM: initial + local only
+]
+
+
+@pytest.mark.parametrize("params", PARAMS, ids=[str(p) for p in PARAMS])
+def test_single_token_updates_match_simulation(params):
+    a, s, p, w = params
+    T = min(3 * (a + s + p + w) + 50, 1400)
+    st = Stream(zlib.crc32(repr(params).encode()), 2, 4, 2, 64, T, 0.3)
+    cache = SepCache(2, 2, 64, a, s, p, w)
+    sims = [oracle.CacheSim(a, s, p, w, SEP_IDS) for _ in range(2)]
+    d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
+    every = max(1, T // 60)
+    for t in range(T):
+        st.push_gpu(cache, t, t + 1, d_sep)
+        for b in range(2):
+            sims[b].push(oracle.Entry(t, int(st.ids[b, t])))
+        if t % every == 0 or t == T - 1:
+            check_cache(cache, sims, st)
+
+
+@pytest.mark.parametrize("params", PARAMS, ids=[str(p) for p in PARAMS])
+def test_bulk_updates_equal_single_updates(params):
+    a, s, p, w = params
+    T = min(4 * (a + s + p + w) + 77, 2000)
+    st = Stream(zlib.crc32(repr(params).encode()) + 1, 3, 4, 2, 128, T, 0.25)
+    d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
+    one = SepCache(3, 2, 128, a, s, p, w)
+    bulk = SepCache(3, 2, 128, a, s, p, w)
+    for t in range(T):
+        st.push_gpu(one, t, t + 1, d_sep)
+    rng = np.random.default_rng(T)
+    cuts = sorted(set([0, T] + rng.integers(1, T, 6).tolist()))
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        st.push_gpu(bulk, t0, t1, d_sep)
+    torch.cuda.synchronize()
+    assert torch.equal(one.state, bulk.state)
+    assert torch.equal(one.pos, bulk.pos)
+    assert torch.equal(one.tok, bulk.tok)
+    sims = [oracle.CacheSim(a, s, p, w, SEP_IDS) for _ in range(3)]
+    for b in range(3):
+        sims[b].push_many([oracle.Entry(t, int(st.ids[b, t])) for t in range(T)])
+    check_cache(bulk, sims, st)
+    check_cache(one, sims, st)
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, D,  a, s,  p,  w,  T
+    (2, 32, 8, 128, 4, 64, 64, 256, 700),
+    (1, 8, 8, 64, 2, 5, 3, 11, 90),
+    (3, 16, 1, 128, 0, 7, 9, 33, 300),
+    (1, 12, 3, 64, 4, 20, 2, 40, 5),      # cache still filling the initial block
+    (2, 4, 2, 128, 4, 0, 0, 50, 200),     # StreamingLLM mode
+    (1, 16, 16, 128, 4, 256, 28, 512, 1500),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
+def test_decode_matches_oracle(case):
+    B, Hq, Hkv, D, a, s, p, w, T = case
+    st = Stream(zlib.crc32(repr(case).encode()), B, Hq, Hkv, D, T + 40, 0.2)
+    d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
+    cache = SepCache(B, Hkv, D, a, s, p, w)
+    sims = [oracle.CacheSim(a, s, p, w, SEP_IDS) for _ in range(B)]
+    st.push_gpu(cache, 0, T, d_sep)
+    for b in range(B):
+        sims[b].push_many([oracle.Entry(t, int(st.ids[b, t])) for t in range(T)])
+    scale = 1.0 / math.sqrt(D)
+    for t in range(T, T + 40):
+        q = to_dev(np.ascontiguousarray(st.q[:, t]), "bf16")
+        kn = to_dev(np.ascontiguousarray(st.k[:, :, t]), "bf16")
+        vn = to_dev(np.ascontiguousarray(st.v[:, :, t]), "bf16")
+        out, lse = sep_attn_decode(q, kn, vn, cache, scale, return_lse=True)
+        o = from_dev(out)
+        l_gpu = from_dev(lse)
+        for b in range(B):
+            keys = [e.pos for e in sims[b].keys()] + [t]
+            kk = gen.bf16_bits_to_f64(st.k[b][:, keys])
+            vv = gen.bf16_bits_to_f64(st.v[b][:, keys])
+            o_ref, l_ref = oracle.decode_attention(gen.bf16_bits_to_f64(st.q[b, t]), kk, vv, scale)
+            check_close(o[b], o_ref, "bf16", f"{case} step {t} b {b}")
+            assert np.max(np.abs(l_gpu[b] - l_ref)) < 1e-3
+        st.push_gpu(cache, t, t + 1, d_sep)
+        for b in range(B):
+            sims[b].push(oracle.Entry(t, int(st.ids[b, t])))
