@@ -1,0 +1,421 @@
+#!/usr/bin/env python
+"""Benchmark of the Sep-Attention hot path on one MI355X.
+
+One step = one pass of the prefill path on the Llama-3-8B single-layer
+workload (1 x 8192 tokens, 32 query / 8 KV heads, D = 128, bf16, a = 4,
+n = 256, separator probability 0.12): sep_mask_build -> sep_index_compact
+-> sep_attn_prefill, inputs resident in HBM. The headline value is useful
+TFLOP/s of that pass (useful FLOPs = 4 * D * visible (query, key) pairs,
+summed over query heads).
+
+The same run also measures the streaming rows of the path and reports them
+under "secondary":
+  * batched decode (64 sequences with 32,768-token histories, cache
+    4/256/28/512): bulk history ingest (sep_cache_update, GB/s) and 1024
+    decode + update steps (KV GB/s on algorithmic bytes);
+  * streaming decode (batch 1, cache 4/64/64/256) over the 4,194,304-token
+    stream: tokens/s of in-order decode + update steps, replayed from HIP
+    graphs of 256 steps.
+
+Prints one JSON line. ``--gpus N`` with N > 1 exits: this build runs on one
+GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "Sep-Attn prefill useful TFLOP/s; decode+cache-update KV GB/s; stream tok/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def visible_pairs(rank: np.ndarray, S: int, a: int, n: int) -> int:
+    """Visible (query, key) pairs of one sequence from its separator ranks:
+    per row i, initial keys + window keys above the initial block +
+    separators between the initial block and the window."""
+    i = np.arange(S, dtype=np.int64)
+    lo = np.maximum(i - n + 1, 0)
+    a_ = min(a, S)
+    hi = np.maximum(lo, a_)
+    rows = np.minimum(i + 1, a) + np.maximum(0, i + 1 - hi) + np.maximum(0, rank[hi] - rank[a_])
+    return int(rows.sum())
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "kv_cache_compression_sep_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+        e = d[kernel]
+        if e.get("source_hash") != kernel_source_hash():
+            return None
+        return e.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+# ------------------------------------------------------------------ prefill
+def bench_prefill(args, torch, sa, configs, gen):
+    cfg = configs.C2
+    B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+    x = gen.prefill_inputs(cfg)
+    dev = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+                               if bf else torch.from_numpy(np.ascontiguousarray(a))).cuda()
+    ids = dev(x["ids"])
+    q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
+    sep = dev(np.asarray(cfg.sep_ids, np.int32))
+    is_sep = torch.empty((B, S), dtype=torch.uint8, device="cuda")
+    rank = torch.empty((B, S + 1), dtype=torch.int32, device="cuda")
+    sep_pos = torch.empty((B, S), dtype=torch.int32, device="cuda")
+    count = torch.empty((B,), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+
+    def step():
+        sa.sep_mask_build(ids, sep, cfg.a, cfg.n, is_sep=is_sep)
+        sa.sep_index_compact(is_sep, rank=rank, sep_pos=sep_pos, count=count)
+        sa.sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, cfg.a, cfg.n, scale, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pairs = sum(visible_pairs(rank[b].cpu().numpy().astype(np.int64), S, cfg.a, cfg.n)
+                for b in range(B))
+    useful = 4.0 * D * pairs * Hq            # pairs counted per kv-head sequence, used by all heads
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st)
+    for i in range(args.steps):
+        sa.sep_mask_build(ids, sep, cfg.a, cfg.n, is_sep=is_sep)
+        sa.sep_index_compact(is_sep, rank=rank, sep_pos=sep_pos, count=count)
+        ev[i][0].record(st)
+        sa.sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, cfg.a, cfg.n, scale, out=out)
+        ev[i][1].record(st)
+    t1.record(st)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    tflops_step = useful / (ms_step * 1e-3) / 1e12
+    tflops_kernel = useful / (ms_kernel * 1e-3) / 1e12
+    log(f"prefill: {pairs} pairs/seq, {useful / 1e9:.1f} useful GFLOP, step {ms_step * 1e3:.1f} us "
+        f"({tflops_step:.1f} TFLOP/s), prefill kernel {ms_kernel * 1e3:.1f} us ({tflops_kernel:.1f} TFLOP/s)")
+    return dict(cfg=cfg, x=x, pairs=pairs, useful=useful, ms_step=ms_step, ms_kernel=ms_kernel,
+                tflops_step=tflops_step, tflops_kernel=tflops_kernel)
+
+
+def cpu_baseline_prefill(res, oracle, gen, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample: whole heads of the same
+    workload (explicit mask + fp64 dense masked softmax attention)."""
+    cfg, x = res["cfg"], res["x"]
+    cores = len(os.sched_getaffinity(0))
+    t_start = time.perf_counter()
+    flags = oracle.is_sep(x["ids"][0], cfg.sep_ids)
+    M = oracle.sep_mask(flags, cfg.a, cfg.n)
+    pairs = int(M.sum())
+    G = cfg.Hq // cfg.Hkv
+    heads = 0
+    scale = 1.0 / math.sqrt(cfg.D)
+    while heads < cfg.Hq:
+        h = heads
+        g = h // G
+        oracle.attention(gen.bf16_bits_to_f64(x["q"][0, h:h + 1]), gen.bf16_bits_to_f64(x["k"][0, g:g + 1]),
+                         gen.bf16_bits_to_f64(x["v"][0, g:g + 1]), M, scale)
+        heads += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    el = time.perf_counter() - t_start
+    useful = 4.0 * cfg.D * pairs * heads
+    return {"value": useful / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {cfg.Hq} query heads of the 1x8192 Llama-3 layer workload, "
+                      f"mask build included ({el:.1f} s)"}
+
+
+# ------------------------------------------------------------------ batched decode
+def bench_batched(args, torch, sa, configs, gen):
+    cfg = configs.C4
+    B, Hq, Hkv, D, H = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.history
+    ids_h = np.stack([gen.stream_ids(cfg, b) for b in range(B)])
+    ids = torch.from_numpy(ids_h).cuda()
+    sep = torch.tensor(cfg.sep_ids, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    hk = torch.randn((B, Hkv, H, D), device="cuda", generator=g).to(torch.bfloat16)
+    hv = torch.randn((B, Hkv, H, D), device="cuda", generator=g).to(torch.bfloat16)
+    pq = torch.randn((cfg.steps, B, Hq, D), device="cuda", generator=g).to(torch.bfloat16)
+    pk = torch.randn((cfg.steps, B, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
+    pv = torch.randn((cfg.steps, B, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
+    hist_ids = ids[:, :H].contiguous()
+    step_ids = ids[:, H:].t().contiguous()             # [steps, B]
+    cache = sa.SepCache(B, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w, Hq=Hq)
+    st = torch.cuda.current_stream()
+    # bulk ingest (warm once, then time a fresh ingest)
+    sa.sep_cache_update(cache, hk, hv, hist_ids, sep)
+    torch.cuda.synchronize()
+    ing = []
+    for _ in range(3):
+        cache.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        sa.sep_cache_update(cache, hk, hv, hist_ids, sep)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ing.append(e0.elapsed_time(e1))
+    ms_ingest = float(np.median(ing))
+    occ0 = _occupancy(cache)
+    row = Hkv * D * 2                                    # bytes of one K (or V) token row
+    ingest_bytes = B * H * 4 + 2 * 2 * int(occ0.sum()) * row
+    # decode + update steps: host-side bookkeeping of algorithmic bytes
+    flags = np.isin(ids_h, np.asarray(cfg.sep_ids))
+    csum = np.concatenate([np.zeros((B, 1), np.int64), np.cumsum(flags, axis=1)], axis=1)
+    total_bytes = 0
+    dec_bytes = 0
+    for j in range(cfg.steps):
+        t = H + j
+        occ = _occ_closed(t, cfg, csum)
+        dec = int(((occ + 1) * 2 * row).sum()) + 2 * B * Hq * D * 2
+        dec_bytes += dec
+        t1 = t + 1
+        K0 = _ncomp(t, cfg)
+        K1 = _ncomp(t1, cfg)
+        moved = 0
+        if K1 > K0:
+            c0 = cfg.a + K0 * (cfg.p + 1)
+            c1 = cfg.a + K1 * (cfg.p + 1)
+            moved = np.minimum(csum[:, c1] - csum[:, c0], cfg.s).sum()
+        upd = 2 * 2 * B * row + 2 * 2 * int(moved) * row
+        total_bytes += dec + upd
+    scale = 1.0 / math.sqrt(D)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(cfg.steps)]
+    torch.cuda.synchronize()
+    e0.record(st)
+    for j in range(cfg.steps):
+        dec_ev[j][0].record(st)
+        sa.sep_attn_decode(pq[j], pk[j], pv[j], cache, scale, out=out)
+        dec_ev[j][1].record(st)
+        sa.sep_cache_update(cache, pk[j].view(B, Hkv, 1, D), pv[j].view(B, Hkv, 1, D),
+                            step_ids[j].view(B, 1), sep)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_steps = e0.elapsed_time(e1)
+    ms_dec = float(sum(a.elapsed_time(b) for a, b in dec_ev))
+    assert int(cache.state[0, 0]) == H + cfg.steps
+    res = dict(
+        ingest_ms=ms_ingest, ingest_GBps=ingest_bytes / (ms_ingest * 1e-3) / 1e9,
+        steps=cfg.steps, step_us=ms_steps * 1e3 / cfg.steps,
+        kv_GBps=total_bytes / (ms_steps * 1e-3) / 1e9,
+        decode_kernel_us=ms_dec * 1e3 / cfg.steps,
+        decode_kernel_GBps=dec_bytes / (ms_dec * 1e-3) / 1e9,
+        decode_bytes_per_step=dec_bytes / cfg.steps)
+    log(f"batched decode: ingest {ms_ingest:.2f} ms ({res['ingest_GBps']:.0f} GB/s), "
+        f"step {res['step_us']:.1f} us, KV {res['kv_GBps']:.0f} GB/s, decode kernel "
+        f"{res['decode_kernel_us']:.1f} us ({res['decode_kernel_GBps']:.0f} GB/s)")
+    return res
+
+
+def _ncomp(t, cfg):
+    m = t - cfg.a
+    if m <= 0:
+        return 0
+    return max(0, (m - cfg.w) // (cfg.p + 1))
+
+
+def _occ_closed(t, cfg, csum):
+    """Occupancy after t tokens for every sequence (closed form of the cache)."""
+    K = _ncomp(t, cfg)
+    cend = cfg.a + K * (cfg.p + 1)
+    if t <= cfg.a:
+        return np.full(csum.shape[0], t)
+    nsep = np.minimum(csum[:, cend] - csum[:, cfg.a], cfg.s)
+    return cfg.a + nsep + (t - max(cend, cfg.a))
+
+
+def _occupancy(cache):
+    st = cache.state.cpu().numpy()
+    a, s, p, w = cache.a, cache.s, cache.p, cache.w
+    occ = []
+    for t, K, head, cnt in st:
+        cend = a + K * (p + 1)
+        occ.append(min(a, t) + cnt + max(0, t - max(cend, a)))
+    return np.asarray(occ)
+
+
+# ------------------------------------------------------------------ stream
+def bench_stream(args, torch, sa, configs, gen):
+    cfg = configs.C3
+    Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
+    steps = args.stream_steps
+    chunk = 256
+    steps = (steps // chunk) * chunk
+    ids_h = gen.stream_ids(cfg, 0, cfg.history + cfg.steps)
+    ids = torch.from_numpy(ids_h).cuda()
+    sep = torch.tensor(cfg.sep_ids, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    P = cfg.pool
+    pq = torch.randn((P, 1, Hq, D), device="cuda", generator=g).to(torch.bfloat16)
+    pk = torch.randn((P, 1, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
+    pv = torch.randn((P, 1, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
+    stage = torch.empty((chunk,), dtype=torch.int32, device="cuda")
+    cache = sa.SepCache(1, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w, Hq=Hq)
+    out = torch.empty((1, Hq, D), dtype=torch.bfloat16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    n_graphs = min(P, steps) // chunk
+
+    def run_chunk(w):
+        for i in range(chunk):
+            t = w * chunk + i
+            sa.sep_attn_decode(pq[t], pk[t], pv[t], cache, scale, out=out)
+            sa.sep_cache_update(cache, pk[t].view(1, Hkv, 1, D), pv[t].view(1, Hkv, 1, D),
+                                stage[i:i + 1].view(1, 1), sep)
+
+    # capture one graph per pool window of `chunk` steps
+    s_cap = torch.cuda.Stream()
+    graphs = []
+    tc0 = time.perf_counter()
+    with torch.cuda.stream(s_cap):
+        for w in range(n_graphs):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s_cap):
+                run_chunk(w)
+            graphs.append(gr)
+    torch.cuda.synchronize()
+    cache.reset()
+    torch.cuda.synchronize()
+    log(f"stream: captured {n_graphs} graphs of {chunk} steps in {time.perf_counter() - tc0:.1f} s")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(st)
+    for c in range(steps // chunk):
+        t0 = c * chunk
+        stage.copy_(ids[t0:t0 + chunk], non_blocking=True)
+        graphs[c % n_graphs].replay()
+        if c % 2048 == 2047:
+            log(f"stream: {t0 + chunk} steps")
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1)
+    assert int(cache.state[0, 0]) == steps
+    # closed-form check of the final positions and ids
+    flags = np.isin(ids_h[:steps], np.asarray(cfg.sep_ids))
+    K = _ncomp(steps, cfg)
+    cend = cfg.a + K * (cfg.p + 1)
+    seps = np.flatnonzero(flags[cfg.a:cend]) + cfg.a
+    want = list(range(cfg.a)) + seps[-cfg.s:].tolist() + list(range(cend, steps))
+    stt = cache.state[0].cpu().numpy()
+    pos = cache.pos[0].cpu().numpy()
+    Sl = [cfg.a + (int(stt[2]) - int(stt[3]) + i) % cfg.s for i in range(int(stt[3]))]
+    Rl = [cfg.a + cfg.s + (x - cfg.a) % (cfg.p + cfg.w) for x in range(max(cend, cfg.a), steps)]
+    got = pos[list(range(cfg.a))].tolist() + pos[Sl].tolist() + pos[Rl].tolist()
+    ok = got == want
+    res = dict(steps=steps, seconds=ms * 1e-3, wall_seconds=wall, tok_per_s=steps / (ms * 1e-3),
+               us_per_step=ms * 1e3 / steps, final_state_matches_closed_form=bool(ok))
+    log(f"stream: {steps} steps in {ms * 1e-3:.2f} s -> {res['tok_per_s']:.0f} tok/s "
+        f"({res['us_per_step']:.2f} us/step), closed form {'ok' if ok else 'MISMATCH'}")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stream-steps", type=int, default=4_194_304)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "stream"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Sep-Attention path here has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_compression_sep_amd as sa
+    from inputs import configs, gen
+    sa._lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    secondary = {}
+    res = None
+    if args.only in ("all", "prefill"):
+        res = bench_prefill(args, torch, sa, configs, gen)
+    if args.only in ("all", "decode"):
+        secondary["batched_decode_b64"] = bench_batched(args, torch, sa, configs, gen)
+    if args.only in ("all", "stream"):
+        secondary["stream_decode_b1"] = bench_stream(args, torch, sa, configs, gen)
+    if res is None:
+        print(json.dumps({"secondary": secondary}))
+        return
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cpu = cpu_baseline_prefill(res, oracle, gen)
+        log(f"cpu baseline: {cpu}")
+    cfg = res["cfg"]
+    traffic = measured_traffic("sep_attn_prefill")
+    line = {
+        "metric": METRIC,
+        "value": round(res["tflops_step"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.D, "seq_len": cfg.S, "a": cfg.a, "n": cfg.n,
+                   "p_sep": cfg.p_sep, "step": "sep_mask_build+sep_index_compact+sep_attn_prefill"},
+        "roofline": {"kernel": "sep_attn_prefill", "bound": "mfma",
+                     "achieved": round(res["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(res["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "useful_flop_per_launch": res["useful"],
+                     "avg_launch_us": round(res["ms_kernel"] * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

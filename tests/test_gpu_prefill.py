@@ -96,8 +96,8 @@ def _sampled_rows_check(cfg, heads, rows, x, out, tag):
     for i, h in enumerate(heads):
         g = h // G
         qr = gen.storage_to_f64(x["q"][0, i][rows], cfg.dtype)[None]
-        o_ref, _ = oracle.attention_rows(qr, {g: gen.storage_to_f64(x["k"][0, g], cfg.dtype)},
-                                         {g: gen.storage_to_f64(x["v"][0, g], cfg.dtype)}, Mr,
+        o_ref, _ = oracle.attention_rows(qr, {g: gen.storage_to_f64(x["k"][g], cfg.dtype)},
+                                         {g: gen.storage_to_f64(x["v"][g], cfg.dtype)}, Mr,
                                          scale, kv_head_of=[g])
         check_close(out[i], o_ref[0], cfg.dtype, f"{tag} head {h}")
 
