@@ -175,7 +175,7 @@ def bench_batched(args, torch, sa, configs, gen):
     pv = torch.randn((cfg.steps, B, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
     hist_ids = ids[:, :H].contiguous()
     step_ids = ids[:, H:].t().contiguous()             # [steps, B]
-    cache = sa.SepCache(B, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w, Hq=Hq)
+    cache = sa.SepCache(B, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w)
     st = torch.cuda.current_stream()
     # bulk ingest (warm once, then time a fresh ingest)
     sa.sep_cache_update(cache, hk, hv, hist_ids, sep)
@@ -288,7 +288,7 @@ def bench_stream(args, torch, sa, configs, gen):
     pk = torch.randn((P, 1, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
     pv = torch.randn((P, 1, Hkv, D), device="cuda", generator=g).to(torch.bfloat16)
     stage = torch.empty((chunk,), dtype=torch.int32, device="cuda")
-    cache = sa.SepCache(1, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w, Hq=Hq)
+    cache = sa.SepCache(1, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w)
     out = torch.empty((1, Hq, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
     n_graphs = min(P, steps) // chunk

@@ -53,7 +53,7 @@ typedef enum {
   SEP_ERR_SHAPE = -2,     /* a size is out of range or inconsistent        */
   SEP_ERR_PARAM = -3,     /* a, n, s, p, w, scale break the contract       */
   SEP_ERR_DTYPE = -4,     /* dtype not supported by this entry point       */
-  SEP_ERR_WORKSPACE = -5, /* workspace missing or too small                */
+  SEP_ERR_WORKSPACE = -5, /* reserved                                       */
   SEP_ERR_HIP = -6,       /* the HIP runtime reported a launch failure     */
   SEP_ERR_ALIGN = -7      /* a tensor pointer is not 16-byte aligned       */
 } sep_status;
@@ -206,23 +206,18 @@ int sep_cache_update(const sep_cache* cache, const void* k_new, const void* v_ne
  * P1 "Streaming-SepLLM" (each token: forward with the cache, then update
  * and compress); P2 §1.3 (only the retained KV are read)]
  *
- *   q      [B, Hq, D] in cache->dtype (SEP_BF16 only).
+ *   q      [B, Hq, D] in cache->dtype (SEP_BF16 only); Hq % Hkv == 0 and
+ *          Hq / Hkv <= 16; query head h reads kv head h / (Hq / Hkv).
  *   k_new, v_new [B, Hkv, D]: the current token's key/value. It attends the
  *          cache as it is (tokens before it) plus itself; call
  *          sep_cache_update afterwards to insert it.
  *   scale  > 0; out [B, Hq, D] (bf16); lse [B, Hq] float32 out or NULL.
- *   ws     device workspace of at least sep_decode_workspace_bytes(...)
- *          bytes, zero-filled before its first use; every call leaves it
- *          zero-filled again. Calls that overlap in time must not share it.
+ * Reads the cache, never writes it; needs no workspace.
  * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
- * SEP_ERR_WORKSPACE, SEP_ERR_ALIGN, SEP_ERR_HIP.
+ * SEP_ERR_ALIGN, SEP_ERR_HIP.
  */
 int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
-                    int Hq, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                    hipStream_t stream);
-
-/* Workspace bytes sep_attn_decode needs for this cache shape and Hq. */
-size_t sep_decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D);
+                    int Hq, float scale, void* out, float* lse, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* sep_status_string(int status);

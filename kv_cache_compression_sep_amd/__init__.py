@@ -129,10 +129,10 @@ def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: floa
 
 class SepCache:
     """A batch of four-block caches in device memory (layout: see sep_cache
-    in include/sepattn.h). Also owns the decode workspace."""
+    in include/sepattn.h)."""
 
     def __init__(self, B: int, Hkv: int, D: int, a: int, s: int, p: int, w: int,
-                 dtype=torch.bfloat16, device="cuda", Hq: int | None = None):
+                 dtype=torch.bfloat16, device="cuda"):
         self.B, self.Hkv, self.D = B, Hkv, D
         self.a, self.s, self.p, self.w = a, s, p, w
         self.c = a + s + p + w
@@ -143,24 +143,11 @@ class SepCache:
         self.pos = torch.full((B, self.c), -1, dtype=torch.int32, device=dev)
         self.tok = torch.full((B, self.c), -1, dtype=torch.int32, device=dev)
         self.state = torch.zeros((B, 4), dtype=torch.int64, device=dev)
-        self._ws = None
-        self._ws_hq = None
-        if Hq is not None:
-            self.workspace(Hq)
 
     def struct(self) -> _lib.SepCacheStruct:
         return _lib.SepCacheStruct(self.a, self.s, self.p, self.w, self.B, self.Hkv, self.D,
                                    _dtype_code(self.k), self.k.data_ptr(), self.v.data_ptr(),
                                    self.pos.data_ptr(), self.tok.data_ptr(), self.state.data_ptr())
-
-    def workspace(self, Hq: int):
-        if self._ws is None or self._ws_hq != Hq:
-            nbytes = _lib.load().sep_decode_workspace_bytes(self.B, Hq, self.Hkv, self.c, self.D)
-            if nbytes == 0:
-                raise ValueError("invalid decode shape")
-            self._ws = torch.zeros((nbytes,), dtype=torch.uint8, device=self.k.device)
-            self._ws_hq = Hq
-        return self._ws
 
     def reset(self):
         sep_cache_reset(self)
@@ -209,10 +196,8 @@ def sep_attn_decode(q, k_new, v_new, cache: SepCache, scale: float | None = None
     out = torch.empty_like(q) if out is None else out
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ws = cache.workspace(Hq)
     st = cache.struct()
     code = lib.sep_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ctypes.byref(st),
-                               Hq, float(scale), out.data_ptr(), _ptr(lse), ws.data_ptr(),
-                               ws.numel(), _stream())
+                               Hq, float(scale), out.data_ptr(), _ptr(lse), _stream())
     _lib.check("sep_attn_decode", code)
     return (out, lse) if return_lse else out

@@ -17,7 +17,6 @@ LIB_PATH = os.environ.get("SEPATTN_LIB", os.path.join(HERE, "libsepattn.so"))
 c_int = ctypes.c_int
 c_float = ctypes.c_float
 c_vp = ctypes.c_void_p
-c_size = ctypes.c_size_t
 
 SEP_OK = 0
 SEP_ERR_NULL = -1
@@ -51,8 +50,7 @@ SIGNATURES = {
     "sep_cache_update": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp, c_vp, c_vp, c_int, c_vp,
                                  c_int, c_vp]),
     "sep_attn_decode": (c_int, [c_vp, c_vp, c_vp, ctypes.POINTER(SepCacheStruct), c_int, c_float,
-                                c_vp, c_vp, c_vp, c_size, c_vp]),
-    "sep_decode_workspace_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
+                                c_vp, c_vp, c_vp]),
     "sep_status_string": (ctypes.c_char_p, [c_int]),
     "sep_version": (c_int, []),
 }

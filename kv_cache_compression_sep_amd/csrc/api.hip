@@ -51,7 +51,7 @@ const char* sep_status_string(int s) {
     case SEP_ERR_SHAPE: return "a size is out of range or inconsistent";
     case SEP_ERR_PARAM: return "a parameter breaks the Sep-Attention / cache contract";
     case SEP_ERR_DTYPE: return "dtype not supported by this entry point";
-    case SEP_ERR_WORKSPACE: return "workspace missing or too small";
+    case SEP_ERR_WORKSPACE: return "reserved";
     case SEP_ERR_HIP: return "HIP launch failure";
     case SEP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     default: return "unknown status";
@@ -129,14 +129,8 @@ int sep_cache_update(const sep_cache* cache, const void* k_new, const void* v_ne
       sep::launch_cache_update(*cache, k_new, v_new, ids_new, T, sep_ids, n_sep_ids, stream));
 }
 
-size_t sep_decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
-  return sep::decode_workspace_bytes(B, Hq, Hkv, c, D);
-}
-
 int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
-                    int Hq, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    int Hq, float scale, void* out, float* lse, hipStream_t stream) {
   int st = check_cache(cache);
   if (st != SEP_OK) return st;
   st = check_cache_kv(cache);
@@ -145,12 +139,9 @@ int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const s
   if (cache->dtype != SEP_BF16) return SEP_ERR_DTYPE;
   if (Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return SEP_ERR_SHAPE;
   if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
-  const int cap = cache->a + cache->s + cache->p + cache->w;
-  const size_t need = sep::decode_workspace_bytes(cache->B, Hq, cache->Hkv, cap, cache->D);
-  if (ws == nullptr || ws_bytes < need) return SEP_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || !aligned16(ws))
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return SEP_ERR_ALIGN;
-  return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, out, lse, ws, stream));
+  return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, out, lse, stream));
 }
 
 }  // extern "C"

@@ -7,26 +7,25 @@
 // retained KV are read). The slot order does not matter for the result, so
 // the retained entries are enumerated as a virtual list
 //   u in [0, n_init)                 -> slot u
-//   u in [n_init, n_init + cnt)      -> separator-ring slots
+//   u in [n_init, n_init + cnt)      -> separator-ring slots, oldest first
 //   u in [.., occ)                   -> recent-ring slots of positions [rec_lo, t)
 //   u == occ                         -> the new token (k_new / v_new)
 //
-// Grid (split, kv head, sequence): each workgroup takes one contiguous chunk
-// of the virtual list for the G query heads of its kv head. Each wave owns a
-// 32-key slice per iteration: S^T = K Q^T with the 16x16x32 bf16 MFMA (K rows
-// read straight from HBM into the A operand, Q^T in registers), online
-// softmax per head column, then O^T += V^T P^T with V staged transposed in
-// the wave's own LDS slice. Waves merge through LDS; splits merge through
-// the workspace, the last workgroup of a (sequence, kv head) to finish doing
-// the final normalisation (ticket counter, reset to zero afterwards).
+// One workgroup per (kv head, sequence) reads that list once. No split of a
+// list over workgroups: merging splits would need a device-scope release and
+// acquire per workgroup, which on this GPU write back and invalidate the L2
+// of each XCD. Waves take 32-key slices, NW slices per iteration: S^T = K Q^T
+// with the 16x16x32 bf16 MFMA (K rows loaded straight into the A operand,
+// Q^T of the G query heads in registers), online softmax per head column,
+// then O^T += V^T P^T with V staged transposed in the wave's LDS slice. The
+// next slice's K and V rows are loaded while the current one is computed.
+// Waves merge through LDS at the end.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace sep {
 
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kSlice = 32;                       // keys per wave per iteration
+constexpr int kSlice = 32;  // keys per wave per iteration
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -37,49 +36,35 @@ struct DecodeArgs {
   const int64_t* state;
   uint16_t* out;
   float* lse;
-  float* part;       // [B*Hkv, nsplit, G*(D+2)]
-  int* tickets;      // [B*Hkv]
-  int a, s, p, w, c, Hq, Hkv, G, nsplit;
+  int a, s, p, w, c, Hq, Hkv, G;
   float scale_log2;
 };
 
-size_t decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D) {
-  (void)c;
-  const int G = Hq / Hkv;
-  const size_t rec = static_cast<size_t>(G) * (D + 2) * sizeof(float);
-  size_t bytes = static_cast<size_t>(B) * Hkv * kDecodeMaxSplit * rec;
-  bytes = (bytes + 255) & ~static_cast<size_t>(255);
-  bytes += static_cast<size_t>(B) * Hkv * sizeof(int);
-  return (bytes + 255) & ~static_cast<size_t>(255);
-}
-
-static inline size_t tickets_offset(int B, int Hkv, int G, int D) {
-  const size_t rec = static_cast<size_t>(G) * (D + 2) * sizeof(float);
-  size_t bytes = static_cast<size_t>(B) * Hkv * kDecodeMaxSplit * rec;
-  return (bytes + 255) & ~static_cast<size_t>(255);
-}
-
-template <int D>
-__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
+  constexpr int NT = NW * kWave;
   constexpr int VSTR = kSlice + 8;               // V^T row stride (bf16)
   constexpr int NDB = D / 16;                    // 16-row d-blocks of O^T
   constexpr int NKS = D / 32;                    // k-steps of QK^T
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDecWaves][D * VSTR];
-  __shared__ float red_m[kDecWaves][16];
-  __shared__ float red_l[kDecWaves][16];
-  __shared__ float red_o[kDecWaves][16][D + 1];
-  __shared__ int last_flag;
+  constexpr int PAIRS = 8 * (D / 8);             // (key quad, 16-byte chunk) pairs per slice
+  constexpr int NPAIR = PAIRS / kWave;
+  constexpr int VT_BYTES = NW * D * VSTR * 2;
+  constexpr int RED_BYTES = NW * 16 * (D + 1) * 4;
+  constexpr int ARENA = VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES;
+  __shared__ __attribute__((aligned(16))) char arena[ARENA];
+  __shared__ float red_m[NW][16];
+  __shared__ float red_l[NW][16];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  const int sp = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
   const int G = A.G;
   const int rw = A.p + A.w;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(arena) + wave * (D * VSTR);
 
-  // ---- cache geometry of this sequence
+  // ---- cache geometry of this sequence (wave-uniform scalars)
   const int64_t* st = A.state + 4 * static_cast<int64_t>(b);
   const int64_t t = st[0];
   const int64_t K = st[1];
@@ -89,11 +74,16 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
   const int64_t cend = A.a + K * (A.p + 1);
   const int64_t rec_lo = cend > A.a ? cend : A.a;
   const int n_rec = static_cast<int>(t > rec_lo ? t - rec_lo : 0);
-  const int occ = n_init + cnt + n_rec;
+  const int u_s = n_init;                        // first separator-ring entry
+  const int u_r = n_init + cnt;                  // first recent-ring entry
+  const int occ = u_r + n_rec;
   const int L = occ + 1;
-  const int chunk = (L + A.nsplit - 1) / A.nsplit;
-  const int u_begin = sp * chunk;
-  const int u_end = min(L, u_begin + chunk);
+  int s0 = 0;                                    // ring index of the oldest separator
+  if (cnt > 0) {
+    s0 = (head - cnt) % A.s;
+    if (s0 < 0) s0 += A.s;
+  }
+  const int r0 = n_rec > 0 ? static_cast<int>((rec_lo - A.a) % rw) : 0;
 
   const int64_t bg = static_cast<int64_t>(b) * A.Hkv + g;
   const uint16_t* kbase = A.kc + bg * A.c * D;
@@ -101,22 +91,21 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
   const uint16_t* knew = A.k_new + bg * D;
   const uint16_t* vnew = A.v_new + bg * D;
 
-  // row pointer of virtual key u (clamped keys are masked later)
-  auto row_of = [&](int u, const uint16_t* base, const uint16_t* nw) -> const uint16_t* {
-    if (u >= occ) return nw;
-    int slot;
-    if (u < n_init) {
-      slot = u;
-    } else if (u < n_init + cnt) {
-      int r = head - cnt + (u - n_init);
-      r %= A.s;
-      if (r < 0) r += A.s;
-      slot = A.a + r;
-    } else {
-      const int64_t x = rec_lo + (u - n_init - cnt);
-      slot = A.a + A.s + static_cast<int>((x - A.a) % rw);
+  // slot of virtual key u (u < occ); keys past the list are clamped by callers
+  auto slot_of = [&](int u) -> int {
+    if (u < u_s) return u;
+    if (u < u_r) {
+      int r = s0 + (u - u_s);
+      r = r >= A.s ? r - A.s : r;
+      return A.a + r;
     }
-    return base + static_cast<int64_t>(slot) * D;
+    int r = r0 + (u - u_r);
+    r = r >= rw ? r - rw : r;
+    return A.a + A.s + r;
+  };
+  auto row_ptr = [&](int u, const uint16_t* base, const uint16_t* nw) -> const uint16_t* {
+    if (u >= occ) return nw;
+    return base + static_cast<int64_t>(slot_of(u)) * D;
   };
 
   // ---- Q^T fragments: lane l holds head l%16 (zero beyond G),
@@ -139,48 +128,56 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
   float m_run = -INFINITY, l_run = 0.0f;
   const int hh = lane / 16;
 
-  const int span = u_end - u_begin;
-  const int iters = span > 0 ? (span + kDecWaves * kSlice - 1) / (kDecWaves * kSlice) : 0;
-  for (int it = 0; it < iters; ++it) {
-    const int u0 = u_begin + (it * kDecWaves + wave) * kSlice;   // this wave's slice
-    // ---- K fragments for two 16-key groups: lane row = key u0 + 16*gq + l%16
-    bf16x8 kf[2][NKS];
+  // ---- per-slice loads into registers
+  struct Regs {
+    u32x4 k[2][NKS];
+    u32x4 v[NPAIR][4];
+  };
+  auto load_slice = [&](int u0, Regs& R) {
 #pragma unroll
     for (int gq = 0; gq < 2; ++gq) {
-      const int u = u0 + 16 * gq + lane % 16;
-      const uint16_t* kr = row_of(u < u_end ? u : u_begin, kbase, knew);
+      const int u = min(u0 + 16 * gq + lane % 16, L - 1);
+      const uint16_t* kr = row_ptr(u, kbase, knew);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        kf[gq][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + 32 * ks + 8 * hh));
+        R.k[gq][ks] = *reinterpret_cast<const u32x4*>(kr + 32 * ks + 8 * hh);
     }
-    // ---- V rows -> transposed LDS slice. Pair index pi = (quad kq, chunk dc).
-    //      Quads q (keys 4q..4q+3) go to column 8*(q%4) + 4*(q/4), so the
-    //      eight keys a PV lane group needs ({4h..4h+3} and {16+4h..16+4h+3})
-    //      are contiguous.
-    constexpr int PAIRS = 8 * (D / 8);
 #pragma unroll
-    for (int pi0 = 0; pi0 < PAIRS; pi0 += kWave) {
-      const int pi = pi0 + lane;
+    for (int j = 0; j < NPAIR; ++j) {
+      const int pi = j * kWave + lane;
       const int kq = pi % 8;
       const int dc = pi / 8;
-      u32x4 vr[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int u = u0 + 4 * kq + e;
-        const uint16_t* vrp = row_of(u < u_end ? u : u_begin, vbase, vnew);
-        vr[e] = *reinterpret_cast<const u32x4*>(vrp + 8 * dc);
+        const int u = min(u0 + 4 * kq + e, L - 1);
+        R.v[j][e] = *reinterpret_cast<const u32x4*>(row_ptr(u, vbase, vnew) + 8 * dc);
       }
+    }
+  };
+
+  const int iters = (L + NW * kSlice - 1) / (NW * kSlice);
+  Regs cur;
+  load_slice(wave * kSlice, cur);
+  for (int it = 0; it < iters; ++it) {
+    const int u0 = (it * NW + wave) * kSlice;   // this wave's slice
+    // ---- V rows -> transposed LDS slice. Quads q (keys 4q..4q+3) go to
+    //      column 8*(q%4) + 4*(q/4), so the eight keys a PV lane group needs
+    //      ({4h..4h+3} and {16+4h..16+4h+3}) are contiguous.
+#pragma unroll
+    for (int j = 0; j < NPAIR; ++j) {
+      const int pi = j * kWave + lane;
+      const int kq = pi % 8;
+      const int dc = pi / 8;
       const int col = 8 * (kq % 4) + 4 * (kq / 4);
-      uint16_t* V = vt[wave];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t w01e = __builtin_amdgcn_perm(vr[1][m], vr[0][m], 0x05040100u);
-        const uint32_t w23e = __builtin_amdgcn_perm(vr[3][m], vr[2][m], 0x05040100u);
-        const uint32_t w01o = __builtin_amdgcn_perm(vr[1][m], vr[0][m], 0x07060302u);
-        const uint32_t w23o = __builtin_amdgcn_perm(vr[3][m], vr[2][m], 0x07060302u);
+        const uint32_t w01e = __builtin_amdgcn_perm(cur.v[j][1][m], cur.v[j][0][m], 0x05040100u);
+        const uint32_t w23e = __builtin_amdgcn_perm(cur.v[j][3][m], cur.v[j][2][m], 0x05040100u);
+        const uint32_t w01o = __builtin_amdgcn_perm(cur.v[j][1][m], cur.v[j][0][m], 0x07060302u);
+        const uint32_t w23o = __builtin_amdgcn_perm(cur.v[j][3][m], cur.v[j][2][m], 0x07060302u);
         const int d = 8 * dc + 2 * m;
-        *reinterpret_cast<u32x2*>(V + d * VSTR + col) = u32x2{w01e, w23e};
-        *reinterpret_cast<u32x2*>(V + (d + 1) * VSTR + col) = u32x2{w01o, w23o};
+        *reinterpret_cast<u32x2*>(vt + d * VSTR + col) = u32x2{w01e, w23e};
+        *reinterpret_cast<u32x2*>(vt + (d + 1) * VSTR + col) = u32x2{w01o, w23o};
       }
     }
     // ---- scores S^T: lane l holds head l%16, keys 16*gq + 4*(l/16) + r
@@ -189,16 +186,20 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
     for (int gq = 0; gq < 2; ++gq) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = mfma16x16x32(kf[gq][ks], qf[ks], acc);
+      for (int ks = 0; ks < NKS; ++ks)
+        acc = mfma16x16x32(__builtin_bit_cast(bf16x8, cur.k[gq][ks]), qf[ks], acc);
       s[gq] = acc;
     }
+    // ---- start the next slice's loads while this one is finished
+    if (it + 1 < iters) load_slice(((it + 1) * NW + wave) * kSlice, cur);
+
     float mx = -INFINITY;
 #pragma unroll
     for (int gq = 0; gq < 2; ++gq)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int u = u0 + 16 * gq + 4 * hh + r;
-        if (u >= u_end) s[gq][r] = -INFINITY;
+        if (u >= L) s[gq][r] = -INFINITY;
         mx = fmaxf(mx, s[gq][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -224,7 +225,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
     __syncthreads();  // V^T slices written
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* vrow = vt[wave] + (16 * db + lane % 16) * VSTR + 8 * hh;
+      const uint16_t* vrow = vt + (16 * db + lane % 16) * VSTR + 8 * hh;
       const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow));
       oacc[db] = oacc[db] * corr;
       oacc[db] = mfma16x16x32(av, pb, oacc[db]);
@@ -237,6 +238,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
   float lw = l_run;
   lw += __shfl_xor(lw, 16, kWave);
   lw += __shfl_xor(lw, 32, kWave);
+  float* red_o = reinterpret_cast<float*>(arena);   // [NW][16][D + 1], reuses the V^T slices
   if (lane < 16) {
     red_m[wave][lane] = m_run;
     red_l[wave][lane] = lw;
@@ -244,63 +246,36 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs A) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red_o[wave][lane % 16][16 * db + 4 * hh + r] = oacc[db][r];
+    for (int r = 0; r < 4; ++r)
+      red_o[(wave * 16 + lane % 16) * (D + 1) + 16 * db + 4 * hh + r] = oacc[db][r];
   __syncthreads();
-
-  // thread e handles (head, d) pairs of this workgroup's merged partial
-  const int rec = G * (D + 2);
-  float* part = A.part + (bg * A.nsplit + sp) * rec;
-  for (int e = tid; e < G * D; e += kDecThreads) {
+  for (int e = tid; e < G * D; e += NT) {
     const int hq = e / D;
     const int d = e % D;
     float M = -INFINITY;
-    for (int wv = 0; wv < kDecWaves; ++wv) M = fmaxf(M, red_m[wv][hq]);
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, red_m[wv][hq]);
     float o = 0.f, l = 0.f;
-    for (int wv = 0; wv < kDecWaves; ++wv) {
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
       const float f = (red_m[wv][hq] == -INFINITY) ? 0.f : fast_exp2(red_m[wv][hq] - M);
-      o += f * red_o[wv][hq][d];
+      o += f * red_o[(wv * 16 + hq) * (D + 1) + d];
       l += f * red_l[wv][hq];
     }
-    part[hq * (D + 2) + d] = o;
-    if (d == 0) {
-      part[hq * (D + 2) + D] = M;
-      part[hq * (D + 2) + D + 1] = l;
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&A.tickets[bg], 1);
-    last_flag = (prev == A.nsplit - 1);
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const float* parts = A.part + bg * A.nsplit * rec;
-  for (int e = tid; e < G * D; e += kDecThreads) {
-    const int hq = e / D;
-    const int d = e % D;
-    float M = -INFINITY;
-    for (int j = 0; j < A.nsplit; ++j) M = fmaxf(M, __builtin_nontemporal_load(parts + j * rec + hq * (D + 2) + D));
-    float o = 0.f, l = 0.f;
-    for (int j = 0; j < A.nsplit; ++j) {
-      const float* pr = parts + j * rec + hq * (D + 2);
-      const float mj = __builtin_nontemporal_load(pr + D);
-      const float f = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
-      o += f * __builtin_nontemporal_load(pr + d);
-      l += f * __builtin_nontemporal_load(pr + D + 1);
-    }
     const int64_t orow = static_cast<int64_t>(b) * A.Hq + g * G + hq;
-    const float val = o / l;
-    const uint32_t bits = pack_bf16x2(val, 0.f);
+    const uint32_t bits = pack_bf16x2(o / l, 0.f);
     A.out[orow * D + d] = static_cast<uint16_t>(bits & 0xffffu);
     if (d == 0 && A.lse != nullptr) A.lse[orow] = (M + fast_log2(l)) * kLn2;
   }
-  if (tid == 0) A.tickets[bg] = 0;
+}
+
+template <int D, int NW>
+static void launch_one(const DecodeArgs& A, int Hkv, int B, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<D, NW>), dim3(Hkv, B), dim3(NW * kWave), 0, st, A);
 }
 
 hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
-                         int Hq, float scale, void* out, float* lse, void* ws, hipStream_t st) {
+                         int Hq, float scale, void* out, float* lse, hipStream_t st) {
   DecodeArgs A;
   A.q = static_cast<const uint16_t*>(q);
   A.k_new = static_cast<const uint16_t*>(k_new);
@@ -318,20 +293,17 @@ hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, co
   A.Hq = Hq;
   A.Hkv = c.Hkv;
   A.G = Hq / c.Hkv;
-  const int pairs = c.B * c.Hkv;
-  int ns = (2048 + pairs - 1) / pairs;
-  const int max_by_len = (A.c + 1 + kSlice - 1) / kSlice;
-  if (ns > max_by_len) ns = max_by_len;
-  if (ns > kDecodeMaxSplit) ns = kDecodeMaxSplit;
-  if (ns < 1) ns = 1;
-  A.nsplit = ns;
-  A.part = static_cast<float*>(ws);
-  A.tickets = reinterpret_cast<int*>(static_cast<char*>(ws) + tickets_offset(c.B, c.Hkv, A.G, c.D));
   A.scale_log2 = scale * kLog2e;
-  if (c.D == 128)
-    hipLaunchKernelGGL(decode_kernel<128>, dim3(ns, c.Hkv, c.B), dim3(kDecThreads), 0, st, A);
-  else
-    hipLaunchKernelGGL(decode_kernel<64>, dim3(ns, c.Hkv, c.B), dim3(kDecThreads), 0, st, A);
+  // Few (sequence, kv head) pairs: wider workgroups so each pair's list is
+  // read by more waves at once.
+  const bool wide = c.B * c.Hkv < 256;
+  if (c.D == 128) {
+    if (wide) launch_one<128, 8>(A, c.Hkv, c.B, st);
+    else launch_one<128, 4>(A, c.Hkv, c.B, st);
+  } else {
+    if (wide) launch_one<64, 8>(A, c.Hkv, c.B, st);
+    else launch_one<64, 4>(A, c.Hkv, c.B, st);
+  }
   return hipGetLastError();
 }
 

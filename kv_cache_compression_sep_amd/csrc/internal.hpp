@@ -27,10 +27,6 @@ hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void
                                const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,
                                hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
-                         int Hq, float scale, void* out, float* lse, void* ws, hipStream_t st);
-
-// Decode split-K geometry shared by the launcher and the workspace query.
-constexpr int kDecodeMaxSplit = 16;
-size_t decode_workspace_bytes(int B, int Hq, int Hkv, int c, int D);
+                         int Hq, float scale, void* out, float* lse, hipStream_t st);
 
 }  // namespace sep

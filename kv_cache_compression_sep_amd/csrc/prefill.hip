@@ -18,24 +18,25 @@
 //     is not fully visible.
 // No other key is touched, so every fully masked block is skipped.
 //
-// Each wave holds 32 query rows of one head. Scores are computed transposed,
-// S^T = K Q^T, with the 32x32 MFMA so that each lane owns one query column:
-// the row max is a max over the lane's 16 values plus one exchange with lane
-// l^32, and the exponentiated scores already sit in the B-operand layout of
-// the P.V product (O^T = V^T P^T). K tiles are staged row-major in LDS; V
-// tiles are staged transposed (d-major) with the key quads permuted so that
-// each lane reads its eight keys with one 16-byte LDS read. Tiles are double
-// buffered: the global loads of tile t+1 are in flight while tile t is
-// computed, and the gather indices run two tiles ahead. Softmax is online in
-// fp32 with exp2 (scale * log2 e folded in) and lazy rescaling: the running
-// max only moves when some row's max grows by more than 8 (log2 units).
+// Each wave holds NQB blocks of 32 query rows of one head. Scores are
+// computed transposed, S^T = K Q^T, with the 32x32 MFMA so that each lane
+// owns one query column: the row max is a max over the lane's values plus
+// one exchange with lane l^32, and the exponentiated scores already sit in
+// the B-operand layout of the P.V product (O^T = V^T P^T). Every K or V
+// fragment read from LDS feeds the NQB blocks. K tiles are staged row-major
+// in LDS; V tiles are staged transposed (d-major) with the key quads
+// permuted so that each lane reads its eight keys with one 16-byte LDS read.
+// Tiles are double buffered: the global loads of tile t+1 are in flight
+// while tile t is computed, and the gather indices run two tiles ahead.
+// Softmax is online in fp32 with exp2 (scale * log2 e folded in) and lazy
+// rescaling: the running max only moves when some row's max grows by more
+// than 8 (log2 units), so exponentials stay below 2^8.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace sep {
 
 constexpr int KT = 64;          // keys per tile
-constexpr int QW = 32;          // query rows per wave
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * kWave;
 constexpr float kLazy = 8.0f;   // lazy-rescale threshold (log2 units)
@@ -55,10 +56,11 @@ struct PrefillArgs {
 };
 
 // ---------------------------------------------------------------- traits
-// bf16 inputs, 32x32x16 bf16 MFMA.
+// bf16 inputs, 32x32x16 bf16 MFMA, two 32-row query blocks per wave.
 template <int D_>
 struct TraitsBF16 {
   static constexpr int D = D_;
+  static constexpr int NQB = 2;
   static constexpr int KS = D / 16;             // k-steps of QK^T
   static constexpr int DB = D / 32;             // d-blocks of O^T
   static constexpr int KSTR = D + 8;            // K row stride (bf16)
@@ -67,7 +69,7 @@ struct TraitsBF16 {
   static constexpr int VBUF = D * VSTR * 2;
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int KLOADS = KT * CPR / NTHREADS;
-  static constexpr int MIN_WAVES = 2;           // waves per SIMD: 256 VGPRs each
+  static constexpr int MIN_WAVES = 1;           // one wave per SIMD: up to 512 registers
   using elem = uint16_t;
   using qfrag = bf16x8;
 
@@ -132,41 +134,49 @@ struct TraitsBF16 {
     }
   }
 
-  // S^T[mb] = K[32 keys of block mb] . Q^T
-  __device__ static void qk(const char* kbuf, int lane, const qfrag (&qf)[KS], f32x16 (&s)[2]) {
+  // S^T[qb][mb] = K[32 keys of block mb] . Q^T[qb]
+  __device__ static void qk(const char* kbuf, int lane, const qfrag (&qf)[NQB][KS],
+                            f32x16 (&s)[NQB][2]) {
     const elem* K = reinterpret_cast<const elem*>(kbuf);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      f32x16 acc = {};
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s[qb][mb] = f32x16{};
       const elem* row = K + (32 * mb + lane % 32) * KSTR + 8 * (lane / 32);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * ks));
-        acc = mfma32x32x16(a, qf[ks], acc);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][mb] = mfma32x32x16(a, qf[qb][ks], s[qb][mb]);
       }
-      s[mb] = acc;
     }
   }
 
-  // O^T += V^T . P^T, P^T taken from the score registers (already
-  // exponentiated, in fp32) and rounded to bf16.
-  __device__ static void pv(const char* vbuf, int lane, const f32x16 (&p)[2], f32x16 (&o)[DB]) {
+  // O^T[qb] += V^T . P^T[qb]; P^T comes from the exponentiated score
+  // registers (fp32), rounded to bf16.
+  __device__ static void pv(const char* vbuf, int lane, const f32x16 (&p)[NQB][2],
+                            f32x16 (&o)[NQB][DB]) {
     const elem* V = reinterpret_cast<const elem*>(vbuf);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const f32x16& src = p[kc >> 1];
-      const int r0 = 8 * (kc & 1);
-      u32x4 pk;
-      pk[0] = pack_bf16x2(src[r0 + 0], src[r0 + 1]);
-      pk[1] = pack_bf16x2(src[r0 + 2], src[r0 + 3]);
-      pk[2] = pack_bf16x2(src[r0 + 4], src[r0 + 5]);
-      pk[3] = pack_bf16x2(src[r0 + 6], src[r0 + 7]);
-      const bf16x8 b = __builtin_bit_cast(bf16x8, pk);
+      bf16x8 b[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const f32x16& src = p[qb][kc >> 1];
+        const int r0 = 8 * (kc & 1);
+        u32x4 pk;
+        pk[0] = pack_bf16x2(src[r0 + 0], src[r0 + 1]);
+        pk[1] = pack_bf16x2(src[r0 + 2], src[r0 + 3]);
+        pk[2] = pack_bf16x2(src[r0 + 4], src[r0 + 5]);
+        pk[3] = pack_bf16x2(src[r0 + 6], src[r0 + 7]);
+        b[qb] = __builtin_bit_cast(bf16x8, pk);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const elem* vrow = V + (32 * db + lane % 32) * VSTR + 16 * kc + 8 * (lane / 32);
         const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow));
-        o[db] = mfma32x32x16(a, b, o[db]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) o[qb][db] = mfma32x32x16(a, b[qb], o[qb][db]);
       }
     }
   }
@@ -179,10 +189,11 @@ struct TraitsBF16 {
   }
 };
 
-// fp32 inputs, 32x32x2 fp32 MFMA (full fp32 products).
+// fp32 inputs, 32x32x2 fp32 MFMA (full fp32 products), one query block.
 template <int D_>
 struct TraitsF32 {
   static constexpr int D = D_;
+  static constexpr int NQB = 1;
   static constexpr int KS = D / 2;
   static constexpr int DB = D / 32;
   static constexpr int KSTR = D + 1;            // odd stride: conflict-free column reads
@@ -231,19 +242,21 @@ struct TraitsF32 {
     }
   }
 
-  __device__ static void qk(const char* kbuf, int lane, const qfrag (&qf)[KS], f32x16 (&s)[2]) {
+  __device__ static void qk(const char* kbuf, int lane, const qfrag (&qf)[NQB][KS],
+                            f32x16 (&s)[NQB][2]) {
     const float* K = reinterpret_cast<const float*>(kbuf);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x16 acc = {};
       const float* row = K + (32 * mb + lane % 32) * KSTR + (lane / 32);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x2f32(row[2 * ks], qf[ks], acc);
-      s[mb] = acc;
+      for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x2f32(row[2 * ks], qf[0][ks], acc);
+      s[0][mb] = acc;
     }
   }
 
-  __device__ static void pv(const char* vbuf, int lane, const f32x16 (&p)[2], f32x16 (&o)[DB]) {
+  __device__ static void pv(const char* vbuf, int lane, const f32x16 (&p)[NQB][2],
+                            f32x16 (&o)[NQB][DB]) {
     const float* V = reinterpret_cast<const float*>(vbuf);
     const int h = lane / 32;
 #pragma unroll
@@ -253,7 +266,7 @@ struct TraitsF32 {
         const int key = 32 * mb + 8 * (r / 4) + 4 * h + (r % 4);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          o[db] = mfma32x32x2f32(V[key * VSTR + 32 * db + lane % 32], p[mb][r], o[db]);
+          o[0][db] = mfma32x32x2f32(V[key * VSTR + 32 * db + lane % 32], p[0][mb][r], o[0][db]);
       }
     }
   }
@@ -268,10 +281,10 @@ struct TileInfo {
   int band_lo, n_init, n_glob, rank_a, ntg, ntiles;
 };
 
-// Key (row to load) and, for the mask, nothing else: masks are recomputed
-// arithmetically at score time.
-__device__ __forceinline__ int tile_key(const TileInfo& ti, const int32_t* sp, int q1, int S, int t,
-                                        int u, bool* is_band) {
+// Row to load for entry u of tile t (keys outside the list are clamped to a
+// valid row; their scores are masked).
+__device__ __forceinline__ int tile_key(const TileInfo& ti, const int32_t* sp, int S, int t, int u,
+                                        bool* is_band) {
   if (t < ti.ntg) {
     *is_band = false;
     const int gu = t * KT + u;
@@ -289,12 +302,14 @@ __global__ void __launch_bounds__(NTHREADS, Tr::MIN_WAVES) prefill_kernel(Prefil
   using elem = typename Tr::elem;
   constexpr int D = Tr::D;
   constexpr int DB = Tr::DB;
+  constexpr int NQB = Tr::NQB;
+  constexpr int QW = 32 * NQB;                  // query rows per wave
 
   // One LDS arena: double-buffered K and V tiles during the key loop, the
-  // normalised output tile in the epilogue.
+  // normalised output tile (one 32-row block per wave at a time) at the end.
   constexpr int OSTR = D + 4;                   // fp32 output-staging row stride
   constexpr int ARENA = 2 * Tr::KBUF + 2 * Tr::VBUF;
-  static_assert(NWAVES * QW * OSTR * 4 <= ARENA, "output staging must fit the arena");
+  static_assert(NWAVES * 32 * OSTR * 4 <= ARENA, "output staging must fit the arena");
   __shared__ __attribute__((aligned(16))) char arena[ARENA];
   __shared__ __attribute__((aligned(16))) int32_t idxbuf[3][KT];
   __shared__ uint64_t sepbits[3];
@@ -349,12 +364,12 @@ __global__ void __launch_bounds__(NTHREADS, Tr::MIN_WAVES) prefill_kernel(Prefil
 
   const elem* kb = reinterpret_cast<const elem*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   const elem* vb = reinterpret_cast<const elem*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  const elem* qb = reinterpret_cast<const elem*>(P.q) + static_cast<int64_t>(b * P.Hq + h) * S * D;
+  const elem* qb_ptr = reinterpret_cast<const elem*>(P.q) + static_cast<int64_t>(b * P.Hq + h) * S * D;
 
   // ---- index stage for tile t into slot t%3 (wave 0 only)
   auto index_load = [&](int t, int& key, uint64_t& bits) {
     bool band;
-    key = tile_key(ti, sp, q1, S, t, lane, &band);
+    key = tile_key(ti, sp, S, t, lane, &band);
     bool f = false;
     if (band) {
       const int j = ti.band_lo + (t - ti.ntg) * KT + lane;
@@ -383,15 +398,21 @@ __global__ void __launch_bounds__(NTHREADS, Tr::MIN_WAVES) prefill_kernel(Prefil
   Tr::store(kbuf(0), vbuf(0), tid, st);
 
   // ---- per-wave query state
-  typename Tr::qfrag qf[Tr::KS];
-  const int qrow = min(qw0 + lane % 32, S - 1);
-  Tr::load_q(qb, qrow, lane, qf);
-  f32x16 oacc[DB];
+  typename Tr::qfrag qf[NQB][Tr::KS];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-  const int qi = qw0 + lane % 32;               // this lane's query row
+  for (int qb = 0; qb < NQB; ++qb)
+    Tr::load_q(qb_ptr, min(qw0 + 32 * qb + lane % 32, S - 1), lane, qf[qb]);
+  f32x16 oacc[NQB][DB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
+  float m_run[NQB], l_run[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
+  }
   const int qmax = min(qw0 + QW - 1, S - 1);
   const int hsel = lane / 32;
 
@@ -417,54 +438,73 @@ __global__ void __launch_bounds__(NTHREADS, Tr::MIN_WAVES) prefill_kernel(Prefil
     }
 
     if (!skip) {
-      f32x16 s[2];
+      f32x16 s[NQB][2];
       Tr::qk(kbuf(cur), lane, qf, s);
       if (need_mask) {
-        const uint64_t bits = sepbits[t % 3];
+        // Lane key offset u = u0 + 4*hsel with u0 a compile-time constant, so
+        // every test below compares against a constant; no branches.
+        const uint64_t lb = sepbits[t % 3] >> (4 * hsel);
+        const uint32_t lo = static_cast<uint32_t>(lb);
+        const uint32_t hi = static_cast<uint32_t>(lb >> 32);
+        const int amj = (band ? P.a - jmin : KT) - 4 * hsel;   // u0 < amj: initial key
+        const int nv = nvalid - 4 * hsel;                      // u0 < nv: listed key
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int dq = qw0 + 32 * qb + lane % 32 - jmin - 4 * hsel;  // u0 <= dq: causal
+          const int dqn = dq - P.n;                                    // u0 > dqn: in window
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int u0 = 32 * mb + 8 * (r / 4) + (r % 4);
+              const uint32_t sb = ((u0 < 32 ? lo >> u0 : hi >> (u0 - 32)) & 1u);
+              const uint32_t vb = static_cast<uint32_t>(u0 <= dq) &
+                                  (static_cast<uint32_t>(u0 > dqn) |
+                                   static_cast<uint32_t>(u0 < amj) | sb);
+              const uint32_t vg = static_cast<uint32_t>(u0 < nv);
+              const uint32_t vis = band ? vb : vg;
+              s[qb][mb][r] = vis ? s[qb][mb][r] : -INFINITY;
+            }
+        }
+      }
+      // ---- online softmax (log2 domain), lazily rescaled
+      float mx[NQB];
+      bool grow = false;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][mb][r]);
+        mx[qb] = fmaxf(m, swap_half(m)) * P.scale_log2;
+        grow |= mx[qb] > m_run[qb] + kLazy;
+      }
+      if (ballot(grow) != 0ull) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float m_new = fmaxf(m_run[qb], mx[qb]);
+          const float corr = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[qb] - m_new);
+          l_run[qb] *= corr;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[qb][db] *= corr;
+          m_run[qb] = m_new;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+        float lsum = 0.0f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int u = 32 * mb + 8 * (r / 4) + 4 * hsel + (r % 4);
-            bool vis;
-            if (band) {
-              const int j = jmin + u;
-              vis = (j <= qi) && ((j < P.a) || (qi - j < P.n) || ((bits >> u) & 1ull));
-            } else {
-              vis = u < nvalid;
-            }
-            s[mb][r] = vis ? s[mb][r] : -INFINITY;
+            const float pv = fast_exp2(__builtin_fmaf(s[qb][mb][r], P.scale_log2, -msub));
+            s[qb][mb][r] = pv;
+            lsum += pv;
           }
+        l_run[qb] += lsum;
       }
-      // ---- online softmax (log2 domain)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      mx = fmaxf(mx, swap_half(mx)) * P.scale_log2;
-      const bool grow = mx > m_run + kLazy;
-      if (ballot(grow) != 0ull) {
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-        l_run *= corr;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= corr;
-        m_run = m_new;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(__builtin_fmaf(s[mb][r], P.scale_log2, -msub));
-          s[mb][r] = pv;
-          lsum += pv;
-        }
-      l_run += lsum;
       Tr::pv(vbuf(cur), lane, s, oacc);
     }
 
@@ -472,36 +512,43 @@ __global__ void __launch_bounds__(NTHREADS, Tr::MIN_WAVES) prefill_kernel(Prefil
     if (more_idx) index_store(t + 2, nkey, nbits);
   }
 
-  // ---- epilogue: normalise, stage through LDS, store coalesced rows
-  const float l_tot = l_run + swap_half(l_run);
-  const float inv = 1.0f / l_tot;
-  __syncthreads();
-  // Each wave writes its 32 x D tile (fp32) into its own slice of the arena.
-  float* slice = reinterpret_cast<float*>(arena) + wave * (QW * OSTR);
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = 32 * db + 8 * j + 4 * hsel;
-      *reinterpret_cast<f32x4*>(slice + (lane % 32) * OSTR + d0) =
-          f32x4{oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
-                oacc[db][4 * j + 3] * inv};
-    }
-  __syncthreads();
+  // ---- epilogue: normalise, stage one 32-row block per wave through LDS,
+  //      store coalesced rows
   elem* ob = reinterpret_cast<elem*>(P.out) + static_cast<int64_t>(b * P.Hq + h) * S * D;
+  float* slice = reinterpret_cast<float*>(arena) + wave * (32 * OSTR);
   constexpr int C4 = D / 4;                     // 4-element groups per row
-  for (int e = lane; e < QW * C4; e += kWave) {
-    const int r = e / C4;
-    const int c = e % C4;
-    const int row = qw0 + r;
-    if (row < S) Tr::write_out(ob + static_cast<int64_t>(row) * D + 4 * c, slice + r * OSTR + 4 * c);
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const float l_tot = l_run[qb] + swap_half(l_run[qb]);
+    const float inv = 1.0f / l_tot;
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * hsel;
+        *reinterpret_cast<f32x4*>(slice + (lane % 32) * OSTR + d0) =
+            f32x4{oacc[qb][db][4 * j] * inv, oacc[qb][db][4 * j + 1] * inv,
+                  oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv};
+      }
+    __syncthreads();
+    const int r0 = qw0 + 32 * qb;
+    for (int e = lane; e < 32 * C4; e += kWave) {
+      const int r = e / C4;
+      const int c = e % C4;
+      const int row = r0 + r;
+      if (row < S) Tr::write_out(ob + static_cast<int64_t>(row) * D + 4 * c, slice + r * OSTR + 4 * c);
+    }
+    const int qi = r0 + lane % 32;
+    if (P.lse != nullptr && lane < 32 && qi < S)
+      P.lse[static_cast<int64_t>(b * P.Hq + h) * S + qi] = (m_run[qb] + fast_log2(l_tot)) * kLn2;
   }
-  if (P.lse != nullptr && lane < 32 && qi < S)
-    P.lse[static_cast<int64_t>(b * P.Hq + h) * S + qi] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 template <class Tr>
-static hipError_t launch(const PrefillArgs& A, hipStream_t st) {
+static hipError_t launch(PrefillArgs A, hipStream_t st) {
+  A.QT = 32 * Tr::NQB * (NWAVES / A.HPW);
+  A.n_qt = (A.S + A.QT - 1) / A.QT;
   const int grid = A.B * A.Hkv * A.n_hg * A.n_qt;
   hipLaunchKernelGGL(prefill_kernel<Tr>, dim3(grid), dim3(NTHREADS), 0, st, A);
   return hipGetLastError();
@@ -528,11 +575,10 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype
   A.n = n;
   A.G = Hq / Hkv;
   A.HPW = (A.G % 4 == 0) ? 4 : ((A.G % 2 == 0) ? 2 : 1);
-  A.QT = QW * (NWAVES / A.HPW);
   A.n_hg = A.G / A.HPW;
-  A.n_qt = (S + A.QT - 1) / A.QT;
   A.scale_log2 = scale * kLog2e;
-  if (dtype == 1) return D == 128 ? launch<TraitsBF16<128>>(A, st) : launch<TraitsBF16<64>>(A, st);
+  if (dtype == SEP_BF16)
+    return D == 128 ? launch<TraitsBF16<128>>(A, st) : launch<TraitsBF16<64>>(A, st);
   return D == 128 ? launch<TraitsF32<128>>(A, st) : launch<TraitsF32<64>>(A, st);
 }
 

@@ -137,16 +137,13 @@ def test_cache_contract_from_the_pages(lib):
 def test_decode_argument_checks(lib):
     E = _lib
     c = _cache()
-    need = lib.sep_decode_workspace_bytes(1, 32, 8, 388, 128)
-    assert need > 0
-    assert lib.sep_decode_workspace_bytes(1, 30, 8, 388, 128) == 0
     dec = lambda cc, **kw: lib.sep_attn_decode(
         kw.get("q", FAKE), FAKE, FAKE, ctypes.byref(cc), kw.get("Hq", 32), kw.get("scale", 0.1),
-        FAKE, None, kw.get("ws", FAKE), kw.get("ws_bytes", need), None)
-    assert dec(c, ws=None) == E.SEP_ERR_WORKSPACE
-    assert dec(c, ws_bytes=need - 1) == E.SEP_ERR_WORKSPACE
+        FAKE, None, None)
     assert dec(c, q=None) == E.SEP_ERR_NULL
     assert dec(c, Hq=12) == E.SEP_ERR_SHAPE
+    assert dec(c, Hq=8 * 17) == E.SEP_ERR_SHAPE
     assert dec(c, scale=-1.0) == E.SEP_ERR_PARAM
     assert dec(_cache(dtype=0)) == E.SEP_ERR_DTYPE
+    assert dec(_cache(s=0)) == E.SEP_ERR_PARAM           # s = 0 needs p = 0
     assert dec(c, q=FAKE + 2) == E.SEP_ERR_ALIGN

@@ -61,7 +61,7 @@ def test_stream_decode_first_65536_steps():
     dq, dk, dv = to_dev(qp, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16")
     d_ids = to_dev(ids[:steps].copy())
     d_sep = to_dev(np.asarray(cfg.sep_ids, np.int32))
-    cache = SepCache(1, cfg.Hkv, cfg.D, cfg.a, cfg.s, cfg.p, cfg.w, Hq=cfg.Hq)
+    cache = SepCache(1, cfg.Hkv, cfg.D, cfg.a, cfg.s, cfg.p, cfg.w)
     outs = torch.empty((steps, cfg.Hq, cfg.D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(cfg.D)
     snaps = {}
@@ -125,7 +125,7 @@ def test_batched_decode_workload():
     print("[batched] inputs ready", flush=True)
     d_ids = to_dev(ids)
     d_sep = to_dev(np.asarray(cfg.sep_ids, np.int32))
-    cache = SepCache(B, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w, Hq=Hq)
+    cache = SepCache(B, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w)
     sep_cache_update(cache, hk, hv, d_ids[:, :H].contiguous(), d_sep)
     torch.cuda.synchronize()
     flags_all = oracle.is_sep(ids, cfg.sep_ids)
