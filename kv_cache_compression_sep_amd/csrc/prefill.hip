@@ -36,6 +36,13 @@
 
 namespace sep {
 
+// Query blocks of 32 rows per wave in the bf16 path (a build-time tuning
+// constant: more blocks reuse each LDS fragment more often but need more
+// registers per wave).
+#ifndef SEPATTN_PREFILL_NQB
+#define SEPATTN_PREFILL_NQB 1
+#endif
+
 constexpr int KT = 64;          // keys per tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * kWave;
@@ -56,11 +63,11 @@ struct PrefillArgs {
 };
 
 // ---------------------------------------------------------------- traits
-// bf16 inputs, 32x32x16 bf16 MFMA, two 32-row query blocks per wave.
+// bf16 inputs, 32x32x16 bf16 MFMA, NQB 32-row query blocks per wave.
 template <int D_>
 struct TraitsBF16 {
   static constexpr int D = D_;
-  static constexpr int NQB = 2;
+  static constexpr int NQB = SEPATTN_PREFILL_NQB;
   static constexpr int KS = D / 16;             // k-steps of QK^T
   static constexpr int DB = D / 32;             // d-blocks of O^T
   static constexpr int KSTR = D + 8;            // K row stride (bf16)
@@ -69,7 +76,7 @@ struct TraitsBF16 {
   static constexpr int VBUF = D * VSTR * 2;
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int KLOADS = KT * CPR / NTHREADS;
-  static constexpr int MIN_WAVES = 1;           // one wave per SIMD: up to 512 registers
+  static constexpr int MIN_WAVES = NQB == 1 ? 2 : 1;   // waves per SIMD the registers allow
   using elem = uint16_t;
   using qfrag = bf16x8;
 
@@ -134,41 +141,38 @@ struct TraitsBF16 {
     }
   }
 
-  // S^T[qb][mb] = K[32 keys of block mb] . Q^T[qb]
-  __device__ static void qk(const char* kbuf, int lane, const qfrag (&qf)[NQB][KS],
-                            f32x16 (&s)[NQB][2]) {
+  // S^T[qb] = K[keys 32*mb .. 32*mb+31] . Q^T[qb]
+  __device__ static void qk_half(const char* kbuf, int lane, const qfrag (&qf)[NQB][KS], int mb,
+                                 f32x16 (&s)[NQB]) {
     const elem* K = reinterpret_cast<const elem*>(kbuf);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int qb = 0; qb < NQB; ++qb) s[qb] = f32x16{};
+    const elem* row = K + (32 * mb + lane % 32) * KSTR + 8 * (lane / 32);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) s[qb][mb] = f32x16{};
-      const elem* row = K + (32 * mb + lane % 32) * KSTR + 8 * (lane / 32);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * ks));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 16 * ks));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][mb] = mfma32x32x16(a, qf[qb][ks], s[qb][mb]);
-      }
+      for (int qb = 0; qb < NQB; ++qb) s[qb] = mfma32x32x16(a, qf[qb][ks], s[qb]);
     }
   }
 
-  // O^T[qb] += V^T . P^T[qb]; P^T comes from the exponentiated score
-  // registers (fp32), rounded to bf16.
-  __device__ static void pv(const char* vbuf, int lane, const f32x16 (&p)[NQB][2],
-                            f32x16 (&o)[NQB][DB]) {
+  // O^T[qb] += V^T[:, keys of half mb] . P^T[qb]; p holds the exponentiated
+  // scores (fp32) of that half, rounded to bf16 here.
+  __device__ static void pv_half(const char* vbuf, int lane, const f32x16 (&p)[NQB], int mb,
+                                 f32x16 (&o)[NQB][DB]) {
     const elem* V = reinterpret_cast<const elem*>(vbuf);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int kc = 2 * mb + c2;
       bf16x8 b[NQB];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const f32x16& src = p[qb][kc >> 1];
-        const int r0 = 8 * (kc & 1);
+        const int r0 = 8 * c2;
         u32x4 pk;
-        pk[0] = pack_bf16x2(src[r0 + 0], src[r0 + 1]);
-        pk[1] = pack_bf16x2(src[r0 + 2], src[r0 + 3]);
-        pk[2] = pack_bf16x2(src[r0 + 4], src[r0 + 5]);
-        pk[3] = pack_bf16x2(src[r0 + 6], src[r0 + 7]);
+        pk[0] = pack_bf16x2(p[qb][r0 + 0], p[qb][r0 + 1]);
+        pk[1] = pack_bf16x2(p[qb][r0 + 2], p[qb][r0 + 3]);
+        pk[2] = pack_bf16x2(p[qb][r0 + 4], p[qb][r0 + 5]);
+        pk[3] = pack_bf16x2(p[qb][r0 + 6], p[qb][r0 + 7]);
         b[qb] = __builtin_bit_cast(bf16x8, pk);
       }
 #pragma unroll
@@ -242,32 +246,26 @@ struct TraitsF32 {
     }
   }
 
-  __device__ static void qk(const char* kbuf, int lane, const qfrag (&qf)[NQB][KS],
-                            f32x16 (&s)[NQB][2]) {
+  __device__ static void qk_half(const char* kbuf, int lane, const qfrag (&qf)[NQB][KS], int mb,
+                                 f32x16 (&s)[NQB]) {
     const float* K = reinterpret_cast<const float*>(kbuf);
+    f32x16 acc = {};
+    const float* row = K + (32 * mb + lane % 32) * KSTR + (lane / 32);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 acc = {};
-      const float* row = K + (32 * mb + lane % 32) * KSTR + (lane / 32);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x2f32(row[2 * ks], qf[0][ks], acc);
-      s[0][mb] = acc;
-    }
+    for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x2f32(row[2 * ks], qf[0][ks], acc);
+    s[0] = acc;
   }
 
-  __device__ static void pv(const char* vbuf, int lane, const f32x16 (&p)[NQB][2],
-                            f32x16 (&o)[NQB][DB]) {
+  __device__ static void pv_half(const char* vbuf, int lane, const f32x16 (&p)[NQB], int mb,
+                                 f32x16 (&o)[NQB][DB]) {
     const float* V = reinterpret_cast<const float*>(vbuf);
     const int h = lane / 32;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * mb + 8 * (r / 4) + 4 * h + (r % 4);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * mb + 8 * (r / 4) + 4 * h + (r % 4);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          o[0][db] = mfma32x32x2f32(V[key * VSTR + 32 * db + lane % 32], p[0][mb][r], o[0][db]);
-      }
+      for (int db = 0; db < DB; ++db)
+        o[0][db] = mfma32x32x2f32(V[key * VSTR + 32 * db + lane % 32], p[0][r], o[0][db]);
     }
   }
 
@@ -438,74 +436,81 @@ __global__ void __launch_bounds__(NTHREADS, Tr::MIN_WAVES) prefill_kernel(Prefil
     }
 
     if (!skip) {
-      f32x16 s[NQB][2];
-      Tr::qk(kbuf(cur), lane, qf, s);
+      // Visibility of this lane's keys, one bit per key of the tile, shifted
+      // so that bit u0 stands for key u0 + 4*hsel (the lane's key for
+      // register r of half mb is u0 = 32*mb + 8*(r/4) + r%4).
+      uint64_t vis[NQB];
       if (need_mask) {
-        // Lane key offset u = u0 + 4*hsel with u0 a compile-time constant, so
-        // every test below compares against a constant; no branches.
-        const uint64_t lb = sepbits[t % 3] >> (4 * hsel);
-        const uint32_t lo = static_cast<uint32_t>(lb);
-        const uint32_t hi = static_cast<uint32_t>(lb >> 32);
-        const int amj = (band ? P.a - jmin : KT) - 4 * hsel;   // u0 < amj: initial key
-        const int nv = nvalid - 4 * hsel;                      // u0 < nv: listed key
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          const int dq = qw0 + 32 * qb + lane % 32 - jmin - 4 * hsel;  // u0 <= dq: causal
-          const int dqn = dq - P.n;                                    // u0 > dqn: in window
+          uint64_t m;
+          if (band) {
+            const int dq = qw0 + 32 * qb + lane % 32 - jmin;     // causal: u <= dq
+            const int wl = dq - P.n + 1;                          // window: u >= wl
+            const int ih = P.a - jmin;                            // initial: u < ih
+            const uint64_t cm = dq >= 63 ? ~0ull : (dq < 0 ? 0ull : ((2ull << dq) - 1));
+            const uint64_t wm = wl <= 0 ? ~0ull : (wl >= 64 ? 0ull : ~((1ull << wl) - 1));
+            const uint64_t im = ih >= 64 ? ~0ull : (ih <= 0 ? 0ull : ((1ull << ih) - 1));
+            m = cm & (wm | im | sepbits[t % 3]);
+          } else {
+            m = nvalid >= 64 ? ~0ull : ((1ull << nvalid) - 1);
+          }
+          vis[qb] = m >> (4 * hsel);
+        }
+      }
+      f32x16 sh[2][NQB];
+      Tr::qk_half(kbuf(cur), lane, qf, 0, sh[0]);
+      Tr::qk_half(kbuf(cur), lane, qf, 1, sh[1]);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 (&s)[NQB] = sh[mb];
+        if (need_mask) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) {
+            const uint32_t word = static_cast<uint32_t>(vis[qb] >> (32 * mb));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int u0 = 32 * mb + 8 * (r / 4) + (r % 4);
-              const uint32_t sb = ((u0 < 32 ? lo >> u0 : hi >> (u0 - 32)) & 1u);
-              const uint32_t vb = static_cast<uint32_t>(u0 <= dq) &
-                                  (static_cast<uint32_t>(u0 > dqn) |
-                                   static_cast<uint32_t>(u0 < amj) | sb);
-              const uint32_t vg = static_cast<uint32_t>(u0 < nv);
-              const uint32_t vis = band ? vb : vg;
-              s[qb][mb][r] = vis ? s[qb][mb][r] : -INFINITY;
+              const uint32_t bit = 1u << (8 * (r / 4) + (r % 4));
+              s[qb][r] = (word & bit) ? s[qb][r] : -INFINITY;
             }
+          }
         }
-      }
-      // ---- online softmax (log2 domain), lazily rescaled
-      float mx[NQB];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][mb][r]);
-        mx[qb] = fmaxf(m, swap_half(m)) * P.scale_log2;
-        grow |= mx[qb] > m_run[qb] + kLazy;
-      }
-      if (ballot(grow) != 0ull) {
+        // ---- online softmax over this half (log2 domain), lazily rescaled
+        float mx[NQB];
+        bool grow = false;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-          const float m_new = fmaxf(m_run[qb], mx[qb]);
-          const float corr = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[qb] - m_new);
-          l_run[qb] *= corr;
+          float m = -INFINITY;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[qb][db] *= corr;
-          m_run[qb] = m_new;
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, s[qb][r]);
+          mx[qb] = fmaxf(m, swap_half(m)) * P.scale_log2;
+          grow |= mx[qb] > m_run[qb] + kLazy;
         }
-      }
+        if (ballot(grow) != 0ull) {
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-        float lsum = 0.0f;
+          for (int qb = 0; qb < NQB; ++qb) {
+            const float m_new = fmaxf(m_run[qb], mx[qb]);
+            const float corr = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run[qb] - m_new);
+            l_run[qb] *= corr;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+            for (int db = 0; db < DB; ++db) oacc[qb][db] *= corr;
+            m_run[qb] = m_new;
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float msub = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+          float lsum = 0.0f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float pv = fast_exp2(__builtin_fmaf(s[qb][mb][r], P.scale_log2, -msub));
-            s[qb][mb][r] = pv;
+            const float pv = fast_exp2(__builtin_fmaf(s[qb][r], P.scale_log2, -msub));
+            s[qb][r] = pv;
             lsum += pv;
           }
-        l_run[qb] += lsum;
+          l_run[qb] += lsum;
+        }
+        Tr::pv_half(vbuf(cur), lane, s, mb, oacc);
       }
-      Tr::pv(vbuf(cur), lane, s, oacc);
     }
 
     if (t + 1 < ti.ntiles) Tr::store(kbuf(cur ^ 1), vbuf(cur ^ 1), tid, st);
