@@ -9,8 +9,9 @@
 // Staging: K and V tiles go straight from global memory into LDS with
 // 16-byte LDS-DMA loads (no registers), into a ring of four stages, three
 // tiles ahead of the tile being computed. Rows are stored row-major with
-// the 16-byte chunk index XOR-swizzled by the row, so that the QK reads (32
-// rows, same chunk) and the transposed V reads hit distinct banks. The data
+// the 16-byte chunk index XOR-swizzled by the row, one swizzle for K (the QK
+// reads take one chunk of 32 rows) and one for V (a transposed read takes 64
+// bytes of 4 rows per half wave), so that both hit distinct banks. The data
 // a tile's gather needs (its slice of sep_pos, or for band tiles two
 // shifted slices of rank whose difference gives the separator bits) also
 // arrives by LDS-DMA, six tiles ahead, into an index ring. So the key loop
@@ -57,11 +58,15 @@ struct Geo {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static_assert(PER_WAVE >= 1, "tile too small for the wave count");
-  // 16-byte slot of (row r, chunk c)
-  __device__ static int slot(int r, int c) {
-    const int sw = CPR == 16 ? (r & 15) : ((r >> 1) & 7);
-    return r * CPR + (c ^ sw);
-  }
+  // 16-byte slot of (row r, chunk c) in a K stage: the QK reads take one
+  // chunk of 32 consecutive rows, so the chunk is XOR-ed with the row.
+  __device__ static int swz_k(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int slot(int r, int c) { return r * CPR + (c ^ swz_k(r)); }
+  // ... and in a V stage: a transposed read covers 4 consecutive rows x 64
+  // bytes per 32 lanes, so rows that share bank positions get their chunk
+  // groups of four exchanged.
+  __device__ static int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  __device__ static int slot_v(int r, int c) { return r * CPR + (c ^ swz_v(r)); }
 };
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -97,6 +102,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Asynchronous global -> LDS copies. Lane l's 16 (or 4) bytes land at LDS
 // address lds_base + 16*l (or + 4*l); lds_base is wave-uniform. There is no
 // register result, so nothing waits for them except the explicit vmcnt.
+// M0 carries the LDS base; the kernel makes no other use of M0 (no LDS-DMA
+// builtins, no message or GWS instructions), so setting it inside the asm
+// statement cannot disturb compiler-generated code.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_x4(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(lds_base) : "memory", "m0");
@@ -105,6 +115,8 @@ __device__ __forceinline__ void dma_x1(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(g), "s"(lds_base) : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ v4i16 read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
@@ -195,11 +207,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       const int sl = ins * kWave + lane;               // 16-byte slot this lane fills
       const int r = sl / CPR;
       const int pos = sl % CPR;
-      const int sw = CPR == 16 ? (r & 15) : ((r >> 1) & 7);
-      const int c = pos ^ sw;                          // chunk that belongs in that slot
-      const int64_t off = real ? static_cast<int64_t>(key_of(t, r)) * D + 8 * c : 0;
-      dma_x4(kb + off, __builtin_amdgcn_readfirstlane(lds_addr(kst + ins * 1024)));
-      dma_x4(vb + off, __builtin_amdgcn_readfirstlane(lds_addr(vst + ins * 1024)));
+      const int64_t row = real ? static_cast<int64_t>(key_of(t, r)) * D : 0;
+      const int64_t offk = real ? row + 8 * (pos ^ G::swz_k(r)) : 0;   // chunk that belongs in that slot
+      const int64_t offv = real ? row + 8 * (pos ^ G::swz_v(r)) : 0;
+      dma_x4(kb + offk, __builtin_amdgcn_readfirstlane(lds_addr(kst + ins * 1024)));
+      dma_x4(vb + offv, __builtin_amdgcn_readfirstlane(lds_addr(vst + ins * 1024)));
     }
   };
 
@@ -329,7 +341,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
             for (int e = 0; e < 2; ++e) {
               const int R = 16 * kc + 8 * e + 4 * th + tj / 4;
               const int dcol = 32 * db + 16 * tdh + 4 * (tj % 4);
-              x[e] = read_tr16(vst + 16 * G::slot(R, dcol / 8) + 2 * (dcol % 8));
+              x[e] = read_tr16(vst + 16 * G::slot_v(R, dcol / 8) + 2 * (dcol % 8));
             }
             const v8i16 cat = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
             oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, cat), pb, oacc[db]);
