@@ -28,6 +28,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # the LDS-DMA asm statements name M0 (reserved) as clobbered on purpose
+    "-Wno-inline-asm",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

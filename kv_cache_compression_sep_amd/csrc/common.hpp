@@ -34,6 +34,30 @@ __device__ __forceinline__ float swap_half(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
+// Max and sum of a value over lanes l and l^32, without LDS. One
+// v_permlane32_swap on two copies of x exchanges the high half of the first
+// with the low half of the second, so that afterwards one copy holds the low
+// half of x on every lane and the other the high half. The swap is written
+// as inline asm: the compiler's builtin for it loses one of the two results
+// when both inputs are the same value. The s_nop pairs cover the VALU
+// write -> permlane read and permlane write -> VALU read hazards.
+__device__ __forceinline__ void lane_halves(float x, float* lo, float* hi) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), w = u;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(u), "+v"(w));
+  *lo = __builtin_bit_cast(float, u);
+  *hi = __builtin_bit_cast(float, w);
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a, b;
+  lane_halves(x, &a, &b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a, b;
+  lane_halves(x, &a, &b);
+  return a + b;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

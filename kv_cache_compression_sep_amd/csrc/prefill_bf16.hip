@@ -7,31 +7,37 @@
 // every K/V tile staged in LDS feeds 8 x 32 query rows.
 //
 // Staging: K and V tiles go straight from global memory into LDS with
-// 16-byte LDS-DMA loads (no registers), into a ring of four stages, three
-// tiles ahead of the tile being computed. Rows are stored row-major with
-// the 16-byte chunk index XOR-swizzled by the row, one swizzle for K (the QK
-// reads take one chunk of 32 rows) and one for V (a transposed read takes 64
-// bytes of 4 rows per half wave), so that both hit distinct banks. The data
-// a tile's gather needs (its slice of sep_pos, or for band tiles two
-// shifted slices of rank whose difference gives the separator bits) also
-// arrives by LDS-DMA, six tiles ahead, into an index ring. So the key loop
-// has no global load with a register result: every wait is explicit. Each
-// wave issues exactly OPS + 1 loads per iteration (a fixed dummy address
-// past the last tile), waits with one exact vmcnt for its own loads of the
-// current tile, and a plain barrier publishes them.
+// 16-byte LDS-DMA loads (no registers), each into a ring of four stages.
+// K of tile t + 3 and V of tile t + 2 are issued in iteration t. Rows are
+// stored row-major with the 16-byte chunk index XOR-swizzled by the row, one
+// swizzle for K (the QK reads take one chunk of 32 rows) and one for V (a
+// transposed read takes 64 bytes of 4 rows per half wave), so that both hit
+// distinct banks. The data a tile's gather needs (its slice of sep_pos, or
+// for band tiles two shifted slices of rank whose difference gives the
+// separator bits) also arrives by LDS-DMA, six tiles ahead, into an index
+// ring. So the key loop has no global load with a register result: every
+// wait is explicit. Each wave issues exactly 1 + OPS loads per iteration (a
+// fixed dummy address past the last tile), waits with one exact vmcnt for
+// its own loads of K(t) and V(t - 1), and a plain barrier publishes them.
 //
 // Scores are computed transposed, S^T = K Q^T: each lane owns one query
 // column, so a row max is a max over the lane's registers plus one exchange
 // with lane l^32, and the exponentiated scores already sit in the B-operand
 // layout of O^T = V^T P^T. The V^T A-operand is read with the LDS transpose
 // load (ds_read_b64_tr_b16): pointing a 16-lane group at four consecutive key
-// rows gives each lane four keys of one d column. Per tile, QK of the second
-// 32-key half is issued before the softmax of the first half and PV of the
-// first half before the softmax of the second. Softmax is online in fp32 in
+// rows gives each lane four keys of one d column.
+//
+// Software pipeline: iteration t issues QK of tile t, then PV of tile t - 1
+// (P kept packed in registers, V still in its stage), then the softmax of
+// tile t. The softmax VALU work therefore overlaps the PV MFMAs of the
+// previous tile instead of waiting for its own. Softmax is online in fp32 in
 // the log2 domain with lazy rescaling (the running max moves only when a
-// row's max grows by more than 8), P is rounded to bf16 for the PV product.
+// row's max grows by more than 8); a move scales l at once and O just before
+// the next PV. P is rounded to bf16 for the PV product; l sums it in fp32.
 #include "prefill.hpp"
 #include "internal.hpp"
+
+#include <type_traits>
 
 namespace sep {
 namespace {
@@ -39,11 +45,13 @@ namespace {
 constexpr int KT = 64;                 // keys per tile
 constexpr int NW = 8;                  // waves per workgroup
 constexpr int NT = NW * kWave;
-constexpr int STAGES = 4;              // LDS ring depth (tiles)
-constexpr int AHEAD = STAGES - 1;      // tiles in flight ahead of the current one
+constexpr int STAGES = 4;              // LDS ring depth (tiles), K and V each
+constexpr int KAHEAD = 3;              // K of tile t + KAHEAD is issued in iteration t
+constexpr int VAHEAD = 2;              // V of tile t + VAHEAD is issued in iteration t
 constexpr int IAHEAD = 6;              // index slices loaded this many tiles ahead
 constexpr int IDXR = 8;                // index ring depth (> IAHEAD)
 constexpr float kLazy = 8.0f;
+static_assert(KAHEAD < STAGES && VAHEAD + 1 < STAGES, "ring too shallow for the pipeline");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -54,7 +62,7 @@ struct Geo {
   static constexpr int TB = KT * D * 2;                // bytes of one K (or V) tile
   static constexpr int INSTR = TB / 1024;              // wave-wide 1 KB loads per tile
   static constexpr int PER_WAVE = INSTR / NW;          // per wave, per tensor
-  static constexpr int OPS = 2 * PER_WAVE;             // LDS-DMA ops per wave per tile
+  static constexpr int OPS = 2 * PER_WAVE;             // K + V LDS-DMA ops per wave per iteration
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static_assert(PER_WAVE >= 1, "tile too small for the wave count");
@@ -78,12 +86,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-// Wait until this wave's loads of tile t landed, then a plain barrier.
-// Memory ops of a wave in issue order: the index slices of tiles 0..5 (one
-// op each), [full wait], tiles 0, 1, 2 (OPS each); then per iteration one
-// index-slice op followed by the OPS loads of tile t + 3. Ops issued after
-// tile t's loads, at the top of iteration t: t = 0: 2*OPS; t = 1:
-// 2*OPS + 1; t >= 2: 2*OPS + 2. Loads complete in issue order.
+// Wait until this wave's loads of K(t) and V(t - 1) landed (and its LDS
+// reads of the previous iteration completed), then a plain barrier. Memory
+// ops of a wave in issue order: the index slices of tiles 0..5, [full
+// wait], K(0); K(1), V(0); K(2), V(1); then per iteration t: one index
+// slice, K(t + 3), V(t + 2). Both K(t) and V(t - 1) are issued in
+// iteration t - 3 (or the prologue), V last; the ops issued after them are
+// t = 0: 2*OPS; t = 1: 2*OPS + 1; t >= 2: 2*OPS + 2. Loads complete in
+// issue order.
 template <int OPS>
 __device__ __forceinline__ void tile_barrier(int t) {
   compiler_fence();
@@ -99,28 +109,35 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
 
-// Asynchronous global -> LDS copies. Lane l's 16 (or 4) bytes land at LDS
-// address lds_base + 16*l (or + 4*l); lds_base is wave-uniform. There is no
-// register result, so nothing waits for them except the explicit vmcnt.
-// M0 carries the LDS base; the kernel makes no other use of M0 (no LDS-DMA
-// builtins, no message or GWS instructions), so setting it inside the asm
-// statement cannot disturb compiler-generated code.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_x4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_base) : "memory", "m0");
+// Asynchronous global -> LDS copies from a wave-uniform base address plus a
+// per-lane 32-bit byte offset. Lane l's 16 (or 4) bytes land at LDS address
+// lds_base + 16*l (or + 4*l); lds_base is wave-uniform. There is no register
+// result, so nothing waits for them except the explicit vmcnt. M0 carries
+// the LDS base; the kernel makes no other use of M0 (no LDS-DMA builtins, no
+// message or GWS instructions), so setting it inside the asm statement
+// cannot disturb compiler-generated code.
+__device__ __forceinline__ void dma_x4(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
-__device__ __forceinline__ void dma_x1(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(lds_base) : "memory", "m0");
+__device__ __forceinline__ void dma_x1(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
-
-#pragma clang diagnostic pop
 
 __device__ __forceinline__ v4i16 read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
 }
+
+// -inf where bit `pos` of `word` is clear (branch-free: extract, then select bits)
+__device__ __forceinline__ float mask_bit(float s, uint32_t word, int pos) {
+  const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(word), pos, 1));
+  const uint32_t x = __builtin_bit_cast(uint32_t, s);
+  return __builtin_bit_cast(float, (x & m) | (0xff800000u & ~m));
+}
+
+template <bool B>
+using flag = std::integral_constant<bool, B>;
 
 template <int D>
 __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
@@ -129,10 +146,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   constexpr int TB = G::TB;
   constexpr int KS = G::KS;
   constexpr int DB = G::DB;
+  constexpr int PW = G::PER_WAVE;
   constexpr int OSTR = D + 8;                          // bf16 output-staging row stride
-  static_assert(NW * 32 * OSTR * 2 <= STAGES * 2 * TB, "output staging must fit the ring");
+  static_assert(NW * 32 * OSTR * 2 <= 2 * STAGES * TB, "output staging must fit the ring");
 
-  __shared__ __attribute__((aligned(1024))) char ring[STAGES * 2 * TB];
+  __shared__ __attribute__((aligned(1024))) char ring[2 * STAGES * TB];   // K stages, then V stages
   __shared__ __attribute__((aligned(16))) int32_t idxr[IDXR][2][KT];   // index slices
   __shared__ __attribute__((aligned(16))) int32_t junk[NW][KT];       // dummy-load targets
 
@@ -158,8 +176,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * S;
   const TileInfo ti = tile_info<KT>(rk, S, P.a, P.n, q0, q1);
 
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
+  const char* kb = reinterpret_cast<const char*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D * 2;
+  const char* vb = reinterpret_cast<const char*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D * 2;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(P.q) + static_cast<int64_t>(b * P.Hq + h) * S * D;
 
   // ---- index slice of tile t into ring slot t % IDXR: wave 0 loads
@@ -169,51 +187,57 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   auto issue_index = [&](int t) {
     const bool real = t < ti.ntiles;
     const bool band = t >= ti.ntg;
-    const int32_t* src = rk;                           // fixed dummy address
+    const int32_t* base = rk;                          // fixed dummy address
+    uint32_t off = 0;
     uint32_t dst = lds_addr(junk[wave]);
     if (real && wave < 2) {
       if (!band) {
         if (wave == 0) {
-          const int si = min(max(ti.rank_a + t * KT + lane - ti.n_init, 0), S - 1);
-          src = sp + si;
+          base = sp;
+          off = 4u * min(max(ti.rank_a + t * KT + lane - ti.n_init, 0), S - 1);
           dst = lds_addr(idxr[t % IDXR][0]);
         }
       } else {
-        const int j = ti.band_lo + (t - ti.ntg) * KT + lane + wave;
-        src = rk + min(j, S);
+        off = 4u * min(ti.band_lo + (t - ti.ntg) * KT + lane + wave, S);
         dst = lds_addr(idxr[t % IDXR][wave]);
       }
     }
-    dma_x1(src, __builtin_amdgcn_readfirstlane(dst));
+    dma_x1(base, off, __builtin_amdgcn_readfirstlane(dst));
   };
-  // key row of entry r of tile t (from the index slice in LDS)
-  auto key_of = [&](int t, int r) -> int {
-    if (t >= ti.ntg) return min(ti.band_lo + (t - ti.ntg) * KT + r, S - 1);
-    const int u = t * KT + r;
-    if (u < ti.n_init) return u;
-    if (u >= ti.n_glob) return 0;
-    return idxr[t % IDXR][0][r];
-  };
-  // ---- LDS-DMA of tile t into ring stage t % STAGES. Past the last tile
-  //      the same number of loads is issued (every lane re-reads one
-  //      16-byte chunk into the unused stage).
-  auto issue = [&](int t) {
+  // key rows this lane copies for tile t (row 0 past the last tile)
+  auto rows_of = [&](int t, int (&rows)[PW]) {
     const bool real = t < ti.ntiles;
-    char* kst = ring + (t % STAGES) * 2 * TB;
-    char* vst = kst + TB;
+    const bool band = t >= ti.ntg;
 #pragma unroll
-    for (int i = 0; i < G::PER_WAVE; ++i) {
-      const int ins = wave * G::PER_WAVE + i;          // 1 KB block of the tile
+    for (int i = 0; i < PW; ++i) {
+      const int r = ((wave * PW + i) * kWave + lane) / CPR;
+      int key;
+      if (band) {
+        key = min(ti.band_lo + (t - ti.ntg) * KT + r, S - 1);
+      } else {
+        const int u = t * KT + r;
+        const int gathered = idxr[t % IDXR][0][r];
+        key = u < ti.n_init ? u : (u >= ti.n_glob ? 0 : gathered);
+      }
+      rows[i] = real ? key : 0;
+    }
+  };
+  // ---- LDS-DMA of the K (or V) rows of tile t into stage t % STAGES
+  auto issue_rows = [&](const char* base, char* stage0, int t, const int (&rows)[PW], auto is_v) {
+    char* st = stage0 + (t % STAGES) * TB;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int ins = wave * PW + i;                   // 1 KB block of the tile
       const int sl = ins * kWave + lane;               // 16-byte slot this lane fills
       const int r = sl / CPR;
       const int pos = sl % CPR;
-      const int64_t row = real ? static_cast<int64_t>(key_of(t, r)) * D : 0;
-      const int64_t offk = real ? row + 8 * (pos ^ G::swz_k(r)) : 0;   // chunk that belongs in that slot
-      const int64_t offv = real ? row + 8 * (pos ^ G::swz_v(r)) : 0;
-      dma_x4(kb + offk, __builtin_amdgcn_readfirstlane(lds_addr(kst + ins * 1024)));
-      dma_x4(vb + offv, __builtin_amdgcn_readfirstlane(lds_addr(vst + ins * 1024)));
+      const int c = pos ^ (decltype(is_v)::value ? G::swz_v(r) : G::swz_k(r));   // chunk for that slot
+      const uint32_t off = static_cast<uint32_t>(rows[i]) * (D * 2) + 16u * c;
+      dma_x4(base, off, __builtin_amdgcn_readfirstlane(lds_addr(st + ins * 1024)));
     }
   };
+  char* const kring = ring;
+  char* const vring = ring + STAGES * TB;
 
   // ---- Q fragments first, so that waiting for them never waits for tiles
   bf16x8 qf[KS];
@@ -228,131 +252,240 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   compiler_fence();
   __builtin_amdgcn_s_waitcnt(0);                       // index slices 0..5 landed
   __syncthreads();
-  for (int t = 0; t < AHEAD; ++t) issue(t);
+  int vrows[PW];
+  {
+    int r0[PW], r1[PW];
+    rows_of(0, r0);
+    issue_rows(kb, kring, 0, r0, flag<false>{});
+    rows_of(1, r1);
+    issue_rows(kb, kring, 1, r1, flag<false>{});
+    issue_rows(vb, vring, 0, r0, flag<true>{});
+    rows_of(2, vrows);
+    issue_rows(kb, kring, 2, vrows, flag<false>{});
+    issue_rows(vb, vring, 1, r1, flag<true>{});
+  }
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  u32x4 pk[4];                                         // bf16 P of the previous tile, per 16-key chunk
+  float m_run = -INFINITY, l_run = 0.0f, corr = 1.0f;
+  bool resc = false;
   const int qmax = min(qw0 + 31, S - 1);
   const int hsel = lane / 32;
   const int qi = qw0 + lane % 32;
 
-  // per-lane pieces of the transposed V read address (see pv below)
+  // per-lane LDS byte offsets of the QK reads (chunk 2*ks + hsel of rows
+  // lane%32 [+32]) and of the transposed V reads (see pv below)
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = 16 * G::slot(lane % 32, 2 * ks + hsel);
   const int tg = lane / 16;                            // 16-lane group
   const int tj = lane % 16;
   const int th = tg / 2;                               // key group of the B operand
   const int tdh = tg % 2;                              // which 16 d-columns
+  int voff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int R = 4 * th + tj / 4;
+    const int dcol = 32 * db + 16 * tdh + 4 * (tj % 4);
+    voff[db] = 16 * G::slot_v(R, dcol / 8) + 2 * (dcol % 8);
+  }
 
-  for (int t = 0; t < ti.ntiles; ++t) {
+  // ---- top of iteration t: wait for K(t) and V(t - 1), issue the loads
+  //      of later tiles (none in the last, PV-only iteration)
+  auto advance = [&](int t) {
     tile_barrier<G::OPS>(t);
-    issue_index(t + IAHEAD);
-    issue(t + AHEAD);
+    if (t < ti.ntiles) {
+      issue_index(t + IAHEAD);
+      int rows[PW];
+      rows_of(t + KAHEAD, rows);
+      issue_rows(kb, kring, t + KAHEAD, rows, flag<false>{});
+      issue_rows(vb, vring, t + VAHEAD, vrows, flag<true>{});
+#pragma unroll
+      for (int i = 0; i < PW; ++i) vrows[i] = rows[i];
+    }
+  };
+  // ---- the running max moved in the previous softmax: O to the new scale
+  auto rescale = [&]() {
+    if (resc) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= corr;
+      corr = 1.0f;
+      resc = false;
+    }
+  };
+  // ---- S^T of tile t (two 32-key halves), masked where the tile needs it.
+  //      A band tile whose keys all lie in the future of this wave's rows
+  //      gets an all-zero visibility word, so its P is zero.
+  auto qk = [&](int t, f32x16 (&sh)[2]) {
+    const char* kst = kring + (t % STAGES) * TB;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(kst + koff[ks] + mb * 32 * CPR * 16));
+        acc = mfma32x32x16(a, qf[ks], acc);
+      }
+      sh[mb] = acc;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
-    const char* kst = ring + (t % STAGES) * 2 * TB;
-    const char* vst = kst + TB;
     const bool band = t >= ti.ntg;
     const int jmin = band ? ti.band_lo + (t - ti.ntg) * KT : 0;
     const int nvalid = band ? KT : min(KT, ti.n_glob - t * KT);
-    bool skip = false, need_mask = false;
-    if (band) {
-      if (jmin > qmax || qw0 >= S) skip = true;        // every key in the future
-      else need_mask = !(jmin + KT - 1 <= qw0 && jmin >= qmax - P.n + 1);
-    } else {
-      need_mask = nvalid < KT;
+    const bool full = band ? (jmin + KT - 1 <= qw0 && jmin >= qmax - P.n + 1) : nvalid == KT;
+    if (!full) {
+      uint64_t sepbits = 0;
+      if (band) {
+        const int32_t* sl = idxr[t % IDXR][0];
+        const bool f = (jmin + lane < S) && (idxr[t % IDXR][1][lane] != sl[lane]);
+        sepbits = ballot(f);
+      }
+      const uint64_t vis = vis_word(band, qi, jmin, P.n, P.a, sepbits, nvalid) >> (4 * hsel);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sh[mb][r] = mask_bit(sh[mb][r], word, 8 * (r / 4) + (r % 4));
+      }
     }
+  };
+  // ---- V^T operand of PV MFMA i (16-key chunk kc = i / DB, d block
+  //      db = i % DB) of the tile in V stage vst. O^T += V^T[:, chunk] . P^T:
+  //      lane (16*tg + tj) points at key row 16*kc + 8*e + 4*th + tj/4, d
+  //      column 32*db + 16*tdh + 4*(tj%4); the transpose load returns to
+  //      lane l the keys {16*kc + 8*e + 4*th + k, k = 0..3} at d = 32*db + l%32.
+  auto vread = [&](const char* vst, int i) -> bf16x8 {
+    const int kc = i / DB, db = i % DB;
+    const v4i16 x0 = read_tr16(vst + voff[db] + (16 * kc) * CPR * 16);
+    const v4i16 x1 = read_tr16(vst + voff[db] + (16 * kc + 8) * CPR * 16);
+    const v8i16 cat = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    return __builtin_bit_cast(bf16x8, cat);
+  };
+  constexpr int NMF = 4 * DB;                          // PV MFMAs per tile
+  // ---- PV of the tile in V stage tv (with pk), and, when sh is given, the
+  //      online softmax of the next tile's scores into pk, m, l. The softmax
+  //      is cut into units (two max units, one unit for the running-max
+  //      update, one unit per exponentiated pair of scores) that are issued
+  //      between the PV MFMAs in a fixed order.
+  auto pv_softmax = [&](int tv, f32x16 (*sh)[2]) {
+    const char* vst = vring + (tv % STAGES) * TB;
+    constexpr int NU = 3 + 16;                         // softmax units
+    float m0 = -INFINITY, m1 = -INFINITY, msub = 0.0f;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 pn[4];
+    auto unit = [&](int u) {
+      if (u == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, (*sh)[0][r]);
+      } else if (u == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m1 = fmaxf(m1, (*sh)[1][r]);
+      } else if (u == 2) {
+        const float mx = half_max(fmaxf(m0, m1)) * P.scale_log2;
+        const bool grow = ballot(mx > m_run + kLazy) != 0ull;
+        const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+        const float c = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+        l_run *= c;
+        corr *= c;
+        m_run = m_new;
+        resc = resc || grow;
+        msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      } else {
+        const int e = u - 3;                           // pair e: keys 2e, 2e + 1 of the lane's 32
+        const int kc = e / 4, j = e % 4;
+        const int o = 8 * (kc % 2) + 2 * j;
+        const float p0 = fast_exp2(__builtin_fmaf((*sh)[kc / 2][o], P.scale_log2, -msub));
+        const float p1 = fast_exp2(__builtin_fmaf((*sh)[kc / 2][o + 1], P.scale_log2, -msub));
+        pn[kc][j] = pack_bf16x2(p0, p1);
+        ls[j] += p0 + p1;
+      }
+    };
+    bf16x8 va[NMF];
+    va[0] = vread(vst, 0);
+    va[1] = vread(vst, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      if (i + 2 < NMF) va[i + 2] = vread(vst, i + 2);
+      oacc[i % DB] = mfma32x32x16(va[i], __builtin_bit_cast(bf16x8, pk[i / DB]), oacc[i % DB]);
+      if (sh != nullptr) {
+#pragma unroll
+        for (int u = i * NU / NMF; u < (i + 1) * NU / NMF; ++u) unit(u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (sh != nullptr) {
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) pk[kc] = pn[kc];
+    }
+  };
+  // ---- online softmax of one tile's scores into pk, m, l (no PV to hide it)
+  auto softmax = [&](f32x16 (&sh)[2]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sh[mb][r]);
+    const float mx = half_max(m) * P.scale_log2;
+    const bool grow = ballot(mx > m_run + kLazy) != 0ull;
+    const float m_new = grow ? fmaxf(m_run, mx) : m_run;
+    const float c = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+    l_run *= c;
+    corr *= c;
+    m_run = m_new;
+    resc = resc || grow;
+    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int o = 8 * (kc % 2);
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(__builtin_fmaf(sh[kc / 2][o + 2 * j], P.scale_log2, -msub));
+        const float p1 = fast_exp2(__builtin_fmaf(sh[kc / 2][o + 2 * j + 1], P.scale_log2, -msub));
+        w[j] = pack_bf16x2(p0, p1);
+        ls[j] += p0 + p1;
+      }
+      pk[kc] = w;
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
 
-    if (!skip) {
-      uint64_t vis = 0;
-      if (need_mask) {
-        uint64_t sepbits = 0;
-        if (band) {
-          const int32_t* sl = idxr[t % IDXR][0];
-          const bool f = (jmin + lane < S) && (idxr[t % IDXR][1][lane] != sl[lane]);
-          sepbits = ballot(f);
-        }
-        vis = vis_word(band, qi, jmin, P.n, P.a, sepbits, nvalid) >> (4 * hsel);
-      }
-      // ---- S^T halves: keys 32*mb .. 32*mb+31 of the tile
-      f32x16 sh[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 acc = {};
-        const int r = 32 * mb + lane % 32;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = 2 * ks + hsel;
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(kst + 16 * G::slot(r, c)));
-          acc = mfma32x32x16(a, qf[ks], acc);
-        }
-        sh[mb] = acc;
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16& s = sh[mb];
-        if (need_mask) {
-          const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t bit = 1u << (8 * (r / 4) + (r % 4));
-            s[r] = (word & bit) ? s[r] : -INFINITY;
-          }
-        }
-        float m = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, s[r]);
-        const float mx = fmaxf(m, swap_half(m)) * P.scale_log2;
-        if (ballot(mx > m_run + kLazy) != 0ull) {
-          const float m_new = fmaxf(m_run, mx);
-          const float corr = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-          l_run *= corr;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= corr;
-          m_run = m_new;
-        }
-        const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-        float lsum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[r], P.scale_log2, -msub));
-          s[r] = p;
-          lsum += p;
-        }
-        l_run += lsum;
-        // ---- O^T += V^T[:, keys of this half] . P^T
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int kc = 2 * mb + c2;                  // 16-key chunk of the tile
-          u32x4 pk;
-          pk[0] = pack_bf16x2(s[8 * c2 + 0], s[8 * c2 + 1]);
-          pk[1] = pack_bf16x2(s[8 * c2 + 2], s[8 * c2 + 3]);
-          pk[2] = pack_bf16x2(s[8 * c2 + 4], s[8 * c2 + 5]);
-          pk[3] = pack_bf16x2(s[8 * c2 + 6], s[8 * c2 + 7]);
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            // lane (16*tg + tj) points at key row 16*kc + 8*e + 4*th + tj/4,
-            // d column 32*db + 16*tdh + 4*(tj%4); the transpose load returns
-            // to lane l the keys {16*kc + 8*e + 4*th + k, k = 0..3} at
-            // d = 32*db + l%32.
-            v4i16 x[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int R = 16 * kc + 8 * e + 4 * th + tj / 4;
-              const int dcol = 32 * db + 16 * tdh + 4 * (tj % 4);
-              x[e] = read_tr16(vst + 16 * G::slot_v(R, dcol / 8) + 2 * (dcol % 8));
-            }
-            const v8i16 cat = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
-            oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, cat), pb, oacc[db]);
-          }
-        }
-      }
-    }
+  // iteration 0: QK and softmax of tile 0
+  {
+    advance(0);
+    f32x16 sh[2];
+    qk(0, sh);
+    softmax(sh);
   }
+  // iteration t: QK of tile t, then PV of tile t - 1 interleaved with the
+  // softmax of tile t
+  for (int t = 1; t < ti.ntiles; ++t) {
+    advance(t);
+    rescale();
+    f32x16 sh[2];
+    qk(t, sh);
+    pv_softmax(t - 1, &sh);
+  }
+  // last iteration: PV of the last tile
+  advance(ti.ntiles);
+  rescale();
+  pv_softmax(ti.ntiles - 1, nullptr);
 
   // ---- epilogue: normalise, stage bf16 rows through LDS, store 16-byte chunks
-  const float l_tot = l_run + swap_half(l_run);
+  const float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
   // no LDS-DMA may still be landing in the ring (or after the wave ends)
   compiler_fence();
