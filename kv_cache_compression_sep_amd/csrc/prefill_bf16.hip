@@ -14,8 +14,10 @@
 // transposed read takes 64 bytes of 4 rows per half wave), so that both hit
 // distinct banks. The data a tile's gather needs (its slice of sep_pos, or
 // for band tiles two shifted slices of rank whose difference gives the
-// separator bits) also arrives by LDS-DMA, six tiles ahead, into an index
-// ring. So the key loop has no global load with a register result: every
+// separator bits) also arrives by LDS-DMA, seven tiles ahead, into an index
+// ring; the key rows of tile t + 4 are read from it in iteration t, one
+// iteration before their loads are issued, so that no load address waits
+// for LDS. So the key loop has no global load with a register result: every
 // wait is explicit. Each wave issues exactly 1 + OPS loads per iteration (a
 // fixed dummy address past the last tile), waits with one exact vmcnt for
 // its own loads of K(t) and V(t - 1), and a plain barrier publishes them.
@@ -45,13 +47,17 @@ namespace {
 constexpr int KT = 64;                 // keys per tile
 constexpr int NW = 8;                  // waves per workgroup
 constexpr int NT = NW * kWave;
-constexpr int STAGES = 4;              // LDS ring depth (tiles), K and V each
+constexpr int KSTAGES = 4;             // K ring depth (tiles)
+constexpr int VSTAGES = 4;             // V ring depth (tiles)
 constexpr int KAHEAD = 3;              // K of tile t + KAHEAD is issued in iteration t
 constexpr int VAHEAD = 2;              // V of tile t + VAHEAD is issued in iteration t
-constexpr int IAHEAD = 6;              // index slices loaded this many tiles ahead
+constexpr int IAHEAD = 7;              // index slices loaded this many tiles ahead
 constexpr int IDXR = 8;                // index ring depth (> IAHEAD)
+static_assert(IDXR > IAHEAD && IAHEAD >= KAHEAD + 4, "index ring too shallow");
 constexpr float kLazy = 8.0f;
-static_assert(KAHEAD < STAGES && VAHEAD + 1 < STAGES, "ring too shallow for the pipeline");
+// V of tiles t - 1 .. t + VAHEAD and K of tiles t .. t + KAHEAD are live in
+// iteration t
+static_assert(KAHEAD < KSTAGES && VAHEAD + 2 <= VSTAGES, "ring too shallow for the pipeline");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -88,7 +94,7 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // Wait until this wave's loads of K(t) and V(t - 1) landed (and its LDS
 // reads of the previous iteration completed), then a plain barrier. Memory
-// ops of a wave in issue order: the index slices of tiles 0..5, [full
+// ops of a wave in issue order: the index slices of tiles 0..6, [full
 // wait], K(0); K(1), V(0); K(2), V(1); then per iteration t: one index
 // slice, K(t + 3), V(t + 2). Both K(t) and V(t - 1) are issued in
 // iteration t - 3 (or the prologue), V last; the ops issued after them are
@@ -148,9 +154,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   constexpr int DB = G::DB;
   constexpr int PW = G::PER_WAVE;
   constexpr int OSTR = D + 8;                          // bf16 output-staging row stride
-  static_assert(NW * 32 * OSTR * 2 <= 2 * STAGES * TB, "output staging must fit the ring");
+  static_assert(NW * 32 * OSTR * 2 <= (KSTAGES + VSTAGES) * TB, "output staging must fit the ring");
 
-  __shared__ __attribute__((aligned(1024))) char ring[2 * STAGES * TB];   // K stages, then V stages
+  __shared__ __attribute__((aligned(1024))) char ring[(KSTAGES + VSTAGES) * TB];   // K stages, then V stages
   __shared__ __attribute__((aligned(16))) int32_t idxr[IDXR][2][KT];   // index slices
   __shared__ __attribute__((aligned(16))) int32_t junk[NW][KT];       // dummy-load targets
 
@@ -216,15 +222,16 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
         key = min(ti.band_lo + (t - ti.ntg) * KT + r, S - 1);
       } else {
         const int u = t * KT + r;
-        const int gathered = idxr[t % IDXR][0][r];
+        int gathered = idxr[t % IDXR][0][r];
+        asm volatile("" : "+v"(gathered));             // read it unconditionally (no branch)
         key = u < ti.n_init ? u : (u >= ti.n_glob ? 0 : gathered);
       }
       rows[i] = real ? key : 0;
     }
   };
-  // ---- LDS-DMA of the K (or V) rows of tile t into stage t % STAGES
+  // ---- LDS-DMA of the K (or V) rows of tile t into its ring stage
   auto issue_rows = [&](const char* base, char* stage0, int t, const int (&rows)[PW], auto is_v) {
-    char* st = stage0 + (t % STAGES) * TB;
+    char* st = stage0 + (t % (decltype(is_v)::value ? VSTAGES : KSTAGES)) * TB;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int ins = wave * PW + i;                   // 1 KB block of the tile
@@ -237,7 +244,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     }
   };
   char* const kring = ring;
-  char* const vring = ring + STAGES * TB;
+  char* const vring = ring + KSTAGES * TB;
 
   // ---- Q fragments first, so that waiting for them never waits for tiles
   bf16x8 qf[KS];
@@ -250,9 +257,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   }
   for (int t = 0; t < IAHEAD; ++t) issue_index(t);
   compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0);                       // index slices 0..5 landed
+  __builtin_amdgcn_s_waitcnt(0);                       // index slices 0..6 landed
   __syncthreads();
-  int vrows[PW];
+  int vrows[PW], knext[PW];                            // key rows of V(t + 2) and K(t + 3)
   {
     int r0[PW], r1[PW];
     rows_of(0, r0);
@@ -263,6 +270,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     rows_of(2, vrows);
     issue_rows(kb, kring, 2, vrows, flag<false>{});
     issue_rows(vb, vring, 1, r1, flag<true>{});
+    rows_of(3, knext);
   }
 
   f32x16 oacc[DB];
@@ -298,66 +306,34 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     tile_barrier<G::OPS>(t);
     if (t < ti.ntiles) {
       issue_index(t + IAHEAD);
-      int rows[PW];
-      rows_of(t + KAHEAD, rows);
-      issue_rows(kb, kring, t + KAHEAD, rows, flag<false>{});
+      issue_rows(kb, kring, t + KAHEAD, knext, flag<false>{});
       issue_rows(vb, vring, t + VAHEAD, vrows, flag<true>{});
 #pragma unroll
-      for (int i = 0; i < PW; ++i) vrows[i] = rows[i];
+      for (int i = 0; i < PW; ++i) vrows[i] = knext[i];
+      rows_of(t + KAHEAD + 1, knext);                  // used in the next iteration
     }
   };
   // ---- the running max moved in the previous softmax: O to the new scale
   auto rescale = [&]() {
     if (resc) {
+      // a real branch: without it the compiler multiplies O by a selected
+      // factor (64 VALU ops) in every iteration
+      asm volatile("");
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= corr;
       corr = 1.0f;
       resc = false;
     }
   };
-  // ---- S^T of tile t (two 32-key halves), masked where the tile needs it.
-  //      A band tile whose keys all lie in the future of this wave's rows
-  //      gets an all-zero visibility word, so its P is zero.
-  auto qk = [&](int t, f32x16 (&sh)[2]) {
-    const char* kst = kring + (t % STAGES) * TB;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(kst + koff[ks] + mb * 32 * CPR * 16));
-        acc = mfma32x32x16(a, qf[ks], acc);
-      }
-      sh[mb] = acc;
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-    const bool band = t >= ti.ntg;
-    const int jmin = band ? ti.band_lo + (t - ti.ntg) * KT : 0;
-    const int nvalid = band ? KT : min(KT, ti.n_glob - t * KT);
-    const bool full = band ? (jmin + KT - 1 <= qw0 && jmin >= qmax - P.n + 1) : nvalid == KT;
-    if (!full) {
-      uint64_t sepbits = 0;
-      if (band) {
-        const int32_t* sl = idxr[t % IDXR][0];
-        const bool f = (jmin + lane < S) && (idxr[t % IDXR][1][lane] != sl[lane]);
-        sepbits = ballot(f);
-      }
-      const uint64_t vis = vis_word(band, qi, jmin, P.n, P.a, sepbits, nvalid) >> (4 * hsel);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sh[mb][r] = mask_bit(sh[mb][r], word, 8 * (r / 4) + (r % 4));
-      }
-    }
+  // ---- separator bits of band tile t (from its two rank slices); read in
+  //      the MFMA phase, used by the VALU phase (the index slot may be
+  //      reloaded before a late wave's VALU phase runs)
+  auto sep_bits = [&](int t) -> uint64_t {
+    if (t < ti.ntg) return 0;
+    const int jmin = ti.band_lo + (t - ti.ntg) * KT;
+    int r0 = idxr[t % IDXR][0][lane], r1 = idxr[t % IDXR][1][lane];
+    asm volatile("" : "+v"(r0), "+v"(r1));            // read both unconditionally (no branch)
+    return ballot((jmin + lane < S) & (r1 != r0));
   };
   // ---- V^T operand of PV MFMA i (16-key chunk kc = i / DB, d block
   //      db = i % DB) of the tile in V stage vst. O^T += V^T[:, chunk] . P^T:
@@ -372,66 +348,59 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     return __builtin_bit_cast(bf16x8, cat);
   };
   constexpr int NMF = 4 * DB;                          // PV MFMAs per tile
-  // ---- PV of the tile in V stage tv (with pk), and, when sh is given, the
-  //      online softmax of the next tile's scores into pk, m, l. The softmax
-  //      is cut into units (two max units, one unit for the running-max
-  //      update, one unit per exponentiated pair of scores) that are issued
-  //      between the PV MFMAs in a fixed order.
-  auto pv_softmax = [&](int tv, f32x16 (*sh)[2]) {
-    const char* vst = vring + (tv % STAGES) * TB;
-    constexpr int NU = 3 + 16;                         // softmax units
-    float m0 = -INFINITY, m1 = -INFINITY, msub = 0.0f;
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    u32x4 pn[4];
-    auto unit = [&](int u) {
-      if (u == 0) {
+
+  // ---- MFMA phase of iteration t: S^T of tile t into sh (two 32-key
+  //      halves), then O^T += V^T P^T for tile t - 1 with pk
+  auto mfma_phase = [&](int t, f32x16 (&sh)[2], auto do_qk, auto do_pv) {
+    if constexpr (decltype(do_qk)::value) {
+      const char* kst = kring + (t % KSTAGES) * TB;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, (*sh)[0][r]);
-      } else if (u == 1) {
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 acc = {};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m1 = fmaxf(m1, (*sh)[1][r]);
-      } else if (u == 2) {
-        const float mx = half_max(fmaxf(m0, m1)) * P.scale_log2;
-        const bool grow = ballot(mx > m_run + kLazy) != 0ull;
-        const float m_new = grow ? fmaxf(m_run, mx) : m_run;
-        const float c = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-        l_run *= c;
-        corr *= c;
-        m_run = m_new;
-        resc = resc || grow;
-        msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      } else {
-        const int e = u - 3;                           // pair e: keys 2e, 2e + 1 of the lane's 32
-        const int kc = e / 4, j = e % 4;
-        const int o = 8 * (kc % 2) + 2 * j;
-        const float p0 = fast_exp2(__builtin_fmaf((*sh)[kc / 2][o], P.scale_log2, -msub));
-        const float p1 = fast_exp2(__builtin_fmaf((*sh)[kc / 2][o + 1], P.scale_log2, -msub));
-        pn[kc][j] = pack_bf16x2(p0, p1);
-        ls[j] += p0 + p1;
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kst + koff[ks] + mb * 32 * CPR * 16));
+          acc = mfma32x32x16(a, qf[ks], acc);
+        }
+        sh[mb] = acc;
       }
-    };
-    bf16x8 va[NMF];
-    va[0] = vread(vst, 0);
-    va[1] = vread(vst, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NMF; ++i) {
-      if (i + 2 < NMF) va[i + 2] = vread(vst, i + 2);
-      oacc[i % DB] = mfma32x32x16(va[i], __builtin_bit_cast(bf16x8, pk[i / DB]), oacc[i % DB]);
-      if (sh != nullptr) {
-#pragma unroll
-        for (int u = i * NU / NMF; u < (i + 1) * NU / NMF; ++u) unit(u);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    if (sh != nullptr) {
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if constexpr (decltype(do_pv)::value) {
+      const char* vst = vring + ((t + VSTAGES - 1) % VSTAGES) * TB;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) pk[kc] = pn[kc];
+      for (int i = 0; i < NMF; ++i)
+        oacc[i % DB] = mfma32x32x16(vread(vst, i), __builtin_bit_cast(bf16x8, pk[i / DB]), oacc[i % DB]);
     }
+    // a few LDS reads ahead of the MFMA that consumes them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS + 2 * NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);                 // no VALU work mixed in
   };
-  // ---- online softmax of one tile's scores into pk, m, l (no PV to hide it)
-  auto softmax = [&](f32x16 (&sh)[2]) {
+
+  // ---- VALU phase for tile t: mask the scores where the tile needs it (a
+  //      band tile whose keys all lie in the future of this wave's rows gets
+  //      an all-zero visibility word, so its P is zero), then the online
+  //      softmax into pk, m, l
+  auto valu_phase = [&](int t, f32x16 (&sh)[2], uint64_t sepbits) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bool band = t >= ti.ntg;
+    const int jmin = band ? ti.band_lo + (t - ti.ntg) * KT : 0;
+    const int nvalid = band ? KT : min(KT, ti.n_glob - t * KT);
+    const bool full = band ? (jmin + KT - 1 <= qw0 && jmin >= qmax - P.n + 1) : nvalid == KT;
+    if (!full) {
+      const uint64_t vis = vis_word(band, qi, jmin, P.n, P.a, sepbits, nvalid) >> (4 * hsel);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sh[mb][r] = mask_bit(sh[mb][r], word, 8 * (r / 4) + (r % 4));
+      }
+    }
     float m = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -458,31 +427,54 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
         w[j] = pack_bf16x2(p0, p1);
         ls[j] += p0 + p1;
       }
+      // computed here, in the VALU phase, not sunk into the MFMA phase
+      // that consumes it
+      asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       pk[kc] = w;
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    asm volatile("" : "+v"(l_run));
   };
 
-  // iteration 0: QK and softmax of tile 0
-  {
+  // The two waves that share a SIMD (waves w and w + 4) alternate between an
+  // MFMA-only phase (QK of tile t and PV of tile t - 1) and a VALU-only phase
+  // (mask and softmax), half an iteration apart, so that one wave's MFMAs
+  // run while the other's VALU work does. Early waves: iteration t = MFMA(t),
+  // VALU(t). Late waves: iteration t = VALU(t - 1), MFMA(t); their scores
+  // wait in registers across the barrier. Both take ntiles + 1 barriers.
+  f32x16 sh[2];
+  uint64_t sepb = 0;
+  if (wave < 4) {
     advance(0);
-    f32x16 sh[2];
-    qk(0, sh);
-    softmax(sh);
-  }
-  // iteration t: QK of tile t, then PV of tile t - 1 interleaved with the
-  // softmax of tile t
-  for (int t = 1; t < ti.ntiles; ++t) {
-    advance(t);
+    mfma_phase(0, sh, flag<true>{}, flag<false>{});
+    sepb = sep_bits(0);
+    valu_phase(0, sh, sepb);
+    for (int t = 1; t < ti.ntiles; ++t) {
+      advance(t);
+      rescale();
+      mfma_phase(t, sh, flag<true>{}, flag<true>{});
+      sepb = sep_bits(t);
+      valu_phase(t, sh, sepb);
+    }
+    advance(ti.ntiles);
     rescale();
-    f32x16 sh[2];
-    qk(t, sh);
-    pv_softmax(t - 1, &sh);
+    mfma_phase(ti.ntiles, sh, flag<false>{}, flag<true>{});
+  } else {
+    advance(0);
+    mfma_phase(0, sh, flag<true>{}, flag<false>{});
+    sepb = sep_bits(0);
+    for (int t = 1; t < ti.ntiles; ++t) {
+      advance(t);
+      valu_phase(t - 1, sh, sepb);
+      rescale();
+      mfma_phase(t, sh, flag<true>{}, flag<true>{});
+      sepb = sep_bits(t);
+    }
+    advance(ti.ntiles);
+    valu_phase(ti.ntiles - 1, sh, sepb);
+    rescale();
+    mfma_phase(ti.ntiles, sh, flag<false>{}, flag<true>{});
   }
-  // last iteration: PV of the last tile
-  advance(ti.ntiles);
-  rescale();
-  pv_softmax(ti.ntiles - 1, nullptr);
 
   // ---- epilogue: normalise, stage bf16 rows through LDS, store 16-byte chunks
   const float l_tot = half_sum(l_run);
