@@ -17,7 +17,7 @@ under "secondary":
     stream: tokens/s of in-order decode + update steps, replayed from HIP
     graphs of 256 steps.
 
-Prints one JSON line. ``--gpus N`` with N > 1 exits: this build runs on one
+Prints one JSON line. ``--gpus N`` with N > 1 exits: the path runs on one
 GPU only.
 """
 from __future__ import annotations
@@ -57,8 +57,10 @@ def visible_pairs(rank: np.ndarray, S: int, a: int, n: int) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources of the bf16 prefill kernel, to tell whether stored
+    traffic counters were taken on the kernel as it stands."""
     h = hashlib.sha256()
-    for f in ("prefill.hip", "common.hpp"):
+    for f in ("prefill_bf16.hip", "prefill.hpp", "common.hpp"):
         with open(os.path.join(ROOT, "kv_cache_compression_sep_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -79,9 +81,26 @@ def measured_traffic(kernel: str):
         return None
 
 
+# ------------------------------------------------------------------ copy
+COPY_BYTES = 1 << 30
+
+
+def bench_copy(torch):
+    """Three launches of a plain device-to-device copy of COPY_BYTES: under
+    rocprofv3 --pmc their FETCH_SIZE / WRITE_SIZE per dispatch, against the
+    bytes known to move, give the scale of those counters."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}))
+
+
 # ------------------------------------------------------------------ prefill
 def bench_prefill(args, torch, sa, configs, gen):
-    cfg = configs.C2
+    cfg = configs.LLAMA3_LAYER_PREFILL
     B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
     x = gen.prefill_inputs(cfg)
     dev = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
@@ -107,20 +126,24 @@ def bench_prefill(args, torch, sa, configs, gen):
     pairs = sum(visible_pairs(rank[b].cpu().numpy().astype(np.int64), S, cfg.a, cfg.n)
                 for b in range(B))
     useful = 4.0 * D * pairs * Hq            # pairs counted per kv-head sequence, used by all heads
-    st = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()      # the stream every call above launches on
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # the timed region: K whole steps
     t0.record(st)
     for i in range(args.steps):
-        sa.sep_mask_build(ids, sep, cfg.a, cfg.n, is_sep=is_sep)
-        sa.sep_index_compact(is_sep, rank=rank, sep_pos=sep_pos, count=count)
+        step()
+    t1.record(st)
+    torch.cuda.synchronize()
+    # the dominant kernel alone: K launches on the same stream, each between
+    # its own pair of events (so that no launch overlaps the next), for its
+    # average launch duration
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
         ev[i][0].record(st)
         sa.sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, cfg.a, cfg.n, scale, out=out)
         ev[i][1].record(st)
-    t1.record(st)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
     ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -161,7 +184,7 @@ def cpu_baseline_prefill(res, oracle, gen, budget_s=20.0):
 
 # ------------------------------------------------------------------ batched decode
 def bench_batched(args, torch, sa, configs, gen):
-    cfg = configs.C4
+    cfg = configs.BATCHED_DECODE
     B, Hq, Hkv, D, H = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.history
     ids_h = np.stack([gen.stream_ids(cfg, b) for b in range(B)])
     ids = torch.from_numpy(ids_h).cuda()
@@ -273,7 +296,7 @@ def _occupancy(cache):
 
 # ------------------------------------------------------------------ stream
 def bench_stream(args, torch, sa, configs, gen):
-    cfg = configs.C3
+    cfg = configs.STREAM_DECODE
     Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
     steps = args.stream_steps
     chunk = 256
@@ -354,7 +377,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--stream-steps", type=int, default=4_194_304)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "stream"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "stream", "copy"], default="all",
+                    help="'copy' runs only a plain device copy of known size, the reference for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -371,6 +396,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
 
+    if args.only == "copy":
+        bench_copy(torch)
+        return
     secondary = {}
     res = None
     if args.only in ("all", "prefill"):

@@ -13,7 +13,7 @@ Separator sets:
   * the Llama-3-shaped configs use the Llama-3 separator ids that the SepLLM
     study notes list for the training-free configs
     (pengpengyi92.github.io "HKUDS047: SepLLM ...", section "Separator Tokens").
-    The vocabulary bound 128256 is this build's choice; the pages do not state
+    The vocabulary bound 128256 is a choice made here; the pages do not state
     it, and any bound above 128000 yields identical separator flags.
 """
 from __future__ import annotations
@@ -73,27 +73,27 @@ class StreamConfig:
         return self.a + self.s + self.p + self.w
 
 
-C1 = PrefillConfig("C1_tiny_prefill_f32", B=1, Hq=2, Hkv=2, D=64, S=512, dtype="f32",
+TINY_PREFILL = PrefillConfig("tiny_prefill_f32_s512", B=1, Hq=2, Hkv=2, D=64, S=512, dtype="f32",
                    a=4, n=64, sep_ids=TINY_SEP_IDS, vocab=TINY_VOCAB, p_sep=0.1,
                    id_mode="iid", run_mean=0.0, seed=1001)
 
-C2 = PrefillConfig("C2_llama3_layer_prefill_s8192", B=1, Hq=32, Hkv=8, D=128, S=8192,
+LLAMA3_LAYER_PREFILL = PrefillConfig("llama3_8b_layer_prefill_s8192", B=1, Hq=32, Hkv=8, D=128, S=8192,
                    dtype="bf16", a=4, n=256, sep_ids=LLAMA3_SEP_IDS, vocab=LLAMA3_VOCAB,
                    p_sep=0.12, id_mode="iid", run_mean=0.0, seed=1002)
 
-C3 = StreamConfig("C3_stream_decode_b1", B=1, Hq=32, Hkv=8, D=128, dtype="bf16",
+STREAM_DECODE = StreamConfig("stream_decode_b1_4m_tokens", B=1, Hq=32, Hkv=8, D=128, dtype="bf16",
                   a=4, s=64, p=64, w=256, sep_ids=LLAMA3_SEP_IDS, vocab=LLAMA3_VOCAB,
                   p_sep=0.1, history=0, steps=4_194_304, pool=65_536, seed=1003,
                   check_steps=65_536, check_every=4096)
 
-C4 = StreamConfig("C4_batched_decode_b64", B=64, Hq=32, Hkv=8, D=128, dtype="bf16",
+BATCHED_DECODE = StreamConfig("batched_decode_b64_h32768", B=64, Hq=32, Hkv=8, D=128, dtype="bf16",
                   a=4, s=256, p=28, w=512, sep_ids=LLAMA3_SEP_IDS, vocab=LLAMA3_VOCAB,
                   p_sep=0.12, history=32_768, steps=1024, pool=1024, seed=1004,
                   check_steps=1024, check_every=128)
 
-C5 = PrefillConfig("C5_long_prefill_s131072", B=1, Hq=32, Hkv=8, D=128, S=131_072,
+LONG_PREFILL = PrefillConfig("long_prefill_runs_s131072", B=1, Hq=32, Hkv=8, D=128, S=131_072,
                    dtype="bf16", a=4, n=256, sep_ids=LLAMA3_SEP_IDS, vocab=LLAMA3_VOCAB,
                    p_sep=0.08, id_mode="runs", run_mean=12.0, seed=1005)
 
-PREFILL_CONFIGS = {c.name: c for c in (C1, C2, C5)}
-STREAM_CONFIGS = {c.name: c for c in (C3, C4)}
+PREFILL_CONFIGS = {c.name: c for c in (TINY_PREFILL, LLAMA3_LAYER_PREFILL, LONG_PREFILL)}
+STREAM_CONFIGS = {c.name: c for c in (STREAM_DECODE, BATCHED_DECODE)}

@@ -81,18 +81,18 @@ def test_empty_separator_set_and_duplicates():
 
 
 def test_tiny_prefill_workload_full():
-    cfg = configs.C1
+    cfg = configs.TINY_PREFILL
     _check_flags_tiles_compact(_ids_for(cfg), cfg.sep_ids, cfg.a, cfg.n, dense=True)
 
 
 def test_llama3_layer_workload_full():
-    cfg = configs.C2
+    cfg = configs.LLAMA3_LAYER_PREFILL
     _check_flags_tiles_compact(_ids_for(cfg), cfg.sep_ids, cfg.a, cfg.n, tiles=((64, 64),),
                                dense=True)
 
 
 def test_long_prefill_workload_flags_ranks_sampled_tiles():
-    cfg = configs.C5
+    cfg = configs.LONG_PREFILL
     nqt = cfg.S // 64
     rng = np.random.default_rng(505)
     sample = sorted(set([0, 1, 2, 3, nqt - 2, nqt - 1] + rng.integers(0, nqt, 24).tolist()))

@@ -82,7 +82,7 @@ def test_prefill_small_cases(case, dtype):
 
 
 def test_tiny_prefill_workload_full():
-    cfg = configs.C1
+    cfg = configs.TINY_PREFILL
     x = gen.prefill_inputs(cfg)
     check_full(x["ids"], x["q"], x["k"], x["v"], cfg.sep_ids, cfg.a, cfg.n, cfg.dtype, cfg.name)
 
@@ -133,7 +133,7 @@ def _full_size_run(cfg, heads, sample_rows):
 
 @pytest.mark.timeout(600)
 def test_llama3_layer_workload_sampled_rows():
-    cfg = configs.C2
+    cfg = configs.LLAMA3_LAYER_PREFILL
     rng = np.random.default_rng(507)
     rows = sorted(set(list(range(0, 64)) + list(range(cfg.S - 64, cfg.S)) +
                       rng.integers(0, cfg.S, 128).tolist()))
@@ -144,7 +144,7 @@ def test_llama3_layer_workload_sampled_rows():
 
 @pytest.mark.timeout(900)
 def test_long_prefill_workload_sampled_rows():
-    cfg = configs.C5
+    cfg = configs.LONG_PREFILL
     rng = np.random.default_rng(509)
     qt0 = int(rng.integers(100, cfg.S // 32 - 100))
     rows = sorted(set(list(range(0, 32)) + list(range(cfg.S - 32, cfg.S)) +

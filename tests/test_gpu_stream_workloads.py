@@ -53,7 +53,7 @@ def compare_state(cache, b, sim, ids, k_of, v_of):
 
 @pytest.mark.timeout(1500)
 def test_stream_decode_first_65536_steps():
-    cfg = configs.C3
+    cfg = configs.STREAM_DECODE
     steps = cfg.check_steps
     ids = gen.stream_ids(cfg, 0, cfg.history + cfg.steps)
     qp, kp, vp = gen.stream_pool(cfg, 0)
@@ -102,7 +102,7 @@ def test_stream_decode_first_65536_steps():
 
 @pytest.mark.timeout(1500)
 def test_batched_decode_workload():
-    cfg = configs.C4
+    cfg = configs.BATCHED_DECODE
     B, Hq, Hkv, D, H = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.history
     checked = [0, 21, 42, 63]
     ids = np.stack([gen.stream_ids(cfg, b) for b in range(B)])       # [B, H + steps]
