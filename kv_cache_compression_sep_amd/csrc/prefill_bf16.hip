@@ -29,13 +29,15 @@
 // load (ds_read_b64_tr_b16): pointing a 16-lane group at four consecutive key
 // rows gives each lane four keys of one d column.
 //
-// Software pipeline: iteration t issues QK of tile t, then PV of tile t - 1
-// (P kept packed in registers, V still in its stage), then the softmax of
-// tile t. The softmax VALU work therefore overlaps the PV MFMAs of the
-// previous tile instead of waiting for its own. Softmax is online in fp32 in
-// the log2 domain with lazy rescaling (the running max moves only when a
-// row's max grows by more than 8); a move scales l at once and O just before
-// the next PV. P is rounded to bf16 for the PV product; l sums it in fp32.
+// Software pipeline: PV of tile t - 1 runs in iteration t (P kept packed in
+// registers, V still in its stage), so an iteration splits into an MFMA-only
+// phase (QK of tile t, PV of tile t - 1) and a VALU-only phase (mask and
+// softmax of tile t). The two waves on a SIMD (waves w and w + 4) run the
+// two phases in opposite order, so one wave's MFMAs overlap the other's VALU
+// work. Softmax is online in fp32 in the log2 domain with lazy rescaling
+// (the running max moves only when a row's max grows by more than 8); a move
+// scales l at once and O just before the next PV. P is rounded to bf16 for
+// the PV product; l sums it in fp32.
 #include "prefill.hpp"
 #include "internal.hpp"
 
