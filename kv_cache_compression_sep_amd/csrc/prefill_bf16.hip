@@ -36,8 +36,9 @@
 // two phases in opposite order, so one wave's MFMAs overlap the other's VALU
 // work. Softmax is online in fp32 in the log2 domain with lazy rescaling
 // (the running max moves only when a row's max grows by more than 8); a move
-// scales l at once and O just before the next PV. P is rounded to bf16 for
-// the PV product; l sums it in fp32.
+// scales O and l just before the next PV. P is rounded to bf16 for the PV
+// product, and l sums the same rounded values on the MFMA pipe (a block of
+// ones as one more A operand).
 #include "prefill.hpp"
 #include "internal.hpp"
 
@@ -279,7 +280,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   u32x4 pk[4];                                         // bf16 P of the previous tile, per 16-key chunk
-  float m_run = -INFINITY, l_run = 0.0f, corr = 1.0f;
+  // l, the row sum of P, is accumulated by the MFMA pipe: O^T gets one more
+  // 32-row block whose A operand is all ones, so every row of lacc holds
+  // sum_k P[q, k] for the lane's query q, in the same scale as O
+  f32x16 lacc = {};
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  float m_run = -INFINITY, corr = 1.0f;
   bool resc = false;
   const int qmax = min(qw0 + 31, S - 1);
   const int hsel = lane / 32;
@@ -323,6 +329,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       asm volatile("");
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= corr;
+      lacc *= corr;
       corr = 1.0f;
       resc = false;
     }
@@ -373,6 +380,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
 #pragma unroll
       for (int i = 0; i < NMF; ++i)
         oacc[i % DB] = mfma32x32x16(vread(vst, i), __builtin_bit_cast(bf16x8, pk[i / DB]), oacc[i % DB]);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) lacc = mfma32x32x16(ones, __builtin_bit_cast(bf16x8, pk[kc]), lacc);
     }
     // a few LDS reads ahead of the MFMA that consumes them
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -412,12 +421,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     const bool grow = ballot(mx > m_run + kLazy) != 0ull;
     const float m_new = grow ? fmaxf(m_run, mx) : m_run;
     const float c = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-    l_run *= c;
     corr *= c;
     m_run = m_new;
     resc = resc || grow;
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int o = 8 * (kc % 2);
@@ -427,15 +434,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
         const float p0 = fast_exp2(__builtin_fmaf(sh[kc / 2][o + 2 * j], P.scale_log2, -msub));
         const float p1 = fast_exp2(__builtin_fmaf(sh[kc / 2][o + 2 * j + 1], P.scale_log2, -msub));
         w[j] = pack_bf16x2(p0, p1);
-        ls[j] += p0 + p1;
       }
       // computed here, in the VALU phase, not sunk into the MFMA phase
       // that consumes it
       asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       pk[kc] = w;
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    asm volatile("" : "+v"(l_run));
   };
 
   // The two waves that share a SIMD (waves w and w + 4) alternate between an
@@ -479,7 +483,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   }
 
   // ---- epilogue: normalise, stage bf16 rows through LDS, store 16-byte chunks
-  const float l_tot = half_sum(l_run);
+  const float l_tot = lacc[0];
   const float inv = 1.0f / l_tot;
   // no LDS-DMA may still be landing in the ring (or after the wave ends)
   compiler_fence();

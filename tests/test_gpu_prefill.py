@@ -24,6 +24,14 @@ from .gpu_util import check_close, from_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 
+# Log-sum-exp tolerance. The bf16 path rounds P to bf16 (round to nearest
+# even, relative error <= 2^-9 per term) before both the PV product and the
+# row sum l, so |l_gpu / l - 1| <= 2^-9 and |lse_gpu - lse| <= -ln(1 - 2^-9)
+# ~ 1.96e-3; fp32 scores, fp32 accumulation and the hardware exp2 add a few
+# ulp. The fp32 path keeps P in fp32.
+LSE_TOL = {"bf16": 2.5e-3, "f32": 1e-5}
+
+
 def run_gpu(ids, q, k, v, sep_ids, a, n, dtype, scale):
     d_ids = to_dev(ids)
     flags, _, _ = sep_mask_build(d_ids, to_dev(np.asarray(sep_ids, np.int32)), a, n)
@@ -53,7 +61,7 @@ def check_full(ids, q, k, v, sep_ids, a, n, dtype, tag):
                                         gen.storage_to_f64(k[b], dtype),
                                         gen.storage_to_f64(v[b], dtype), M, scale)
         check_close(out[b], o_ref, dtype, f"{tag} b={b} out")
-        assert np.max(np.abs(lse[b] - l_ref)) < (1e-3 if dtype == "bf16" else 1e-5), tag
+        assert np.max(np.abs(lse[b] - l_ref)) < LSE_TOL[dtype], tag
 
 
 CASES = [
