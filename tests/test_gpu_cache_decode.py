@@ -102,8 +102,26 @@ def test_single_token_updates_match_simulation(params):
             check_cache(cache, sims, st)
 
 
+def _cuts(T, mode, params, rng):
+    """Chunk boundaries of a bulk replay: `random` (6 random cuts), `small`
+    (chunks of 2..7 tokens: compactions straddle call boundaries) or `wrap`
+    (a partial first call, then one call longer than the whole cache, so
+    separators still in the recent ring survive while new rows overwrite it)."""
+    a, s, p, w = params
+    if mode == "random":
+        return sorted(set([0, T] + rng.integers(1, T, 6).tolist()))
+    if mode == "small":
+        cuts = [0]
+        while cuts[-1] < T:
+            cuts.append(min(T, cuts[-1] + int(rng.integers(2, 8))))
+        return cuts
+    first = min(T - 1, a + w + (p + w) // 2 + 1)
+    return [0, first, T]
+
+
+@pytest.mark.parametrize("mode", ["random", "small", "wrap"])
 @pytest.mark.parametrize("params", PARAMS, ids=[str(p) for p in PARAMS])
-def test_bulk_updates_equal_single_updates(params):
+def test_bulk_updates_equal_single_updates(params, mode):
     a, s, p, w = params
     T = min(4 * (a + s + p + w) + 77, 2000)
     st = Stream(zlib.crc32(repr(params).encode()) + 1, 3, 4, 2, 128, T, 0.25)
@@ -112,8 +130,7 @@ def test_bulk_updates_equal_single_updates(params):
     bulk = SepCache(3, 2, 128, a, s, p, w)
     for t in range(T):
         st.push_gpu(one, t, t + 1, d_sep)
-    rng = np.random.default_rng(T)
-    cuts = sorted(set([0, T] + rng.integers(1, T, 6).tolist()))
+    cuts = _cuts(T, mode, params, np.random.default_rng(T))
     for t0, t1 in zip(cuts[:-1], cuts[1:]):
         st.push_gpu(bulk, t0, t1, d_sep)
     torch.cuda.synchronize()
