@@ -480,7 +480,57 @@ __global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
   int32_t* lid = dyn + smax;
   SetList L;
   if (MODE == UPD_FUSED) {
-    // a T == 1 call tests at most p + 1 ids: no table
+    // T == 1. The new K/V row, its id and the state are loaded together;
+    // when no compaction is due (K(t0 + 1) == K(t0)) the token only takes
+    // its slot: the row, one pos/tok entry and state[0], with no barrier.
+    // Otherwise the general block plans the compaction (p + 1 ids, no table).
+    const int tid = threadIdx.x;
+    const int b = blockIdx.y;
+    const int rw = A.p + A.w;
+    const int row_bytes = A.D * A.esize;
+    const int cpr = row_bytes / 16;
+    const int W = A.Hkv * 2 * cpr;
+    const int64_t* st = A.state + 4 * static_cast<int64_t>(b);
+    const int64_t t0 = ld_global(st), K0 = ld_global(st + 1);
+    const int32_t id = ld_global(A.ids_new + b);
+    u32x4 val[2];
+    int col[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      col[u] = tid + u * kUpdThreads;
+      if (col[u] < W) {
+        const int kv = (col[u] / cpr) & 1;
+        const int g = col[u] / (2 * cpr);
+        const char* src = (kv ? A.v_new : A.k_new) + (static_cast<int64_t>(b) * A.Hkv + g) * row_bytes;
+        val[u] = ld_global_nt(reinterpret_cast<const u32x4*>(src + 16 * (col[u] % cpr)));
+      }
+    }
+    if (n_compact(t0 + 1, A.a, A.p, A.w) == K0) {
+      const int slot = t0 < A.a ? static_cast<int>(t0) : slot_r(t0, A.a, A.s, rw);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (col[u] < W) {
+          const int kv = (col[u] / cpr) & 1;
+          const int g = col[u] / (2 * cpr);
+          char* dst = (kv ? A.v : A.k) + ((static_cast<int64_t>(b) * A.Hkv + g) * A.c + slot) * row_bytes;
+          st_global(reinterpret_cast<u32x4*>(dst + 16 * (col[u] % cpr)), val[u]);
+        }
+      }
+      for (int c0 = 2 * kUpdThreads + tid; c0 < W; c0 += kUpdThreads) {
+        const int kv = (c0 / cpr) & 1;
+        const int g = c0 / (2 * cpr);
+        const int64_t hrow = static_cast<int64_t>(b) * A.Hkv + g;
+        const u32x4 v = ld_global_nt(reinterpret_cast<const u32x4*>((kv ? A.v_new : A.k_new) + hrow * row_bytes +
+                                                                    16 * (c0 % cpr)));
+        st_global(reinterpret_cast<u32x4*>((kv ? A.v : A.k) + (hrow * A.c + slot) * row_bytes + 16 * (c0 % cpr)), v);
+      }
+      if (tid == 0) {
+        st_global(A.pos + static_cast<int64_t>(b) * A.c + slot, static_cast<int32_t>(t0));
+        st_global(A.tok + static_cast<int64_t>(b) * A.c + slot, id);
+        st_global(A.state + 4 * static_cast<int64_t>(b), t0 + 1);
+      }
+      return;
+    }
     L.load(A.sep_ids, A.n_sep, nullptr, set_lds);
     update_block<MODE>(A, L, ph, lpos, lid, wave_tot);
   } else {
