@@ -37,4 +37,4 @@ from .mask import (is_sep, sep_mask, mask_rows, compact, tile_class,  # noqa: F4
                    tile_class_slabs, visible_count)
 from .attention import attention, attention_rows, decode_attention  # noqa: F401
 from .cache import (CacheSim, Entry, closed_form_positions, check_cache_params,  # noqa: F401
-                    n_compactions)
+                    n_compactions, policy_positions)

@@ -21,6 +21,18 @@ Both SEP_ACCUMULATION and USE_MAX_SEP_CACHE are on, as in the SepLLM branch
 of P1 "Streaming-SepLLM". With s = 0 and p = 0 the same rule keeps only
 initial + local tokens: the StreamingLLM baseline of P1 "Streaming-SepLLM".
 
+Policy variants (P1 "KV Cache Manager", the compression pseudo-code):
+  dynamic=True     the trigger of that pseudo-code: compress as soon as the
+                   whole cache (I + S + R, after the push) holds more than
+                   c = a + s + p + w entries. The past window is then R
+                   without its last w entries, so while S is not full R
+                   grows past p + w. With S full this is the fixed rule.
+  accumulate=False SEP_ACCUMULATION off: S becomes the separators of the
+                   compressed past window alone (then capped to its last s).
+In both rules a compression takes R minus its last w entries (in the fixed
+rule that is exactly the oldest p + 1). USE_MAX_SEP_CACHE = False (an
+unbounded S) has no fixed-size form and is not modelled.
+
 Order within one streaming step (P1 "Streaming-SepLLM" evaluation loop:
 forward with the cache, then update ids, then compress): the decode
 attention of token t reads I ++ S ++ R (the state after tokens 0..t-1) plus
@@ -59,15 +71,19 @@ class Entry:
 class CacheSim:
     """The four blocks as Python lists, one token at a time."""
 
-    def __init__(self, a: int, s: int, p: int, w: int, sep_ids: Sequence[int]):
+    def __init__(self, a: int, s: int, p: int, w: int, sep_ids: Sequence[int],
+                 dynamic: bool = False, accumulate: bool = True):
         check_cache_params(a, s, p, w)
         self.a, self.s, self.p, self.w = a, s, p, w
+        self.c = a + s + p + w
+        self.dynamic, self.accumulate = dynamic, accumulate
         self.sep_set = set(int(x) for x in sep_ids)
         self.I: List[Entry] = []
         self.S: deque = deque()
         self.R: deque = deque()
         self.t = 0
         self.compactions = 0
+        self.compacted = 0          # entries taken out of R so far (= cend - a)
 
     def push(self, e: Entry) -> None:
         """Insert the next token of the stream (its position must be t)."""
@@ -77,14 +93,21 @@ class CacheSim:
             self.I.append(e)
             return
         self.R.append(e)
-        if len(self.R) > self.p + self.w:
-            batch = [self.R.popleft() for _ in range(self.p + 1)]
+        if self.dynamic:
+            due = len(self.I) + len(self.S) + len(self.R) > self.c
+        else:
+            due = len(self.R) > self.p + self.w
+        if due:
+            batch = [self.R.popleft() for _ in range(len(self.R) - self.w)]
+            if not self.accumulate:
+                self.S.clear()
             for x in batch:
                 if x.tok in self.sep_set:
                     self.S.append(x)
                     if len(self.S) > self.s:
                         self.S.popleft()
             self.compactions += 1
+            self.compacted += len(batch)
 
     def push_many(self, entries: Sequence[Entry]) -> None:
         """A bulk insert is the same as inserting the tokens one by one."""
@@ -122,4 +145,30 @@ def closed_form_positions(flags: np.ndarray, t: int, a: int, s: int, p: int, w: 
     cend = a + K * (p + 1)
     seps = [x for x in range(a, cend) if flags[x]]
     S = seps[max(0, len(seps) - s):] if s > 0 else []
+    return list(range(a)), S, list(range(cend, t))
+
+
+def policy_positions(flags: np.ndarray, t: int, a: int, s: int, p: int, w: int,
+                     dynamic: bool = False, accumulate: bool = True):
+    """Positions held by I, S, R after tokens 0..t-1, from the compression
+    points alone (no per-token lists).
+
+    R is always [cend, t). Pushing position x makes the cache hold
+    a + |S| + (x + 1 - cend) entries, so the next compression is at
+    x = cend + c - a - |S| (dynamic: the whole cache exceeds c) or at
+    x = cend + p + w (fixed: R exceeds p + w); it moves cend to x + 1 - w
+    and sets S from the separators in the old [cend, x + 1 - w)."""
+    if t <= a:
+        return list(range(t)), [], []
+    c = a + s + p + w
+    cend, S = a, []
+    while True:
+        x = cend + (c - a - len(S) if dynamic else p + w)
+        if x >= t:
+            break
+        new_cend = x + 1 - w
+        batch = [z for z in range(cend, new_cend) if flags[z]]
+        S = S + batch if accumulate else batch
+        S = S[len(S) - s:] if len(S) > s else S
+        cend = new_cend
     return list(range(a)), S, list(range(cend, t))

@@ -217,3 +217,158 @@ def test_planted_cache_mistakes_fail_the_pin(mutant):
         if caught:
             break
     assert caught
+
+
+# ----------------------------------------------------------- policy variants
+# P1 "KV Cache Manager" prints the compression step as pseudo-code: when the
+# cache holds more than cache_size entries, the separators of the past window
+# (R without its last w entries) join S (SEP_ACCUMULATION) or replace it, and
+# S keeps its last sep_cache_size entries (USE_MAX_SEP_CACHE).
+POLICIES = [(False, True), (True, True), (False, False), (True, False)]   # (dynamic, accumulate)
+
+
+def run_policy(a, s, p, w, flags, dynamic, accumulate, check_each=None):
+    sim = oracle.CacheSim(a, s, p, w, sep_ids=[1], dynamic=dynamic, accumulate=accumulate)
+    for t, f in enumerate(flags):
+        before = (sim.occupancy(), sim.compacted, list(sim.S))
+        sim.push(oracle.Entry(pos=t, tok=int(f)))
+        if check_each:
+            check_each(sim, t + 1, before)
+    return sim
+
+
+def test_hand_worked_policy_trace():
+    """a=1, s=2, p=1, w=2 (c = 6), separators at positions 2, 3 and 6, worked
+    by hand from the pseudo-code. Dynamic trigger, accumulating: R grows to
+    [1..5] (cache 6); pushing 6 makes 7 > 6, so the past window [1, 2, 3, 4]
+    is compressed, S = [2, 3], R = [5, 6]; pushing 8 (cache 7) compresses
+    [5, 6]: S = [2, 3, 6] -> last 2 = [3, 6], R = [7, 8]; pushing 10
+    compresses [7, 8] (no separator), R = [9, 10]. Without accumulation the
+    compression at 8 leaves S = [6], the cache then holds 1 + 1 + |R| and
+    only pushing 11 exceeds 6: [7, 8, 9] is compressed, S = [], R = [10, 11].
+    Fixed caps, without accumulation: R exceeds p + w = 3 at 4, 6, 8, 10,
+    each time S becomes the separators of the two oldest entries."""
+    flags = np.zeros(12, bool)
+    flags[[2, 3, 6]] = True
+    want = {
+        (True, True): {5: ([0], [], [1, 2, 3, 4, 5]), 6: ([0], [2, 3], [5, 6]),
+                       8: ([0], [3, 6], [7, 8]), 10: ([0], [3, 6], [9, 10]),
+                       11: ([0], [3, 6], [9, 10, 11])},
+        (True, False): {6: ([0], [2, 3], [5, 6]), 8: ([0], [6], [7, 8]),
+                        10: ([0], [6], [7, 8, 9, 10]), 11: ([0], [], [10, 11])},
+        (False, False): {4: ([0], [2], [3, 4]), 6: ([0], [3], [5, 6]), 8: ([0], [6], [7, 8]),
+                         10: ([0], [], [9, 10])},
+    }
+    for pol, states in want.items():
+        sim = oracle.CacheSim(1, 2, 1, 2, sep_ids=[1], dynamic=pol[0], accumulate=pol[1])
+        for t in range(12):
+            sim.push(oracle.Entry(t, int(flags[t])))
+            if t in states:
+                assert sim.positions() == states[t], (pol, t)
+
+
+def test_policy_simulation_matches_compression_points():
+    for a, s, p, w, flags in param_cases(count=100, seed=97):
+        for dyn, acc in POLICIES:
+            def chk(sim, t, before):
+                assert sim.positions() == tuple(oracle.policy_positions(flags, t, a, s, p, w, dyn, acc)), \
+                    (a, s, p, w, t, dyn, acc)
+                assert sim.compacted == (sim.R[0].pos if sim.R else t) - a if t > a else sim.compacted == 0
+            run_policy(a, s, p, w, flags, dyn, acc, chk)
+        assert all(oracle.policy_positions(flags, t, a, s, p, w) ==
+                   oracle.closed_form_positions(flags, t, a, s, p, w) for t in range(len(flags) + 1))
+
+
+def test_dynamic_trigger_is_the_cache_size():
+    """Dynamic rule: the cache never holds more than c entries after a push,
+    and a compression happens exactly when the push would exceed c."""
+    for a, s, p, w, flags in param_cases(count=80, seed=101):
+        c = a + s + p + w
+        for acc in (True, False):
+            def chk(sim, t, before):
+                occ0, comp0, _ = before
+                assert sim.occupancy() <= c
+                compressed = sim.compacted != comp0
+                assert compressed == (t > a and occ0 + 1 > c), (a, s, p, w, t)
+                if compressed:
+                    assert len(sim.R) == w
+            run_policy(a, s, p, w, flags, True, acc, chk)
+
+
+def test_dynamic_with_full_separator_cache_has_fixed_spacing():
+    """Once S holds s entries (accumulating), the dynamic rule compresses
+    every p + 1 tokens, p + 1 entries at a time, as the fixed rule does."""
+    for a, s, p, w, flags in param_cases(count=80, seed=103):
+        full = [False]
+        def chk(sim, t, before):
+            _, comp0, S0 = before
+            if len(S0) == s and s > 0:
+                full[0] = True
+            if full[0] and sim.compacted != comp0:
+                assert sim.compacted - comp0 == p + 1
+        run_policy(a, s, p, w, flags, True, True, chk)
+
+
+def test_no_accumulation_keeps_only_the_last_window():
+    for a, s, p, w, flags in param_cases(count=80, seed=107):
+        for dyn in (False, True):
+            def chk(sim, t, before):
+                _, comp0, S0 = before
+                Spos = [e.pos for e in sim.S]
+                if sim.compacted != comp0:
+                    lo, hi = a + comp0, a + sim.compacted
+                    seps = [x for x in range(lo, hi) if flags[x]]
+                    assert Spos == seps[max(0, len(seps) - s):]
+                else:
+                    assert Spos == [e.pos for e in S0]
+            run_policy(a, s, p, w, flags, dyn, False, chk)
+
+
+def test_streamingllm_is_the_same_under_every_policy():
+    rng = np.random.default_rng(109)
+    for a, w in [(4, 8), (0, 3), (2, 1)]:
+        flags = rng.random(90) < 0.5
+        ref = run_policy(a, 0, 0, w, flags, False, True).positions()
+        for dyn, acc in POLICIES:
+            assert run_policy(a, 0, 0, w, flags, dyn, acc).positions() == ref
+
+
+class _MutDynIgnoresS(ocache.CacheSim):
+    """dynamic trigger that forgets the separator block in the cache size"""
+    def push(self, e):
+        self.t += 1
+        if len(self.I) < self.a:
+            self.I.append(e)
+            return
+        self.R.append(e)
+        if len(self.I) + len(self.R) > self.c:
+            batch = [self.R.popleft() for _ in range(len(self.R) - self.w)]
+            for x in batch:
+                if x.tok in self.sep_set:
+                    self.S.append(x)
+                    if len(self.S) > self.s:
+                        self.S.popleft()
+            self.compacted += len(batch)
+
+
+class _MutNoAccumKeepsOld(ocache.CacheSim):
+    """SEP_ACCUMULATION off, but the old separators are kept anyway"""
+    def __init__(self, *args, **kw):
+        super().__init__(*args, **kw)
+        self.accumulate = True
+
+
+@pytest.mark.parametrize("mutant,dyn,acc", [(_MutDynIgnoresS, True, True), (_MutNoAccumKeepsOld, True, False),
+                                            (_MutNoAccumKeepsOld, False, False)])
+def test_planted_policy_mistakes_fail_the_pin(mutant, dyn, acc):
+    caught = False
+    for a, s, p, w, flags in param_cases(count=60, seed=113):
+        sim = mutant(a, s, p, w, sep_ids=[1], dynamic=dyn, accumulate=acc)
+        for t, f in enumerate(flags):
+            sim.push(oracle.Entry(t, int(f)))
+            if sim.positions() != tuple(oracle.policy_positions(flags, t + 1, a, s, p, w, dyn, acc)):
+                caught = True
+                break
+        if caught:
+            break
+    assert caught
