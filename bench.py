@@ -288,8 +288,8 @@ def _occupancy(cache):
     st = cache.state.cpu().numpy()
     a, s, p, w = cache.a, cache.s, cache.p, cache.w
     occ = []
-    for t, K, head, cnt in st:
-        cend = a + K * (p + 1)
+    for t, ncomp, head, cnt in st[:, :4]:
+        cend = a + ncomp
         occ.append(min(a, t) + cnt + max(0, t - max(cend, a)))
     return np.asarray(occ)
 

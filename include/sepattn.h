@@ -132,33 +132,59 @@ int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
                      hipStream_t stream);
 
 /*
+ * Cache policies (bits of sep_cache.policy) [P1 "KV Cache Manager": the
+ * compression pseudo-code and its SEP_ACCUMULATION / USE_MAX_SEP_CACHE
+ * switches].
+ *   0                    fixed caps: R is compressed when it would hold
+ *                        p + w + 1 entries.
+ *   SEP_POLICY_DYNAMIC   the pseudo-code's trigger: R is compressed when
+ *                        the whole cache (I + S + R) would hold more than
+ *                        c = a + s + p + w entries; while S is not full R
+ *                        grows past p + w (its ring has s + p + w slots).
+ *   SEP_POLICY_NO_ACCUM  SEP_ACCUMULATION off: a compression replaces S by
+ *                        the separators of the compressed entries.
+ * Either way a compression takes R minus its last w entries (under fixed
+ * caps exactly its oldest p + 1), and S keeps its last s separators
+ * (USE_MAX_SEP_CACHE on; an unbounded S has no fixed-size form and is not
+ * offered). Under SEP_POLICY_DYNAMIC, s + p + w <= SEP_MAX_DYN_RING.
+ */
+#define SEP_POLICY_DYNAMIC 1
+#define SEP_POLICY_NO_ACCUM 2
+#define SEP_MAX_DYN_RING 32768
+
+/*
  * sep_cache - a batch of four-block KV caches in caller-owned device memory.
  * [P2 §1.3 and P3 §3.3 (initial / separator / past window / local window);
  * P1 "SepCache" (parameter names)]
  *
- * Slot layout per sequence, c = a + s + p + w slots:
- *   [0, a)       initial block: position x < a lives in slot x.
- *   [a, a+s)     separator ring (FIFO, cap s).
- *   [a+s, c)     recent ring R = past window ++ local window (cap p + w):
- *                position x >= a lives in slot a + s + (x - a) mod (p + w).
+ * Slot layout per sequence, with the recent-ring size r = p + w (fixed
+ * caps) or s + p + w (SEP_POLICY_DYNAMIC) and nslots = a + s + r:
+ *   [0, a)          initial block: position x < a lives in slot x.
+ *   [a, a+s)        separator ring (FIFO, cap s).
+ *   [a+s, nslots)   recent ring R = past window ++ local window:
+ *                   position x >= a lives in slot a + s + (x - a) mod r.
  * Device arrays:
- *   k, v   [B, Hkv, c, D] in `dtype`.
- *   pos    [B, c] int32: absolute position held by each slot, -1 if empty.
- *   tok    [B, c] int32: token id held by each slot, -1 if empty.
- *   state  [B, 4] int64 per sequence:
+ *   k, v   [B, Hkv, nslots, D] in `dtype`.
+ *   pos    [B, nslots] int32: absolute position held by each slot, -1 if
+ *          empty. Positions are below 2^31.
+ *   tok    [B, nslots] int32: token id held by each slot, -1 if empty.
+ *   state  [B, 8] int64 per sequence:
  *          [0] n_seen        tokens inserted so far (t);
- *          [1] n_compact     compactions so far (K); the compacted prefix
- *                            is [a, a + K (p + 1)) and R holds
- *                            positions [a + K (p + 1), t);
+ *          [1] n_compacted   entries taken out of R so far: the compacted
+ *                            prefix is [a, a + n_compacted) and R holds
+ *                            positions [a + n_compacted, t) (fixed caps:
+ *                            n_compacted = K (p + 1) after K compressions);
  *          [2] sep_head      separator-ring slot the next separator takes;
- *          [3] sep_count     separators held (<= s).
+ *          [3] sep_count     separators held (<= s);
+ *          [4] n_compacted before the last sep_cache_update call;
+ *          [5..7] reserved, 0.
  *          The ring's entries, oldest first, are the slots
  *          a + (sep_head - sep_count + i) mod s, i = 0 .. sep_count-1.
  * An empty cache is state all zero and pos/tok all -1 (sep_cache_reset).
  * K/V rows of empty slots are never read.
  * Contract [P1 "Streaming 参数约束"]: a >= 0, w >= 1, and either s >= 1 and
  * p >= 1 (SepLLM: a + s + w < c) or s == 0 and p == 0 (StreamingLLM: the
- * local window is c - a).
+ * local window is c - a); policy is a combination of the bits above.
  */
 typedef struct {
   int32_t a, s, p, w;
@@ -168,6 +194,7 @@ typedef struct {
   int32_t* pos;
   int32_t* tok;
   int64_t* state;
+  int32_t policy;
 } sep_cache;
 
 /*
@@ -189,10 +216,14 @@ int sep_cache_reset(const sep_cache* cache, hipStream_t stream);
  *   sep_ids [n_sep_ids] int32 device array (0..64 ids).
  * Rule, per token (positions t = n_seen, n_seen+1, ...): if fewer than a
  * tokens are held in the initial block, the token goes there. Otherwise it
- * joins R; when R would hold p + w + 1 entries, its oldest p + 1 entries are
- * compacted first: each separator among them, oldest first, is copied into
- * the separator ring (overwriting the oldest entry once the ring holds s),
- * the rest are dropped. T > 1 gives exactly the state of T calls with T = 1.
+ * joins R; when the policy's trigger fires (fixed caps: R would hold
+ * p + w + 1 entries; SEP_POLICY_DYNAMIC: the cache would hold more than c),
+ * R minus its last w entries is compressed first: under SEP_POLICY_NO_ACCUM
+ * the separator ring is emptied (its next entry takes slot a, sep_head 0);
+ * then each separator among the compressed
+ * entries, oldest first, is copied into the separator ring (overwriting the
+ * oldest entry once the ring holds s); the rest are dropped. T > 1 gives
+ * exactly the state of T calls with T = 1.
  * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
  * SEP_ERR_ALIGN, SEP_ERR_HIP.
  */

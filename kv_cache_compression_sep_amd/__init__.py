@@ -24,7 +24,8 @@ from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
 __all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_decode",
-           "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version"]
+           "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
+           "SEP_POLICY_DYNAMIC", "SEP_POLICY_NO_ACCUM"]
 
 
 def _ptr(t) -> int | None:
@@ -127,27 +128,50 @@ def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: floa
     return (out, lse) if return_lse else out
 
 
+# cache policies (sep_cache.policy in include/sepattn.h)
+SEP_POLICY_DYNAMIC = 1     # compress when the whole cache exceeds c = a + s + p + w
+SEP_POLICY_NO_ACCUM = 2    # SEP_ACCUMULATION off: a compression replaces the separators
+STATE_WORDS = 8
+
+
 class SepCache:
     """A batch of four-block caches in device memory (layout: see sep_cache
-    in include/sepattn.h)."""
+    in include/sepattn.h). ``policy`` combines SEP_POLICY_DYNAMIC and
+    SEP_POLICY_NO_ACCUM; the recent ring has p + w slots, or s + p + w under
+    SEP_POLICY_DYNAMIC."""
 
     def __init__(self, B: int, Hkv: int, D: int, a: int, s: int, p: int, w: int,
-                 dtype=torch.bfloat16, device="cuda"):
+                 dtype=torch.bfloat16, device="cuda", policy: int = 0):
         self.B, self.Hkv, self.D = B, Hkv, D
         self.a, self.s, self.p, self.w = a, s, p, w
+        self.policy = int(policy)
         self.c = a + s + p + w
+        self.ring = p + w + (s if self.policy & SEP_POLICY_DYNAMIC else 0)
+        self.slots = a + s + self.ring
         self.dtype = dtype
         dev = torch.device(device)
-        self.k = torch.zeros((B, Hkv, self.c, D), dtype=dtype, device=dev)
+        self.k = torch.zeros((B, Hkv, self.slots, D), dtype=dtype, device=dev)
         self.v = torch.zeros_like(self.k)
-        self.pos = torch.full((B, self.c), -1, dtype=torch.int32, device=dev)
-        self.tok = torch.full((B, self.c), -1, dtype=torch.int32, device=dev)
-        self.state = torch.zeros((B, 4), dtype=torch.int64, device=dev)
+        self.pos = torch.full((B, self.slots), -1, dtype=torch.int32, device=dev)
+        self.tok = torch.full((B, self.slots), -1, dtype=torch.int32, device=dev)
+        self.state = torch.zeros((B, STATE_WORDS), dtype=torch.int64, device=dev)
 
     def struct(self) -> _lib.SepCacheStruct:
         return _lib.SepCacheStruct(self.a, self.s, self.p, self.w, self.B, self.Hkv, self.D,
                                    _dtype_code(self.k), self.k.data_ptr(), self.v.data_ptr(),
-                                   self.pos.data_ptr(), self.tok.data_ptr(), self.state.data_ptr())
+                                   self.pos.data_ptr(), self.tok.data_ptr(), self.state.data_ptr(),
+                                   self.policy)
+
+    def slots_of(self, b: int):
+        """Slots of sequence b's retained entries per block, oldest first:
+        (initial, separator ring, recent ring), from its state words."""
+        t, ncomp, head, cnt = [int(x) for x in self.state[b, :4].cpu().numpy()]
+        a, s = self.a, self.s
+        I = list(range(min(a, t)))
+        S = [a + (head - cnt + i) % s for i in range(cnt)] if s > 0 else []
+        cend = a + ncomp
+        R = [a + s + (x - a) % self.ring for x in range(max(cend, a), t)] if t > a else []
+        return I, S, R
 
     def reset(self):
         sep_cache_reset(self)

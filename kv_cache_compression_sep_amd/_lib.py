@@ -37,6 +37,7 @@ class SepCacheStruct(ctypes.Structure):
         ("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("k", c_vp), ("v", c_vp), ("pos", c_vp), ("tok", c_vp), ("state", c_vp),
+        ("policy", ctypes.c_int32),
     ]
 
 

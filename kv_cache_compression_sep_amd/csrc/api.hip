@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;   // 1.1: cache policies, 8-word state
 constexpr int kMaxSepCache = 8192;   // separator-ring cap (plan list lives in LDS)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -27,8 +27,12 @@ int check_cache(const sep_cache* c) {
   const bool streaming = c->s == 0 && c->p == 0;
   if (!sepllm && !streaming) return SEP_ERR_PARAM;
   if (c->s > kMaxSepCache) return SEP_ERR_PARAM;
-  const int64_t cap = static_cast<int64_t>(c->a) + c->s + c->p + c->w;
-  if (cap > (1 << 24)) return SEP_ERR_SHAPE;
+  if ((c->policy & ~(SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM)) != 0) return SEP_ERR_PARAM;
+  const bool dynamic = (c->policy & SEP_POLICY_DYNAMIC) != 0;
+  const int64_t ring = static_cast<int64_t>(c->p) + c->w + (dynamic ? c->s : 0);
+  if (dynamic && ring > SEP_MAX_DYN_RING) return SEP_ERR_PARAM;
+  const int64_t slots = static_cast<int64_t>(c->a) + c->s + ring;
+  if (slots > (1 << 24)) return SEP_ERR_SHAPE;
   return SEP_OK;
 }
 

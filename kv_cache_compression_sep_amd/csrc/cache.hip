@@ -4,24 +4,32 @@
 // "KV Cache Manager"): initial tokens are fixed; the local window overflows
 // into the past window; when the past window is full its separators are
 // kept and the rest dropped; the separator cache holds at most s entries and
-// drops its oldest. With fixed caps this becomes: a token at position t >= a
-// joins the recent ring R (= past ++ local, cap p + w); when R would hold
-// p + w + 1 entries, its oldest p + 1 are compacted first (separators to the
-// separator ring, others dropped). The timing of compactions depends only on
-// t, so after t tokens the number of compactions is
-//   K(t) = max(0, floor((t - a - w) / (p + 1)))   (t > a), 0 otherwise,
-// and the compacted prefix is [a, a + K (p + 1)).
+// drops its oldest. A token at position t >= a joins the recent ring R
+// (= past ++ local); when the policy's trigger fires, R minus its last w
+// entries is compressed (separators to the separator ring, the rest
+// dropped; without SEP_ACCUMULATION the ring is emptied first).
+//   fixed caps: R would hold p + w + 1 entries. The timing depends only on
+//     t: after t tokens K(t) = max(0, floor((t - a - w) / (p + 1))) (t > a)
+//     compressions of p + 1 entries each have happened.
+//   dynamic (P1's trigger): the whole cache would hold more than
+//     c = a + s + p + w entries. Pushing position x makes it hold
+//     a + |S| + (x + 1 - cend) entries, so the next compression is at
+//     x = cend + c - a - |S|; its timing depends on |S|, i.e. on content.
 //
 // A call that appends T tokens is planned once per sequence: the positions
-// compacted by this call are [cend0, cend1); their separators are numbered
-// k = 0 .. nL-1 in position order, and only the last min(nL, s) survive,
-// the k-th landing in ring slot (sep_head + k) mod s. A block-wide count
-// gives nL; a backward walk with wavefront ballots finds the survivors.
-// Surviving rows are copied into the separator ring before any newly arriving
-// token overwrites a recent-ring slot. A call with T > 1 runs two kernels:
-// one block per sequence plans and writes pos / tok / state, then one block
-// per (head, sequence) copies K/V rows, reading the plan back from pos[] of
-// the separator ring. T == 1 runs one fused block per sequence.
+// compressed by this call are [cend0, cend1). Their separators that can
+// survive (all of them, or without accumulation those of the call's last
+// compression, [wlo, cend1)) are numbered k = 0 .. nL-1 in position order,
+// and only the last min(nL, s) survive, the k-th landing in ring slot
+// (sep_head + k) mod s. A block-wide count gives nL; a backward walk with
+// wavefront ballots finds the survivors. Under the dynamic trigger one
+// thread steps through the call's compressions, counting separators in a
+// bitmap of [cend0, t1) built block-wide in LDS. Surviving rows are copied
+// into the separator ring before any newly arriving token overwrites a
+// recent-ring slot. A call with T > 1 runs two kernels: one block per
+// sequence plans and writes pos / tok / state, then one block per (head,
+// sequence) copies K/V rows, reading the plan back from pos[] of the
+// separator ring. T == 1 runs one fused block per sequence.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -31,6 +39,10 @@ namespace sep {
 
 constexpr int kUpdThreads = 512;
 constexpr int kUpdWaves = kUpdThreads / kWave;
+// positions a dynamic-trigger plan covers at most (its bitmap): the ring
+// (<= SEP_MAX_DYN_RING) plus the new tokens of one chunk of a call
+constexpr int kSpan = 2 * SEP_MAX_DYN_RING;
+constexpr int kSpanWords = kSpan / 32;
 
 struct CacheArgs {
   char* k;
@@ -38,19 +50,26 @@ struct CacheArgs {
   int32_t* pos;
   int32_t* tok;
   int64_t* state;
-  const char* k_new;
+  const char* k_new;         // rows of this call's first token
   const char* v_new;
   const int32_t* ids_new;
   const int32_t* sep_ids;
   int n_sep;
-  int a, s, p, w, c, Hkv, D, esize, T;
+  int a, s, p, w;
+  int rw;                    // recent-ring size
+  int c;                     // slots per sequence
+  int Hkv, D, esize;
+  int T;                     // tokens of this call
+  int tstride;               // tokens per (sequence, head) row of k_new / ids_new
+  int dynamic, accumulate;
 };
 
 struct PlanHead {
   int64_t t0, t1, cend0, cend1;
-  int64_t nL;        // separators compacted by this call
+  int64_t wlo;       // separators in [wlo, cend1) can survive
+  int64_t nL;        // separators in [wlo, cend1)
   int head0, cnt0;
-  int64_t K1;
+  int reset;         // the separator ring is emptied first (no accumulation)
 };
 
 __device__ __forceinline__ int64_t n_compact(int64_t t, int a, int p, int w) {
@@ -141,68 +160,166 @@ struct SetList {
   __device__ __forceinline__ bool operator()(int32_t id) const { return in_set(id, set, n); }
 };
 
+// Separator bitmap of positions [x0, x0 + L) (L <= kSpan): bit o of word
+// o / 32 is set iff position x0 + o is a separator; pre[i] counts the set
+// bits of words 0 .. i-1. Built by the whole block; ends with a barrier.
+struct SepBits {
+  uint32_t* bits;
+  int32_t* pre;
+  // separators at offsets [0, o)
+  __device__ __forceinline__ int rank(int o) const {
+    const int wi = o >> 5, r = o & 31;
+    return pre[wi] + (r ? __popc(bits[wi] & ((1u << r) - 1u)) : 0);
+  }
+};
+
+template <class Set, class IdAt>
+__device__ void build_bits(SepBits& B, const Set& S, IdAt id_at, int64_t x0, int L, int32_t* wave_tot) {
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int nwords = (L + 31) / 32;
+  for (int base = 0; base < L; base += kWave * kUpdWaves) {
+    const int o = base + wv * kWave + lane;
+    const bool f = o < L && S(id_at(x0 + o));
+    const uint64_t m = ballot(f);
+    const int w0 = (base + wv * kWave) / 32;
+    if (lane == 0 && w0 < nwords) B.bits[w0] = static_cast<uint32_t>(m);
+    if (lane == 1 && w0 + 1 < nwords) B.bits[w0 + 1] = static_cast<uint32_t>(m >> 32);
+  }
+  __syncthreads();
+  // exclusive prefix of the word popcounts, kSpanWords / kUpdThreads words per thread
+  constexpr int PER = kSpanWords / kUpdThreads;
+  int c[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int wi = tid * PER + i;
+    c[i] = wi < nwords ? __popc(B.bits[wi]) : 0;
+    sum += c[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    incl += (lane >= off) ? y : 0;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  int before = incl - sum;
+  for (int i = 0; i < wv; ++i) before += wave_tot[i];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int wi = tid * PER + i;
+    if (wi <= nwords) B.pre[wi] = before;
+    before += c[i];
+  }
+  if (tid == kUpdThreads - 1 && nwords == kSpanWords) B.pre[kSpanWords] = before;   // the total
+  __syncthreads();
+}
+
 // Plan one sequence's call. Fills `ph` and the survivor list: entry (k mod s)
-// of lpos/lid holds the position and id of the k-th compacted separator for
-// the last min(nL, s) values of k. Reads state and tok[] of the recent ring;
-// nothing is written to global memory. `early(ph)` runs once `ph` is known,
-// before the plan's own loads, so that a caller can put its own independent
-// loads in flight. Ends with a barrier. The caller has loaded `S`.
+// of lpos/lid holds the position and id of the k-th separator of
+// [wlo, cend1) for the last min(nL, s) values of k. Reads state and tok[] of
+// the recent ring; nothing is written to global memory. `early(ph)` runs
+// once `ph` is known, before the plan's own loads, so that a caller can put
+// its own independent loads in flight. Ends with a barrier. The caller has
+// loaded `S`; `sb` (bitmap storage) is used under the dynamic trigger only.
 //
-// nL is a block-wide count over [cend0, cend1): the positions still in the
-// ring (at most p + w) one per thread, the new ones from ids_new in 16-byte
-// loads, kCountUnroll of them in flight per thread. The survivors are then
-// found by walking that range backwards in chunks of kWalkPer * kUpdThreads
-// positions (kWalkPer consecutive positions per thread) until min(nL, s)
-// separators are seen; the first chunk is loaded together with the count.
+// nL is a block-wide count over [wlo, cend1): the positions still in the
+// ring one per thread, the new ones from ids_new in 16-byte loads,
+// kCountUnroll of them in flight per thread. The survivors are then found by
+// walking that range backwards in chunks of kWalkPer * kUpdThreads positions
+// (kWalkPer consecutive positions per thread) until min(nL, s) separators
+// are seen; the first chunk is loaded together with the count.
 constexpr int kCountUnroll = 16;
 constexpr int kWalkPer = 8;
 
-template <class Set, class Early>
+template <bool DYN, class Set, class Early>
 __device__ void plan(const CacheArgs& A, int b, const Set& S, PlanHead& ph, int32_t* lpos, int32_t* lid,
-                     int32_t* wave_tot, Early early) {
+                     int32_t* wave_tot, SepBits sb, Early early) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wv = tid / kWave;
-  const int rw = A.p + A.w;
+  const int rw = A.rw;
   if (tid == 0) {
-    const int64_t* st = A.state + 4 * static_cast<int64_t>(b);
+    const int64_t* st = A.state + kStateWords * static_cast<int64_t>(b);
     ph.t0 = st[0];
-    const int64_t K0 = st[1];
+    ph.cend0 = A.a + st[1];
     ph.head0 = static_cast<int>(st[2]);
     ph.cnt0 = static_cast<int>(st[3]);
     ph.t1 = ph.t0 + A.T;
-    ph.K1 = n_compact(ph.t1, A.a, A.p, A.w);
-    ph.cend0 = A.a + K0 * (A.p + 1);
-    ph.cend1 = A.a + ph.K1 * (A.p + 1);
+    if (!DYN) {
+      ph.cend1 = A.a + n_compact(ph.t1, A.a, A.p, A.w) * (A.p + 1);
+      // without accumulation only the last compression's separators count
+      const bool comp = ph.cend1 > ph.cend0;
+      ph.wlo = (A.accumulate || !comp) ? ph.cend0 : ph.cend1 - (A.p + 1);
+      ph.reset = (!A.accumulate && comp) ? 1 : 0;
+    }
   }
   __syncthreads();
-  early(ph);
-  const int64_t t0 = ph.t0, cend0 = ph.cend0, cend1 = ph.cend1;
+  const int64_t t0 = ph.t0, cend0 = ph.cend0;
   const int32_t* tokb = A.tok + static_cast<int64_t>(b) * A.c;
-  const int32_t* idsb = A.ids_new + static_cast<int64_t>(b) * A.T;
+  const int32_t* idsb = A.ids_new + static_cast<int64_t>(b) * A.tstride;
   // id of position x (cend0 <= x < t1): the ring's tok[] before this call,
   // the new ids from t0 on
   auto id_at = [&](int64_t x) -> int32_t {
     const int32_t* src = (x < t0) ? tokb + slot_r(x, A.a, A.s, rw) : idsb + (x - t0);
     return ld_global(src);
   };
+  if (DYN) {
+    // the call's compressions, one after the other (thread 0), with the
+    // separators of [cend0, t1) in a bitmap
+    const int L = static_cast<int>(ph.t1 - cend0 > 0 ? ph.t1 - cend0 : 0);
+    build_bits(sb, S, id_at, cend0, L, wave_tot);
+    if (tid == 0) {
+      const int c = A.a + A.s + A.p + A.w;
+      int64_t cend = cend0, last_lo = -1;
+      int cnt = ph.cnt0;
+      const int64_t t1 = ph.t1;
+      for (;;) {
+        if (A.accumulate && cnt == A.s) {
+          // S stays full from here: a compression every p + 1 tokens
+          const int64_t x = cend + A.p + A.w;
+          if (x < t1) {
+            const int64_t k = (t1 - 1 - x) / (A.p + 1) + 1;
+            cend += k * (A.p + 1);
+            last_lo = cend - (A.p + 1);
+          }
+          break;
+        }
+        const int64_t x = cend + (c - A.a - cnt);
+        if (x >= t1) break;
+        const int64_t nc = x + 1 - A.w;
+        const int n = sb.rank(static_cast<int>(nc - cend0)) - sb.rank(static_cast<int>(cend - cend0));
+        const int acc = A.accumulate ? cnt + n : n;
+        cnt = acc < A.s ? acc : A.s;
+        last_lo = cend;
+        cend = nc;
+      }
+      ph.cend1 = cend;
+      const bool comp = cend > cend0;
+      ph.wlo = (A.accumulate || !comp) ? cend0 : last_lo;
+      ph.reset = (!A.accumulate && comp) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  early(ph);
+  const int64_t cend1 = ph.cend1, wlo = ph.wlo;
 
   // first chunk of the walk, loaded now
   int32_t wid[kWalkPer];
-  const bool walk = (A.s > 0) && (cend1 > cend0);
+  const bool walk = (A.s > 0) && (cend1 > wlo);
   if (walk) {
 #pragma unroll
     for (int u = 0; u < kWalkPer; ++u) {
       const int64_t x = cend1 - kWalkPer * kUpdThreads + kWalkPer * tid + u;
-      wid[u] = id_at(x >= cend0 ? x : cend0);
+      wid[u] = id_at(x >= wlo ? x : wlo);
     }
   }
 
-  // (1) nL = number of separators among the compacted positions
+  // (1) nL = number of separators in [wlo, cend1)
   int cnt = 0;
   const int64_t xr_end = cend1 < t0 ? cend1 : t0;
-  for (int64_t x = cend0 + tid; x < xr_end; x += kUpdThreads) cnt += S(ld_global(tokb + slot_r(x, A.a, A.s, rw))) ? 1 : 0;
-  const int64_t xn_beg = cend0 > t0 ? cend0 : t0;
+  for (int64_t x = wlo + tid; x < xr_end; x += kUpdThreads) cnt += S(ld_global(tokb + slot_r(x, A.a, A.s, rw))) ? 1 : 0;
+  const int64_t xn_beg = wlo > t0 ? wlo : t0;
   const int n_new = static_cast<int>(cend1 > xn_beg ? cend1 - xn_beg : 0);
   const int32_t* nb = idsb + (xn_beg - t0);
   // nb[0 .. n_head) up to a 16-byte boundary, then whole 16-byte groups, then the rest
@@ -237,19 +354,19 @@ __device__ void plan(const CacheArgs& A, int b, const Set& S, PlanHead& ph, int3
   const int64_t nsurv = (A.s > 0) ? (nL < A.s ? nL : A.s) : 0;
   __syncthreads();
 
-  // (2) survivors: walk [cend0, cend1) backwards; `after` counts the
+  // (2) survivors: walk [wlo, cend1) backwards; `after` counts the
   //     separators at higher positions than the current chunk. Thread tid
   //     owns positions lo + kWalkPer*tid + u, u = 0 .. kWalkPer-1.
   int64_t after = 0;
   // entry of the last separator: (nL - 1) mod s; from_end < s steps back from it
   const int li_last = (A.s > 0 && nL > 0) ? static_cast<int>((nL - 1) % A.s) : 0;
-  for (int64_t hi = cend1; hi > cend0 && after < nsurv; hi -= kWalkPer * kUpdThreads) {
+  for (int64_t hi = cend1; hi > wlo && after < nsurv; hi -= kWalkPer * kUpdThreads) {
     const int64_t lo = hi - kWalkPer * kUpdThreads;
     if (hi != cend1) {
 #pragma unroll
       for (int u = 0; u < kWalkPer; ++u) {
         const int64_t x = lo + kWalkPer * tid + u;
-        wid[u] = id_at(x >= cend0 ? x : cend0);
+        wid[u] = id_at(x >= wlo ? x : wlo);
       }
     }
     uint32_t fl = 0;   // bit u: position lo + kWalkPer*tid + u is a separator
@@ -257,7 +374,7 @@ __device__ void plan(const CacheArgs& A, int b, const Set& S, PlanHead& ph, int3
     int wtot = 0;
 #pragma unroll
     for (int u = 0; u < kWalkPer; ++u) {
-      const bool f = lo + kWalkPer * tid + u >= cend0 && S(wid[u]);
+      const bool f = lo + kWalkPer * tid + u >= wlo && S(wid[u]);
       const uint64_t m = ballot(f);
       fl |= f ? (1u << u) : 0u;
       above += (lane == 63) ? 0 : __popcll(m >> (lane + 1));
@@ -340,10 +457,10 @@ __device__ __forceinline__ void copy_rows(int nrows, int g0, int g1, int row_byt
 
 // K/V rows of new tokens that stay, for heads [g0, g1): initial slots, and
 // recent-ring slots for positions >= cend1 (those below cend1 were compacted
-// away, and a ring holds at most p + w positions).
+// away, and the ring holds at most rw positions).
 __device__ __forceinline__ void copy_new_rows(const CacheArgs& A, int b, int g0, int g1, int64_t t0,
                                               int64_t t1, int64_t cend1) {
-  const int rw = A.p + A.w;
+  const int rw = A.rw;
   const int row_bytes = A.D * A.esize;
   const int64_t cache_seq = static_cast<int64_t>(b) * A.Hkv;
   const int64_t keep_lo = t1 - rw > t0 ? t1 - rw : t0;
@@ -357,7 +474,7 @@ __device__ __forceinline__ void copy_new_rows(const CacheArgs& A, int b, int g0,
     const int dslot = (y < A.a) ? static_cast<int>(y) : slot_r(y, A.a, A.s, rw);
     const char* base_new = kv ? A.v_new : A.k_new;
     char* base_c = kv ? A.v : A.k;
-    *src = base_new + ((cache_seq + g) * A.T + (y - t0)) * row_bytes;
+    *src = base_new + ((cache_seq + g) * A.tstride + (y - t0)) * row_bytes;
     *dst = base_c + ((cache_seq + g) * A.c + dslot) * row_bytes;
   });
 }
@@ -366,23 +483,23 @@ enum { UPD_META = 1, UPD_FUSED = 2 };
 
 // UPD_META : grid (1, B), plan + pos / tok / state; K/V untouched.
 // UPD_FUSED: grid (1, B), everything (used for T == 1).
-template <int MODE, class Set>
+template <int MODE, bool DYN, class Set>
 __device__ void update_block(const CacheArgs& A, const Set& S, PlanHead& ph, int32_t* lpos, int32_t* lid,
-                             int32_t* wave_tot) {
+                             int32_t* wave_tot, SepBits sb) {
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
-  const int rw = A.p + A.w;
-  const int32_t* idsb = A.ids_new + static_cast<int64_t>(b) * A.T;
+  const int rw = A.rw;
+  const int32_t* idsb = A.ids_new + static_cast<int64_t>(b) * A.tstride;
   // New tokens that stay, as one list: i < n_init are initial positions
   // t0 + i, the rest the recent-ring tail from r_start on (positions below
-  // cend1 are compacted by this call, and a ring holds at most p + w). Their
-  // ids are loaded before the plan; the stores wait for it.
+  // cend1 are compacted by this call, and the ring holds at most rw). Their
+  // ids are loaded before the plan's count; the stores wait for it.
   constexpr int kKeepPre = 2;
   int64_t r_start = 0;
   int n_init = 0, n_keep = 0;
   int32_t kid[kKeepPre];
   auto keep_pos = [&](int i) -> int64_t { return (i < n_init) ? ph.t0 + i : r_start + (i - n_init); };
-  plan(A, b, S, ph, lpos, lid, wave_tot, [&](const PlanHead& h) {
+  plan<DYN>(A, b, S, ph, lpos, lid, wave_tot, sb, [&](const PlanHead& h) {
     const int64_t keep_lo = h.t1 - rw > h.t0 ? h.t1 - rw : h.t0;
     const int64_t r_lo = (h.cend1 > keep_lo) ? h.cend1 : keep_lo;
     r_start = r_lo > A.a ? r_lo : A.a;
@@ -402,7 +519,9 @@ __device__ void update_block(const CacheArgs& A, const Set& S, PlanHead& ph, int
   // survivor r (k = kfirst + r): list entry (li0 + r) mod s, ring slot
   // a + (d0 + r) mod s
   const int li0 = A.s > 0 ? static_cast<int>(kfirst % A.s) : 0;
-  const int d0 = A.s > 0 ? static_cast<int>((ph.head0 + kfirst) % A.s) : 0;
+  // an emptied ring restarts at its first slot, so that its layout depends
+  // on the last compression only (as after single-token calls)
+  const int d0 = A.s > 0 ? (ph.reset ? 0 : static_cast<int>((ph.head0 + kfirst) % A.s)) : 0;
   const int row_bytes = A.D * A.esize;
   const int64_t cache_seq = static_cast<int64_t>(b) * A.Hkv;
 
@@ -418,7 +537,7 @@ __device__ void update_block(const CacheArgs& A, const Set& S, PlanHead& ph, int
       if (x < t0) {
         *src = base_c + (crow + slot_r(x, A.a, A.s, rw)) * row_bytes;
       } else {
-        *src = base_new + ((cache_seq + g) * A.T + (x - t0)) * row_bytes;
+        *src = base_new + ((cache_seq + g) * A.tstride + (x - t0)) * row_bytes;
       }
       *dst = base_c + (crow + dslot) * row_bytes;
     });
@@ -429,6 +548,14 @@ __device__ void update_block(const CacheArgs& A, const Set& S, PlanHead& ph, int
 
   int32_t* posb = A.pos + static_cast<int64_t>(b) * A.c;
   int32_t* tokb = A.tok + static_cast<int64_t>(b) * A.c;
+  // without accumulation a compression empties the separator ring first
+  if (ph.reset) {
+    for (int j = tid; j < A.s; j += kUpdThreads) {
+      st_global(posb + A.a + j, -1);
+      st_global(tokb + A.a + j, -1);
+    }
+    __syncthreads();
+  }
   // survivors -> separator-ring metadata (ids were captured by the plan)
   for (int r = tid; r < nsurv; r += kUpdThreads) {
     const int li = wrap_add(li0, r, A.s);
@@ -457,42 +584,46 @@ __device__ void update_block(const CacheArgs& A, const Set& S, PlanHead& ph, int
     if (tid + u * kUpdThreads < n_keep) put(tid + u * kUpdThreads, kid[u]);
   for (int i = tid + kKeepPre * kUpdThreads; i < n_keep; i += kUpdThreads) put(i, ld_global(idsb + (keep_pos(i) - t0)));
   if (tid == 0) {
-    int64_t* st = A.state + 4 * static_cast<int64_t>(b);
+    int64_t* st = A.state + kStateWords * static_cast<int64_t>(b);
     st[0] = t1;
-    st[1] = ph.K1;
+    st[1] = cend1 - A.a;
+    st[4] = ph.cend0 - A.a;
     if (A.s > 0) {
-      st[2] = (ph.head0 + nL) % A.s;
-      const int64_t cnt = ph.cnt0 + nL;
+      st[2] = ph.reset ? nsurv % A.s : (ph.head0 + nL) % A.s;
+      const int64_t cnt = (ph.reset ? 0 : ph.cnt0) + nL;
       st[3] = cnt < A.s ? cnt : A.s;
     }
   }
 }
 
-template <int MODE>
+template <int MODE, bool DYN>
 __global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
   extern __shared__ int32_t dyn[];
   __shared__ int32_t set_lds[SEP_MAX_SEP_IDS_];
   __shared__ int32_t set_tab[MODE == UPD_FUSED ? 1 : kHashSize];
   __shared__ int32_t wave_tot[2 * kUpdWaves];
+  __shared__ uint32_t sb_bits[DYN ? kSpanWords : 1];
+  __shared__ int32_t sb_pre[DYN ? kSpanWords + 1 : 1];
   __shared__ PlanHead ph;
   const int smax = A.s > 0 ? A.s : 1;
   int32_t* lpos = dyn;
   int32_t* lid = dyn + smax;
+  SepBits sb{sb_bits, sb_pre};
   SetList L;
   if (MODE == UPD_FUSED) {
     // T == 1. The new K/V row, its id and the state are loaded together;
-    // when no compaction is due (K(t0 + 1) == K(t0)) the token only takes
-    // its slot: the row, one pos/tok entry and state[0], with no barrier.
-    // Otherwise the general block plans the compaction (p + 1 ids, no table).
+    // when no compression is due the token only takes its slot: the row, one
+    // pos/tok entry and the state words, with no barrier. Otherwise the
+    // general block plans the compression (few ids, no table).
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
-    const int rw = A.p + A.w;
+    const int rw = A.rw;
     const int row_bytes = A.D * A.esize;
     const int cpr = row_bytes / 16;
     const int W = A.Hkv * 2 * cpr;
-    const int64_t* st = A.state + 4 * static_cast<int64_t>(b);
-    const int64_t t0 = ld_global(st), K0 = ld_global(st + 1);
-    const int32_t id = ld_global(A.ids_new + b);
+    const int64_t* st = A.state + kStateWords * static_cast<int64_t>(b);
+    const int64_t t0 = ld_global(st), ncomp = ld_global(st + 1), cnt0 = ld_global(st + 3);
+    const int32_t id = ld_global(A.ids_new + static_cast<int64_t>(b) * A.tstride);
     u32x4 val[2];
     int col[2];
 #pragma unroll
@@ -501,11 +632,14 @@ __global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
       if (col[u] < W) {
         const int kv = (col[u] / cpr) & 1;
         const int g = col[u] / (2 * cpr);
-        const char* src = (kv ? A.v_new : A.k_new) + (static_cast<int64_t>(b) * A.Hkv + g) * row_bytes;
+        const char* src = (kv ? A.v_new : A.k_new) + (static_cast<int64_t>(b) * A.Hkv + g) * A.tstride * row_bytes;
         val[u] = ld_global_nt(reinterpret_cast<const u32x4*>(src + 16 * (col[u] % cpr)));
       }
     }
-    if (n_compact(t0 + 1, A.a, A.p, A.w) == K0) {
+    // R after the push holds t0 + 1 - cend0 entries
+    const int64_t r_after = t0 + 1 - (A.a + ncomp);
+    const int64_t r_cap = DYN ? (A.s + A.p + A.w - cnt0) : (A.p + A.w);
+    if (t0 < A.a || r_after <= r_cap) {
       const int slot = t0 < A.a ? static_cast<int>(t0) : slot_r(t0, A.a, A.s, rw);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -520,57 +654,60 @@ __global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
         const int kv = (c0 / cpr) & 1;
         const int g = c0 / (2 * cpr);
         const int64_t hrow = static_cast<int64_t>(b) * A.Hkv + g;
-        const u32x4 v = ld_global_nt(reinterpret_cast<const u32x4*>((kv ? A.v_new : A.k_new) + hrow * row_bytes +
-                                                                    16 * (c0 % cpr)));
+        const u32x4 v = ld_global_nt(reinterpret_cast<const u32x4*>((kv ? A.v_new : A.k_new) +
+                                                                    hrow * A.tstride * row_bytes + 16 * (c0 % cpr)));
         st_global(reinterpret_cast<u32x4*>((kv ? A.v : A.k) + (hrow * A.c + slot) * row_bytes + 16 * (c0 % cpr)), v);
       }
       if (tid == 0) {
+        int64_t* stw = A.state + kStateWords * static_cast<int64_t>(b);
         st_global(A.pos + static_cast<int64_t>(b) * A.c + slot, static_cast<int32_t>(t0));
         st_global(A.tok + static_cast<int64_t>(b) * A.c + slot, id);
-        st_global(A.state + 4 * static_cast<int64_t>(b), t0 + 1);
+        st_global(stw, t0 + 1);
+        st_global(stw + 4, ncomp);
       }
       return;
     }
     L.load(A.sep_ids, A.n_sep, nullptr, set_lds);
-    update_block<MODE>(A, L, ph, lpos, lid, wave_tot);
+    update_block<MODE, DYN>(A, L, ph, lpos, lid, wave_tot, sb);
   } else {
     SetHash H;
     H.load(A.sep_ids, A.n_sep, set_tab, set_lds);
     if (H.exact) {
-      update_block<MODE>(A, H, ph, lpos, lid, wave_tot);
+      update_block<MODE, DYN>(A, H, ph, lpos, lid, wave_tot, sb);
     } else {
       L.set = set_lds;
       L.n = A.n_sep;
-      update_block<MODE>(A, L, ph, lpos, lid, wave_tot);
+      update_block<MODE, DYN>(A, L, ph, lpos, lid, wave_tot, sb);
     }
   }
 }
 
 // K/V rows of a call with T > 1, grid (Hkv, B), one head per block; runs
 // after update_kernel<UPD_META> of the same call and plans nothing itself.
-// From the state META left (t1 = t0 + T, sep_head1) it takes t0, cend0 and
-// cend1. A separator-ring slot whose pos[] is >= cend0 was written by this
-// call (every earlier entry was compacted below cend0); those slots form the
-// ring range ending just before sep_head1. Each such row comes from the
-// recent ring (position < t0: K/V there are untouched until step (2) below)
-// or from the new rows.
+// From the state META left it takes t1 (t0 = t1 - T), cend1 and cend0 (state
+// words 1 and 4). A separator-ring slot whose pos[] is >= cend0 was written
+// by this call (every older entry was compacted below cend0, or was cleared
+// when the call emptied the ring); those slots form the ring range ending
+// just before the new sep_head. Each such row comes from the recent ring
+// (position < t0: K/V there are untouched until step (2) below) or from the
+// new rows.
 __global__ void __launch_bounds__(kUpdThreads) data_kernel(CacheArgs A) {
   extern __shared__ int32_t dyn[];
   __shared__ int32_t wave_tot[kUpdWaves];
-  __shared__ int64_t st_s[3];
+  __shared__ int64_t st_s[kStateWords];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wv = tid / kWave;
   const int b = blockIdx.y;
   const int g = blockIdx.x;
-  const int rw = A.p + A.w;
+  const int rw = A.rw;
   const int row_bytes = A.D * A.esize;
   const int64_t cache_seq = static_cast<int64_t>(b) * A.Hkv;
-  if (tid < 3) st_s[tid] = A.state[4 * static_cast<int64_t>(b) + tid];
+  if (tid < kStateWords) st_s[tid] = A.state[kStateWords * static_cast<int64_t>(b) + tid];
   __syncthreads();
   const int64_t t1 = st_s[0], t0 = t1 - A.T;
-  const int64_t cend1 = A.a + st_s[1] * (A.p + 1);
-  const int64_t cend0 = A.a + n_compact(t0, A.a, A.p, A.w) * (A.p + 1);
+  const int64_t cend1 = A.a + st_s[1];
+  const int64_t cend0 = A.a + st_s[4];
 
   if (A.s > 0) {
     const int head1 = static_cast<int>(st_s[2]);
@@ -600,7 +737,7 @@ __global__ void __launch_bounds__(kUpdThreads) data_kernel(CacheArgs A) {
       if (x < t0) {
         *src = base_c + (crow + slot_r(x, A.a, A.s, rw)) * row_bytes;
       } else {
-        *src = base_new + ((cache_seq + gg) * A.T + (x - t0)) * row_bytes;
+        *src = base_new + ((cache_seq + gg) * A.tstride + (x - t0)) * row_bytes;
       }
       *dst = base_c + (crow + A.a + j) * row_bytes;
     });
@@ -617,12 +754,26 @@ __global__ void __launch_bounds__(kUpdThreads) reset_kernel(int32_t* pos, int32_
     pos[static_cast<int64_t>(b) * c + i] = -1;
     tok[static_cast<int64_t>(b) * c + i] = -1;
   }
-  if (threadIdx.x < 4) state[4 * static_cast<int64_t>(b) + threadIdx.x] = 0;
+  if (threadIdx.x < kStateWords) state[kStateWords * static_cast<int64_t>(b) + threadIdx.x] = 0;
 }
 
 hipError_t launch_cache_reset(const sep_cache& c, hipStream_t st) {
-  const int cap = c.a + c.s + c.p + c.w;
-  hipLaunchKernelGGL(reset_kernel, dim3(c.B), dim3(kUpdThreads), 0, st, c.pos, c.tok, c.state, cap);
+  hipLaunchKernelGGL(reset_kernel, dim3(c.B), dim3(kUpdThreads), 0, st, c.pos, c.tok, c.state,
+                     cache_slots(c));
+  return hipGetLastError();
+}
+
+template <bool DYN>
+static hipError_t launch_update_chunk(const sep_cache& c, const CacheArgs& A, size_t dyn, hipStream_t st) {
+  if (A.T == 1) {
+    hipLaunchKernelGGL((update_kernel<UPD_FUSED, DYN>), dim3(1, c.B), dim3(kUpdThreads), dyn, st, A);
+    return hipGetLastError();
+  }
+  // metadata (and the plan) first; the K/V copy reads what it wrote
+  hipLaunchKernelGGL((update_kernel<UPD_META, DYN>), dim3(1, c.B), dim3(kUpdThreads), dyn, st, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(data_kernel, dim3(c.Hkv, c.B), dim3(kUpdThreads), dyn, st, A);
   return hipGetLastError();
 }
 
@@ -635,31 +786,36 @@ hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void
   A.pos = c.pos;
   A.tok = c.tok;
   A.state = c.state;
-  A.k_new = static_cast<const char*>(k_new);
-  A.v_new = static_cast<const char*>(v_new);
-  A.ids_new = ids_new;
   A.sep_ids = sep_ids;
   A.n_sep = n_sep;
   A.a = c.a;
   A.s = c.s;
   A.p = c.p;
   A.w = c.w;
-  A.c = c.a + c.s + c.p + c.w;
+  A.rw = cache_ring(c);
+  A.c = cache_slots(c);
   A.Hkv = c.Hkv;
   A.D = c.D;
   A.esize = (c.dtype == SEP_BF16) ? 2 : 4;
-  A.T = T;
+  A.tstride = T;
+  A.dynamic = (c.policy & SEP_POLICY_DYNAMIC) ? 1 : 0;
+  A.accumulate = (c.policy & SEP_POLICY_NO_ACCUM) ? 0 : 1;
   const size_t dyn = 2 * sizeof(int32_t) * static_cast<size_t>(c.s > 0 ? c.s : 1);
-  if (T == 1) {
-    hipLaunchKernelGGL(update_kernel<UPD_FUSED>, dim3(1, c.B), dim3(kUpdThreads), dyn, st, A);
-    return hipGetLastError();
+  const size_t row_bytes = static_cast<size_t>(c.D) * A.esize;
+  // a dynamic-trigger plan covers the ring plus the new tokens in one
+  // bitmap of kSpan positions, so a long call runs as consecutive chunks
+  // (T tokens at once equal T single updates, hence any split of them)
+  const int chunk = A.dynamic ? kSpan - A.rw : T;
+  for (int off = 0; off < T; off += chunk) {
+    A.T = T - off < chunk ? T - off : chunk;
+    A.k_new = static_cast<const char*>(k_new) + off * row_bytes;
+    A.v_new = static_cast<const char*>(v_new) + off * row_bytes;
+    A.ids_new = ids_new + off;
+    const hipError_t e = A.dynamic ? launch_update_chunk<true>(c, A, dyn, st)
+                                   : launch_update_chunk<false>(c, A, dyn, st);
+    if (e != hipSuccess) return e;
   }
-  // metadata (and the plan) first; the K/V copy reads what it wrote
-  hipLaunchKernelGGL(update_kernel<UPD_META>, dim3(1, c.B), dim3(kUpdThreads), dyn, st, A);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(data_kernel, dim3(c.Hkv, c.B), dim3(kUpdThreads), dyn, st, A);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace sep

@@ -36,7 +36,7 @@ struct DecodeArgs {
   const int64_t* state;
   uint16_t* out;
   float* lse;
-  int a, s, p, w, c, Hq, Hkv, G;
+  int a, s, p, w, rw, c, Hq, Hkv, G;
   float scale_log2;
 };
 
@@ -61,17 +61,17 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
   const int g = blockIdx.x;
   const int b = blockIdx.y;
   const int G = A.G;
-  const int rw = A.p + A.w;
+  const int rw = A.rw;                          // recent-ring size
   uint16_t* vt = reinterpret_cast<uint16_t*>(arena) + wave * (D * VSTR);
 
   // ---- cache geometry of this sequence (wave-uniform scalars)
-  const int64_t* st = A.state + 4 * static_cast<int64_t>(b);
+  const int64_t* st = A.state + kStateWords * static_cast<int64_t>(b);
   const int64_t t = st[0];
-  const int64_t K = st[1];
+  const int64_t ncomp = st[1];                   // entries compacted out of R so far
   const int head = static_cast<int>(st[2]);
   const int cnt = static_cast<int>(st[3]);
   const int n_init = static_cast<int>(t < A.a ? t : A.a);
-  const int64_t cend = A.a + K * (A.p + 1);
+  const int64_t cend = A.a + ncomp;
   const int64_t rec_lo = cend > A.a ? cend : A.a;
   const int n_rec = static_cast<int>(t > rec_lo ? t - rec_lo : 0);
   const int u_s = n_init;                        // first separator-ring entry
@@ -289,7 +289,8 @@ hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, co
   A.s = c.s;  // the separator-ring branch is only reached when cnt > 0, i.e. s >= 1
   A.p = c.p;
   A.w = c.w;
-  A.c = c.a + c.s + c.p + c.w;
+  A.rw = cache_ring(c);
+  A.c = cache_slots(c);
   A.Hq = Hq;
   A.Hkv = c.Hkv;
   A.G = Hq / c.Hkv;

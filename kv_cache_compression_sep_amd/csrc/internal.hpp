@@ -10,6 +10,15 @@
 
 namespace sep {
 
+// int64 words of cache state per sequence (see sep_cache in sepattn.h)
+constexpr int kStateWords = 8;
+
+// recent-ring size and slot count of a cache under its policy
+inline int cache_ring(const sep_cache& c) {
+  return c.p + c.w + ((c.policy & SEP_POLICY_DYNAMIC) ? c.s : 0);
+}
+inline int cache_slots(const sep_cache& c) { return c.a + c.s + cache_ring(c); }
+
 hipError_t launch_is_sep(const int32_t* ids, int64_t N, const int32_t* sep_ids, int n_sep,
                          uint8_t* is_sep, hipStream_t st);
 hipError_t launch_tile_class(const uint8_t* is_sep, int B, int S, int a, int n, int tq, int tk,

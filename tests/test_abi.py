@@ -48,15 +48,17 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sep_version() >= 10000
+    assert lib.sep_version() >= 10100
     for code in range(-7, 1):
         assert lib.sep_status_string(code)
     assert lib.sep_status_string(-99) == b"unknown status"
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(_lib.SepCacheStruct) == 8 * 4 + 5 * 8
+    # 8 int32, 5 pointers, the int32 policy (padded to 8 bytes)
+    assert ctypes.sizeof(_lib.SepCacheStruct) == 8 * 4 + 5 * 8 + 8
     assert _lib.SepCacheStruct.k.offset == 32
+    assert _lib.SepCacheStruct.policy.offset == 72
 
 
 def test_mask_build_argument_checks(lib):
@@ -107,7 +109,7 @@ def test_prefill_argument_checks(lib):
 
 def _cache(**kw):
     d = dict(a=4, s=64, p=64, w=256, B=1, Hkv=8, D=128, dtype=1, k=FAKE, v=FAKE, pos=FAKE,
-             tok=FAKE, state=FAKE)
+             tok=FAKE, state=FAKE, policy=0)
     d.update(kw)
     return _lib.SepCacheStruct(*d.values())
 
@@ -132,6 +134,19 @@ def test_cache_contract_from_the_pages(lib):
     assert lib.sep_cache_update(ctypes.byref(c), FAKE, FAKE, FAKE, 0, FAKE, 1, None) == E.SEP_ERR_SHAPE
     assert lib.sep_cache_update(ctypes.byref(c), None, FAKE, FAKE, 1, FAKE, 1, None) == E.SEP_ERR_NULL
     assert lib.sep_cache_reset(ctypes.byref(_cache(w=0)), None) == E.SEP_ERR_PARAM
+
+
+def test_cache_policy_checks(lib):
+    """Policy bits: SEP_POLICY_DYNAMIC (1) and SEP_POLICY_NO_ACCUM (2) only; the
+    dynamic trigger's recent ring (s + p + w slots) is bounded."""
+    E = _lib
+    upd = lambda c: lib.sep_cache_update(ctypes.byref(c), FAKE, FAKE, FAKE, 1, FAKE, 1, None)
+    assert upd(_cache(policy=4)) == E.SEP_ERR_PARAM
+    assert upd(_cache(policy=-1)) == E.SEP_ERR_PARAM
+    assert upd(_cache(policy=1, s=64, p=16384, w=16384)) == E.SEP_ERR_PARAM   # ring 32832 > 32768
+    for pol in (1, 2, 3):
+        c = _cache(policy=pol)
+        assert lib.sep_cache_update(ctypes.byref(c), FAKE, FAKE, FAKE, 0, FAKE, 1, None) == E.SEP_ERR_SHAPE
 
 
 def test_decode_argument_checks(lib):

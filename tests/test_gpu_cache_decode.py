@@ -17,7 +17,8 @@ import torch
 
 import oracle
 from inputs import configs, gen
-from kv_cache_compression_sep_amd import SepCache, sep_attn_decode, sep_cache_update
+from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache,
+                                          sep_attn_decode, sep_cache_update)
 
 from .gpu_util import check_close, from_dev, to_dev
 
@@ -44,13 +45,7 @@ class Stream:
 
 
 def live_slots(cache, b):
-    t, K, head, cnt = [int(x) for x in cache.state[b].cpu().numpy()]
-    a, s, p, w = cache.a, cache.s, cache.p, cache.w
-    I = list(range(min(a, t)))
-    S = [a + (head - cnt + i) % s for i in range(cnt)] if s > 0 else []
-    cend = a + K * (p + 1)
-    R = [a + s + (x - a) % (p + w) for x in range(max(cend, a), t)] if t > a else []
-    return I, S, R
+    return cache.slots_of(b)
 
 
 def check_cache(cache, sims, stream):
@@ -68,7 +63,7 @@ def check_cache(cache, sims, stream):
             if wpos:
                 assert np.array_equal(kc[b][:, slots], stream.k[b][:, wpos].view(np.int16)), (b, name)
                 assert np.array_equal(vc[b][:, slots], stream.v[b][:, wpos].view(np.int16)), (b, name)
-        dead = sorted(set(range(cache.c)) - set(I) - set(S) - set(R))
+        dead = sorted(set(range(cache.slots)) - set(I) - set(S) - set(R))
         assert (pos[b, dead] == -1).all() and (tok[b, dead] == -1).all(), b
         assert sim.occupancy() == len(I) + len(S) + len(R)
 
@@ -85,13 +80,35 @@ PARAMS = [
 ]
 
 
+# cache policies (P1 "KV Cache Manager" pseudo-code): the dynamic trigger and
+# SEP_ACCUMULATION off, on the SepLLM parameter sets
+POLICIES = [SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM]
+POLICY_PARAMS = [(4, 6, 5, 9), (2, 1, 3, 1), (3, 10, 70, 20), (1, 40, 300, 7), (4, 64, 64, 256)]
+
+
+def sim_for(params, policy):
+    a, s, p, w = params
+    return oracle.CacheSim(a, s, p, w, SEP_IDS, dynamic=bool(policy & SEP_POLICY_DYNAMIC),
+                           accumulate=not (policy & SEP_POLICY_NO_ACCUM))
+
+
 @pytest.mark.parametrize("params", PARAMS, ids=[str(p) for p in PARAMS])
 def test_single_token_updates_match_simulation(params):
+    single_token_updates(params, 0)
+
+
+@pytest.mark.parametrize("policy", POLICIES)
+@pytest.mark.parametrize("params", POLICY_PARAMS, ids=[str(p) for p in POLICY_PARAMS])
+def test_policy_single_token_updates_match_simulation(params, policy):
+    single_token_updates(params, policy)
+
+
+def single_token_updates(params, policy):
     a, s, p, w = params
     T = min(3 * (a + s + p + w) + 50, 1400)
     st = Stream(zlib.crc32(repr(params).encode()), 2, 4, 2, 64, T, 0.3)
-    cache = SepCache(2, 2, 64, a, s, p, w)
-    sims = [oracle.CacheSim(a, s, p, w, SEP_IDS) for _ in range(2)]
+    cache = SepCache(2, 2, 64, a, s, p, w, policy=policy)
+    sims = [sim_for(params, policy) for _ in range(2)]
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
     every = max(1, T // 60)
     for t in range(T):
@@ -122,22 +139,33 @@ def _cuts(T, mode, params, rng):
 @pytest.mark.parametrize("mode", ["random", "small", "wrap"])
 @pytest.mark.parametrize("params", PARAMS, ids=[str(p) for p in PARAMS])
 def test_bulk_updates_equal_single_updates(params, mode):
+    bulk_equals_single(params, mode, 0)
+
+
+@pytest.mark.parametrize("mode", ["random", "wrap"])
+@pytest.mark.parametrize("policy", POLICIES)
+@pytest.mark.parametrize("params", POLICY_PARAMS, ids=[str(p) for p in POLICY_PARAMS])
+def test_policy_bulk_updates_equal_single_updates(params, policy, mode):
+    bulk_equals_single(params, mode, policy)
+
+
+def bulk_equals_single(params, mode, policy):
     a, s, p, w = params
     T = min(4 * (a + s + p + w) + 77, 2000)
     st = Stream(zlib.crc32(repr(params).encode()) + 1, 3, 4, 2, 128, T, 0.25)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    one = SepCache(3, 2, 128, a, s, p, w)
-    bulk = SepCache(3, 2, 128, a, s, p, w)
+    one = SepCache(3, 2, 128, a, s, p, w, policy=policy)
+    bulk = SepCache(3, 2, 128, a, s, p, w, policy=policy)
     for t in range(T):
         st.push_gpu(one, t, t + 1, d_sep)
     cuts = _cuts(T, mode, params, np.random.default_rng(T))
     for t0, t1 in zip(cuts[:-1], cuts[1:]):
         st.push_gpu(bulk, t0, t1, d_sep)
     torch.cuda.synchronize()
-    assert torch.equal(one.state, bulk.state)
+    assert torch.equal(one.state[:, :4], bulk.state[:, :4])    # word 4 records the last call
     assert torch.equal(one.pos, bulk.pos)
     assert torch.equal(one.tok, bulk.tok)
-    sims = [oracle.CacheSim(a, s, p, w, SEP_IDS) for _ in range(3)]
+    sims = [sim_for(params, policy) for _ in range(3)]
     for b in range(3):
         sims[b].push_many([oracle.Entry(t, int(st.ids[b, t])) for t in range(T)])
     check_cache(bulk, sims, st)
@@ -152,16 +180,20 @@ DECODE_CASES = [
     (1, 12, 3, 64, 4, 20, 2, 40, 5),      # cache still filling the initial block
     (2, 4, 2, 128, 4, 0, 0, 50, 200),     # StreamingLLM mode
     (1, 16, 16, 128, 4, 256, 28, 512, 1500),
+    # the dynamic trigger and no accumulation (the recent ring grows past p + w)
+    (2, 32, 8, 128, 4, 64, 16, 96, 700, SEP_POLICY_DYNAMIC),
+    (1, 8, 2, 64, 2, 9, 5, 20, 300, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM),
 ]
 
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
 def test_decode_matches_oracle(case):
-    B, Hq, Hkv, D, a, s, p, w, T = case
+    B, Hq, Hkv, D, a, s, p, w, T = case[:9]
+    policy = case[9] if len(case) > 9 else 0
     st = Stream(zlib.crc32(repr(case).encode()), B, Hq, Hkv, D, T + 40, 0.2)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    cache = SepCache(B, Hkv, D, a, s, p, w)
-    sims = [oracle.CacheSim(a, s, p, w, SEP_IDS) for _ in range(B)]
+    cache = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
+    sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     st.push_gpu(cache, 0, T, d_sep)
     for b in range(B):
         sims[b].push_many([oracle.Entry(t, int(st.ids[b, t])) for t in range(T)])

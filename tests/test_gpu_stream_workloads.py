@@ -27,14 +27,7 @@ pytestmark = pytest.mark.gpu
 
 
 def logical(cache, b):
-    st = [int(x) for x in cache.state[b].cpu().numpy()]
-    t, K, head, cnt = st
-    a, s, p, w = cache.a, cache.s, cache.p, cache.w
-    I = list(range(min(a, t)))
-    S = [a + (head - cnt + i) % s for i in range(cnt)] if s > 0 else []
-    cend = a + K * (p + 1)
-    R = [a + s + (x - a) % (p + w) for x in range(max(cend, a), t)] if t > a else []
-    return I, S, R
+    return cache.slots_of(b)
 
 
 def compare_state(cache, b, sim, ids, k_of, v_of):
@@ -92,6 +85,7 @@ def test_stream_decode_first_65536_steps():
             st, pos, tok, kk, vv = snaps[t + 1]
             view = SepCache.__new__(SepCache)
             view.a, view.s, view.p, view.w, view.c = cfg.a, cfg.s, cfg.p, cfg.w, cfg.c
+            view.ring, view.policy = cfg.p + cfg.w, 0
             view.state, view.pos, view.tok, view.k, view.v = st, pos, tok, kk, vv
             compare_state(view, 0, sim, ids, k_of, v_of)
             assert sim.occupancy() <= cfg.c
@@ -184,6 +178,7 @@ def test_batched_decode_workload():
                 st, pos, tok, kc, vc = snaps[j + 1]
                 view = SepCache.__new__(SepCache)
                 view.a, view.s, view.p, view.w, view.c = cfg.a, cfg.s, cfg.p, cfg.w, cfg.c
+                view.ring, view.policy = cfg.p + cfg.w, 0
                 view.state, view.pos, view.tok, view.k, view.v = st, pos, tok, kc, vc
                 compare_state(view, b, sims[b], ids[b], kr, vr)
         print(f"[batched] sequence {b} matches", flush=True)
