@@ -254,7 +254,42 @@ def bench_batched(args, torch, sa, configs, gen):
     ms_steps = e0.elapsed_time(e1)
     ms_dec = float(sum(a.elapsed_time(b) for a, b in dec_ev))
     assert int(cache.state[0, 0]) == H + cfg.steps
+    # the same history and 32 decode steps under the other cache policies
+    # (the manager's trigger, accumulation off): ingest and decode rates on
+    # their algorithmic bytes, and the mean occupancy they leave
+    policy = {}
+    for name, pol in (("dynamic", sa.SEP_POLICY_DYNAMIC), ("no_accum", sa.SEP_POLICY_NO_ACCUM),
+                      ("dynamic_no_accum", sa.SEP_POLICY_DYNAMIC | sa.SEP_POLICY_NO_ACCUM)):
+        pc = sa.SepCache(B, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w, policy=pol)
+        sa.sep_cache_update(pc, hk, hv, hist_ids, sep)
+        tt = []
+        for _ in range(3):
+            pc.reset()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            sa.sep_cache_update(pc, hk, hv, hist_ids, sep)
+            e1.record(st)
+            torch.cuda.synchronize()
+            tt.append(e0.elapsed_time(e1))
+        occ_p = _occupancy(pc)
+        ms_p = float(np.median(tt))
+        pout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for j in range(32):
+            sa.sep_attn_decode(pq[j], pk[j], pv[j], pc, 1.0 / math.sqrt(D), out=pout)
+        e1.record(st)
+        torch.cuda.synchronize()
+        us_dec = e0.elapsed_time(e1) * 1e3 / 32
+        dec_b = int(((occ_p + 1) * 2 * row).sum()) + 2 * B * Hq * D * 2
+        policy[name] = dict(ingest_ms=ms_p, ingest_GBps=(B * H * 4 + 4 * int(occ_p.sum()) * row) / (ms_p * 1e-3) / 1e9,
+                            mean_occupancy=float(occ_p.mean()), decode_us=us_dec,
+                            decode_GBps=dec_b / (us_dec * 1e-6) / 1e9)
+        log(f"policy {name}: ingest {ms_p:.2f} ms ({policy[name]['ingest_GBps']:.0f} GB/s), occupancy "
+            f"{occ_p.mean():.0f}, decode {us_dec:.1f} us ({policy[name]['decode_GBps']:.0f} GB/s)")
+        del pc
     res = dict(
+        policies=policy,
         ingest_ms=ms_ingest, ingest_GBps=ingest_bytes / (ms_ingest * 1e-3) / 1e9,
         steps=cfg.steps, step_us=ms_steps * 1e3 / cfg.steps,
         kv_GBps=total_bytes / (ms_steps * 1e-3) / 1e9,
