@@ -55,6 +55,45 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, M: np.ndarray, scale:
     return out, lse
 
 
+def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, M: np.ndarray, scale: float,
+                       dout: np.ndarray):
+    """Gradients of the prefill attention of one sequence (the training use of
+    Sep-Attention: P1 "Training-SepLLM" trains through the same mask).
+
+    For L = sum(dout * O), with P the softmax weights of query head h over
+    kv head g = h // G (P2 §1.2: scaled scores, -inf where M = 0):
+        dV_g  = sum over the G heads h of P_h^T dout_h
+        dP_h  = dout_h V_g^T
+        dS_h  = P_h * (dP_h - rowsum(dout_h * O_h))
+        dQ_h  = scale * dS_h K_g
+        dK_g  = scale * sum over the heads h of dS_h^T Q_h
+    (the chain rule through the row softmax: d softmax = P * (dP - (P dP)
+    summed over the row), and rowsum(P * dP) = rowsum(dout * O)).
+    q/dout [Hq, S, D], k/v [Hkv, S, D], M [S, S] bool; float64.
+    Returns dq [Hq, S, D], dk, dv [Hkv, S, D] and delta = rowsum(dout * O)
+    [Hq, S]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    Hq, S, D = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    out, _, P = attention(q, k, v, M, scale, return_weights=True)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    delta = (dout * out).sum(axis=-1)
+    for h in range(Hq):
+        g = h // G
+        dv[g] += P[h].T @ dout[h]
+        dP = dout[h] @ v[g].T
+        dS = P[h] * (dP - delta[h][:, None])
+        dq[h] = scale * (dS @ k[g])
+        dk[g] += scale * (dS.T @ q[h])
+    return dq, dk, dv, delta
+
+
 def attention_rows(q_rows, k, v, M_rows, scale, kv_head_of):
     """Prefill attention for a subset of query rows.
 

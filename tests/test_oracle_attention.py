@@ -179,3 +179,99 @@ def test_planted_attention_mistakes_fail_the_pin(mutant):
     M = oracle.sep_mask(flags, 2, 3)
     ref = loop_attention(q, k, v, flags, 2, 3, 1 / math.sqrt(3))
     assert not np.allclose(mutant(q, k, v, M, 1 / math.sqrt(3)), ref, atol=1e-9)
+
+
+# ------------------------------------------------------------ backward pass
+def _loss(q, k, v, M, scale, dout):
+    out, _ = oracle.attention(q, k, v, M, scale)
+    return float((out * dout).sum())
+
+
+def test_backward_matches_finite_differences():
+    """dL/dx for L = sum(dout * O), by central differences of the forward
+    oracle (no gradient formula involved), on tiny GQA cases."""
+    rng = np.random.default_rng(131)
+    for Hq, Hkv, S, D, a, n in [(2, 1, 7, 3, 1, 2), (4, 2, 9, 2, 2, 3), (2, 2, 6, 4, 0, 1)]:
+        q, k, v, flags = rand_case(rng, Hq, Hkv, S, D, a, n, 0.3)
+        M = oracle.sep_mask(flags, a, n)
+        dout = rng.standard_normal((Hq, S, D))
+        scale = 0.7
+        dq, dk, dv, _ = oracle.attention_backward(q, k, v, M, scale, dout)
+        eps = 1e-6
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp = x.copy(); xp[idx] += eps
+                xm = x.copy(); xm[idx] -= eps
+                args_p = dict(q=q, k=k, v=v); args_p[name] = xp
+                args_m = dict(q=q, k=k, v=v); args_m[name] = xm
+                num[idx] = (_loss(args_p["q"], args_p["k"], args_p["v"], M, scale, dout) -
+                            _loss(args_m["q"], args_m["k"], args_m["v"], M, scale, dout)) / (2 * eps)
+            assert np.max(np.abs(num - g)) < 1e-7 * max(1.0, np.max(np.abs(g))), (name, Hq, Hkv, S)
+
+
+def test_backward_matches_torch_autograd():
+    """PyTorch's float64 autograd through a dense masked softmax attention
+    written here with torch ops (GQA by repeating the kv heads)."""
+    rng = np.random.default_rng(137)
+    Hq, Hkv, S, D, a, n = 8, 2, 40, 16, 3, 5
+    q, k, v, flags = rand_case(rng, Hq, Hkv, S, D, a, n, 0.15)
+    M = oracle.sep_mask(flags, a, n)
+    dout = rng.standard_normal((Hq, S, D))
+    scale = 1 / math.sqrt(D)
+    dq, dk, dv, delta = oracle.attention_backward(q, k, v, M, scale, dout)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    G = Hq // Hkv
+    kk = tk.repeat_interleave(G, dim=0)
+    vv = tv.repeat_interleave(G, dim=0)
+    x = scale * (tq @ kk.transpose(1, 2))
+    x = x.masked_fill(~torch.tensor(M), float("-inf"))
+    out = torch.softmax(x, dim=-1) @ vv
+    (out * torch.tensor(dout)).sum().backward()
+    assert np.allclose(dq, tq.grad.numpy(), atol=1e-11)
+    assert np.allclose(dk, tk.grad.numpy(), atol=1e-11)
+    assert np.allclose(dv, tv.grad.numpy(), atol=1e-11)
+    assert np.allclose(delta, (out.detach().numpy() * dout).sum(-1), atol=1e-12)
+
+
+def _bwd_no_delta(q, k, v, M, scale, dout):
+    """dS = P * dP, the softmax's row term forgotten"""
+    _, _, P = oracle.attention(q, k, v, M, scale, return_weights=True)
+    G = q.shape[0] // k.shape[0]
+    dq = np.stack([scale * ((P[h] * (dout[h] @ v[h // G].T)) @ k[h // G]) for h in range(q.shape[0])])
+    return dq
+
+
+def _bwd_dq_no_scale(q, k, v, M, scale, dout):
+    dq, _, _, _ = oracle.attention_backward(q, k, v, M, scale, dout)
+    return dq / scale
+
+
+def _bwd_dk_last_head_only(q, k, v, M, scale, dout):
+    """dK from the last query head of each group instead of their sum"""
+    G = q.shape[0] // k.shape[0]
+    _, dk1, _, _ = oracle.attention_backward(q[G - 1::G], k, v, M, scale, dout[G - 1::G])
+    return dk1
+
+
+@pytest.mark.parametrize("mutant,which", [(_bwd_no_delta, 0), (_bwd_dq_no_scale, 0),
+                                          (_bwd_dk_last_head_only, 1)])
+def test_planted_backward_mistakes_fail_the_pin(mutant, which):
+    rng = np.random.default_rng(139)
+    Hq, Hkv, S, D, a, n = 4, 2, 8, 3, 1, 2
+    q, k, v, flags = rand_case(rng, Hq, Hkv, S, D, a, n, 0.3)
+    M = oracle.sep_mask(flags, a, n)
+    dout = rng.standard_normal((Hq, S, D))
+    scale = 0.7
+    x = (q, k)[which]
+    g = mutant(q, k, v, M, scale, dout)
+    eps = 1e-6
+    num = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        xp = x.copy(); xp[idx] += eps
+        xm = x.copy(); xm[idx] -= eps
+        if which == 0:
+            num[idx] = (_loss(xp, k, v, M, scale, dout) - _loss(xm, k, v, M, scale, dout)) / (2 * eps)
+        else:
+            num[idx] = (_loss(q, xp, v, M, scale, dout) - _loss(q, xm, v, M, scale, dout)) / (2 * eps)
+    assert np.max(np.abs(num - g)) > 1e-4
