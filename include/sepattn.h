@@ -132,6 +132,35 @@ int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
                      hipStream_t stream);
 
 /*
+ * sep_attn_prefill_backward - gradients of sep_attn_prefill.
+ * [P2 §1.2 (scaled masked softmax attention); P1 "Training-SepLLM" (training
+ * runs through the same Sep-Attention mask)]
+ *
+ * For L = sum(dout * out): dq = dL/dq, dk = dL/dk, dv = dL/dv, with the
+ * same mask and scale as the forward (see sep_attn_prefill):
+ *   delta_i = sum_d dout_id out_id;  P = softmax weights, recomputed as
+ *   exp(scale q_i.k_j - lse_i) on visible pairs;  dP = dout V^T;
+ *   dS = P * (dP - delta);  dq = scale dS K;  dk_g = scale sum over the
+ *   query heads h of group g of dS_h^T Q_h;  dv_g = sum_h P_h^T dout_h.
+ *   q, out, dout [B, Hq, S, D] and k, v [B, Hkv, S, D] in `dtype`; lse
+ *          [B, Hq, S] float32 as written by sep_attn_prefill (natural log);
+ *   is_sep, rank, sep_pos as for sep_attn_prefill.
+ *   delta  [B, Hq, S] float32 workspace, overwritten.
+ *   dq     [B, Hq, S, D] float32 out; dk, dv [B, Hkv, S, D] float32 out
+ *          (written, not accumulated).
+ * Arithmetic: fp32 throughout (bf16 inputs are widened exactly); dk and dv
+ * of initial and separator keys are summed with fp32 atomics, so their
+ * summation order varies between runs.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, int dtype, int B, int Hq, int Hkv,
+                              int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                              const int32_t* sep_pos, int a, int n, float scale, float* delta,
+                              float* dq, float* dk, float* dv, hipStream_t stream);
+
+/*
  * Cache policies (bits of sep_cache.policy) [P1 "KV Cache Manager": the
  * compression pseudo-code and its SEP_ACCUMULATION / USE_MAX_SEP_CACHE
  * switches].

@@ -23,7 +23,8 @@ import torch
 from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
-__all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_decode",
+__all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
+           "sep_attn_decode",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
            "SEP_POLICY_DYNAMIC", "SEP_POLICY_NO_ACCUM"]
 
@@ -126,6 +127,39 @@ def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: floa
                                 a, n, float(scale), out.data_ptr(), _ptr(lse), _stream())
     _lib.check("sep_attn_prefill", code)
     return (out, lse) if return_lse else out
+
+
+def sep_attn_prefill_backward(q, k, v, out, dout, lse, is_sep, rank, sep_pos, a: int, n: int,
+                              scale: float | None = None, *, dq=None, dk=None, dv=None, delta=None):
+    """Gradients of sep_attn_prefill for L = sum(dout * out): returns float32
+    dq [B,Hq,S,D], dk, dv [B,Hkv,S,D]. `out` and `lse` are the forward's."""
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, None, 4)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise ValueError("q, k, v, out, dout must share a dtype")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k/v must be [B, Hkv, S, D]; out/dout [B, Hq, S, D]")
+    _need(lse, "lse", torch.float32, 3)
+    _need(is_sep, "is_sep", torch.uint8, 2)
+    _need(rank, "rank", torch.int32, 2)
+    _need(sep_pos, "sep_pos", torch.int32, 2)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, Hq, S, D), **f32) if dq is None else dq
+    dk = torch.empty((B, Hkv, S, D), **f32) if dk is None else dk
+    dv = torch.empty((B, Hkv, S, D), **f32) if dv is None else dv
+    delta = torch.empty((B, Hq, S), **f32) if delta is None else delta
+    code = lib.sep_attn_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         dout.data_ptr(), lse.data_ptr(), _dtype_code(q), B, Hq, Hkv, S, D,
+                                         is_sep.data_ptr(), rank.data_ptr(), sep_pos.data_ptr(), a, n,
+                                         float(scale), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                         dv.data_ptr(), _stream())
+    _lib.check("sep_attn_prefill_backward", code)
+    return dq, dk, dv
 
 
 # cache policies (sep_cache.policy in include/sepattn.h)

@@ -47,6 +47,9 @@ SIGNATURES = {
     "sep_index_compact": (c_int, [c_vp, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "sep_attn_prefill": (c_int, [c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_vp,
                                  c_vp, c_vp, c_int, c_int, c_float, c_vp, c_vp, c_vp]),
+    "sep_attn_prefill_backward": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                          c_int, c_int, c_vp, c_vp, c_vp, c_int, c_int, c_float, c_vp,
+                                          c_vp, c_vp, c_vp, c_vp]),
     "sep_cache_reset": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp]),
     "sep_cache_update": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp, c_vp, c_vp, c_int, c_vp,
                                  c_int, c_vp]),

@@ -111,6 +111,27 @@ int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
                                         n, scale, out, lse, stream));
 }
 
+int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, int dtype, int B, int Hq, int Hkv,
+                              int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                              const int32_t* sep_pos, int a, int n, float scale, float* delta,
+                              float* dq, float* dk, float* dv, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr) return SEP_ERR_NULL;
+  if (lse == nullptr || delta == nullptr || dq == nullptr || dk == nullptr || dv == nullptr) return SEP_ERR_NULL;
+  if (is_sep == nullptr || rank == nullptr || sep_pos == nullptr) return SEP_ERR_NULL;
+  if (dtype != SEP_BF16 && dtype != SEP_F32) return SEP_ERR_DTYPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0) return SEP_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq / Hkv > 16) return SEP_ERR_SHAPE;
+  if (D != 64 && D != 128) return SEP_ERR_SHAPE;
+  if (a < 0 || n < 1) return SEP_ERR_PARAM;
+  if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_prefill_backward(q, k, v, out, dout, lse, dtype, B, Hq, Hkv, S, D, is_sep,
+                                                 rank, sep_pos, a, n, scale, delta, dq, dk, dv, stream));
+}
+
 int sep_cache_reset(const sep_cache* cache, hipStream_t stream) {
   const int st = check_cache(cache);
   if (st != SEP_OK) return st;

@@ -31,6 +31,11 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype
                           int Hkv, int S, int D, const uint8_t* is_sep, const int32_t* rank,
                           const int32_t* sep_pos, int a, int n, float scale, void* out, float* lse,
                           hipStream_t st);
+hipError_t launch_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, int dtype, int B, int Hq, int Hkv,
+                                   int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                                   const int32_t* sep_pos, int a, int n, float scale, float* delta, float* dq,
+                                   float* dk, float* dv, hipStream_t st);
 hipError_t launch_cache_reset(const sep_cache& c, hipStream_t st);
 hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void* v_new,
                                const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,

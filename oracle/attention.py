@@ -56,7 +56,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, M: np.ndarray, scale:
 
 
 def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, M: np.ndarray, scale: float,
-                       dout: np.ndarray):
+                       dout: np.ndarray, out: np.ndarray = None):
     """Gradients of the prefill attention of one sequence (the training use of
     Sep-Attention: P1 "Training-SepLLM" trains through the same mask).
 
@@ -69,9 +69,11 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, M: np.ndarra
         dK_g  = scale * sum over the heads h of dS_h^T Q_h
     (the chain rule through the row softmax: d softmax = P * (dP - (P dP)
     summed over the row), and rowsum(P * dP) = rowsum(dout * O)).
-    q/dout [Hq, S, D], k/v [Hkv, S, D], M [S, S] bool; float64.
-    Returns dq [Hq, S, D], dk, dv [Hkv, S, D] and delta = rowsum(dout * O)
-    [Hq, S]."""
+    q/dout [Hq, S, D], k/v [Hkv, S, D], M [S, S] bool; float64. ``out``, when
+    given, is the forward output a caller stored (e.g. rounded to bf16):
+    delta is then rowsum(dout * out), as a backward that is handed that
+    tensor computes it; by default it is the exact O.
+    Returns dq [Hq, S, D], dk, dv [Hkv, S, D] and delta [Hq, S]."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -79,7 +81,8 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, M: np.ndarra
     Hq, S, D = q.shape
     Hkv = k.shape[0]
     G = Hq // Hkv
-    out, _, P = attention(q, k, v, M, scale, return_weights=True)
+    exact, _, P = attention(q, k, v, M, scale, return_weights=True)
+    out = exact if out is None else np.asarray(out, np.float64)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)

@@ -1,0 +1,151 @@
+"""GPU parity of sep_attn_prefill_backward against the fp64 oracle.
+
+The GPU forward (sep_attn_prefill) supplies out and lse, as a training step
+would; the oracle's gradients use the same out for delta = rowsum(dout * out)
+(oracle.attention_backward's ``out``) and the exact softmax weights.
+
+Acceptance, element by element, for g in (dq, dk, dv):
+    |g_gpu - g_ref| <= (eps + gamma) * B_g
+where B_g is the same sum taken over absolute values:
+    aS_ij = P_ij (sum_d |dO_id||V_jd| + sum_d |dO_id||out_id|)
+    B_dq  = scale aS |K|,  B_dk = scale sum_h aS^T |Q|,  B_dv = sum_h P^T |dO|.
+eps bounds the relative error of the recomputed weights P = exp(s - lse)
+that the forward's lse carries: |lse_gpu - lse| <= delta_lse gives
+|P_gpu / P - 1| <= exp(delta_lse) - 1 (delta_lse = 2.5e-3 for bf16, whose
+forward sums bf16-rounded weights, and 1e-5 for fp32; both are the
+forward's own log-sum-exp tolerances), plus a few ulp of the hardware exp2.
+gamma = n u / (1 - n u), u = 2^-24, is the worst-case error of an fp32 sum
+of n terms, with n = D + G S the longest chain of fp32 operations (dot
+products of length D, then sums over at most G S query rows); the kernels'
+inputs are widened exactly and every product is fp32. A wrong index, a
+dropped term or a mask error shifts an element by a multiple of a single
+weight's contribution, far above (eps + gamma) B at these sizes.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from inputs import gen
+from kv_cache_compression_sep_amd import (sep_attn_prefill, sep_attn_prefill_backward, sep_index_compact,
+                                          sep_mask_build)
+
+from .gpu_util import from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"bf16": 2.5e-3, "f32": 1e-5}
+U32 = 2.0 ** -24
+
+
+def run_gpu(ids, q, k, v, dout, sep_ids, a, n, dtype, scale):
+    d_ids = to_dev(ids)
+    flags, _, _ = sep_mask_build(d_ids, to_dev(np.asarray(sep_ids, np.int32)), a, n)
+    rank, sep_pos, _ = sep_index_compact(flags)
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    out, lse = sep_attn_prefill(tq, tk, tv, flags, rank, sep_pos, a, n, scale, return_lse=True)
+    B, Hq, S, _ = q.shape
+    delta = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    gq, gk, gv = sep_attn_prefill_backward(tq, tk, tv, out, to_dev(dout, dtype), lse, flags, rank, sep_pos,
+                                           a, n, scale, delta=delta)
+    torch.cuda.synchronize()
+    return from_dev(out), from_dev(gq), from_dev(gk), from_dev(gv), from_dev(delta)
+
+
+def grad_bounds(q, k, v, out, dout, M, scale):
+    """Absolute-value sums B_dq, B_dk, B_dv and B_delta (see the module
+    docstring) of one sequence, float64."""
+    Hq, S, D = q.shape
+    G = Hq // k.shape[0]
+    _, _, P = oracle.attention(q, k, v, M, scale, return_weights=True)
+    bq, bk, bv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    bdelta = (np.abs(dout) * np.abs(out)).sum(-1)
+    for h in range(Hq):
+        g = h // G
+        aS = P[h] * (np.abs(dout[h]) @ np.abs(v[g]).T + bdelta[h][:, None])
+        bq[h] = scale * (aS @ np.abs(k[g]))
+        bk[g] += scale * (aS.T @ np.abs(q[h]))
+        bv[g] += P[h].T @ np.abs(dout[h])
+    return bq, bk, bv, bdelta
+
+
+def check_bound(got, ref, bound, rel, what):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    err = np.abs(got - ref)
+    lim = rel * bound + 1e-30
+    worst = np.unravel_index(np.argmax(err / lim), err.shape)
+    assert np.all(err <= lim), (f"{what}: err {err[worst]:.3e} > {lim[worst]:.3e} at {worst} "
+                                f"(ref {ref[worst]:.5f}, got {got[worst]:.5f}, max err {err.max():.3e})")
+    print(f"{what}: max err {err.max():.3e}, max err / bound {np.max(err / lim):.3f}", flush=True)
+
+
+def rand_inputs(rng, B, Hq, Hkv, S, D, p_sep, dtype):
+    ids = np.where(rng.random((B, S)) < p_sep, rng.integers(0, 8, (B, S)),
+                   rng.integers(8, 1000, (B, S))).astype(np.int32)
+    q = gen.round_storage(rng.standard_normal((B, Hq, S, D)), dtype)
+    k = gen.round_storage(rng.standard_normal((B, Hkv, S, D)), dtype)
+    v = gen.round_storage(rng.standard_normal((B, Hkv, S, D)), dtype)
+    dout = gen.round_storage(rng.standard_normal((B, Hq, S, D)), dtype)
+    return ids, q, k, v, dout
+
+
+def check_case(ids, q, k, v, dout, sep_ids, a, n, dtype, tag):
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(D)
+    out, gq, gk, gv, delta = run_gpu(ids, q, k, v, dout, sep_ids, a, n, dtype, scale)
+    nterms = D + G * S
+    gamma = nterms * U32 / (1 - nterms * U32)
+    eps = math.expm1(LSE_TOL[dtype]) + 8 * U32
+    for b in range(B):
+        M = oracle.sep_mask(oracle.is_sep(ids[b], sep_ids), a, n)
+        f = [gen.storage_to_f64(x[b], dtype) for x in (q, k, v, dout)]
+        rq, rk, rv, rdelta = oracle.attention_backward(*f[:3], M, scale, f[3], out=out[b])
+        bq, bk, bv, bdelta = grad_bounds(f[0], f[1], f[2], out[b], f[3], M, scale)
+        check_bound(delta[b], rdelta, bdelta, (D + 2) * U32, f"{tag} b={b} delta")
+        check_bound(gq[b], rq, bq, eps + gamma, f"{tag} b={b} dq")
+        check_bound(gk[b], rk, bk, eps + gamma, f"{tag} b={b} dk")
+        check_bound(gv[b], rv, bv, eps + gamma, f"{tag} b={b} dv")
+
+
+CASES = [
+    # B, Hq, Hkv, S,   D,   a,   n,   p_sep
+    (1, 4, 1, 97, 64, 4, 16, 0.1),
+    (2, 8, 2, 300, 128, 4, 64, 0.12),
+    (1, 8, 1, 513, 128, 0, 1, 0.3),       # window 1: a key sees only itself and the globals
+    (1, 2, 2, 257, 64, 9, 300, 0.05),     # window longer than the sequence
+    (1, 16, 2, 200, 128, 4, 32, 0.0),     # no separators, G = 8
+    (1, 16, 1, 130, 64, 2, 8, 1.0),       # every token a separator, G = 16
+    (1, 3, 1, 190, 128, 500, 4, 0.1),     # more initial tokens than tokens, G = 3
+    (1, 4, 4, 1, 128, 4, 256, 0.5),       # a single token
+    (1, 2, 1, 33, 128, 1, 2, 0.2),
+    (1, 32, 8, 1100, 128, 4, 256, 0.12),  # Llama-3 head shape, ragged S, several 256-row chunks
+    (1, 6, 3, 777, 64, 3, 100, 0.08),     # G = 2
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_prefill_backward_small_cases(case, dtype):
+    B, Hq, Hkv, S, D, a, n, p = case
+    print(f"backward case {case} {dtype}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(repr(("bwd", case, dtype)).encode()))
+    ids, q, k, v, dout = rand_inputs(rng, B, Hq, Hkv, S, D, p, dtype)
+    check_case(ids, q, k, v, dout, list(range(8)), a, n, dtype, f"{case} {dtype}")
+
+
+def test_prefill_backward_repeat_is_stable():
+    """Two calls on the same inputs: the band kernels' results are
+    deterministic; only the global keys' atomic sums may differ, within a
+    few ulp of their magnitude."""
+    rng = np.random.default_rng(151)
+    ids, q, k, v, dout = rand_inputs(rng, 1, 8, 2, 600, 128, 0.1, "bf16")
+    r1 = run_gpu(ids, q, k, v, dout, list(range(8)), 4, 64, "bf16", 1 / math.sqrt(128))
+    r2 = run_gpu(ids, q, k, v, dout, list(range(8)), 4, 64, "bf16", 1 / math.sqrt(128))
+    assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+    for x, y in zip(r1[2:4], r2[2:4]):
+        assert np.max(np.abs(x - y)) <= 1e-5 * np.max(np.abs(x))

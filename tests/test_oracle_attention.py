@@ -275,3 +275,17 @@ def test_planted_backward_mistakes_fail_the_pin(mutant, which):
         else:
             num[idx] = (_loss(q, xp, v, M, scale, dout) - _loss(q, xm, v, M, scale, dout)) / (2 * eps)
     assert np.max(np.abs(num - g)) > 1e-4
+
+
+def test_backward_delta_uses_the_given_output():
+    rng = np.random.default_rng(149)
+    q, k, v, flags = rand_case(rng, 2, 1, 12, 4, 1, 3, 0.3)
+    M = oracle.sep_mask(flags, 1, 3)
+    dout = rng.standard_normal((2, 12, 4))
+    exact, _ = oracle.attention(q, k, v, M, 0.5)
+    a = oracle.attention_backward(q, k, v, M, 0.5, dout)
+    b = oracle.attention_backward(q, k, v, M, 0.5, dout, out=exact)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    c = oracle.attention_backward(q, k, v, M, 0.5, dout, out=exact + 0.01)
+    assert np.allclose(c[3], a[3] + 0.01 * dout.sum(-1))
+    assert np.array_equal(c[2], a[2])                     # dv does not involve delta
