@@ -15,7 +15,11 @@ under "secondary":
     decode + update steps (KV GB/s on algorithmic bytes);
   * streaming decode (batch 1, cache 4/64/64/256) over the 4,194,304-token
     stream: tokens/s of in-order decode + update steps, replayed from HIP
-    graphs of 256 steps.
+    graphs of 256 steps;
+  * prefill backward on the prefill workload (sep_attn_prefill_backward,
+    fp32 arithmetic): useful TFLOP/s = 10 * D * visible pairs per query head
+    (S = QK^T recomputed, dP = dO V^T, dQ, dK, dV) over its launch time,
+    against the fp32 peak.
 
 Prints one JSON line. ``--gpus N`` with N > 1 exits: the path runs on one
 GPU only.
@@ -37,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and vector)
 METRIC = "Sep-Attn prefill useful TFLOP/s; decode+cache-update KV GB/s; stream tok/s"
 
 
@@ -153,6 +158,50 @@ def bench_prefill(args, torch, sa, configs, gen):
         f"({tflops_step:.1f} TFLOP/s), prefill kernel {ms_kernel * 1e3:.1f} us ({tflops_kernel:.1f} TFLOP/s)")
     return dict(cfg=cfg, x=x, pairs=pairs, useful=useful, ms_step=ms_step, ms_kernel=ms_kernel,
                 tflops_step=tflops_step, tflops_kernel=tflops_kernel)
+
+
+def bench_backward(args, torch, sa, res):
+    cfg = res["cfg"]
+    B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+    x = res["x"]
+    dev = lambda a, bf=False: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+                               if bf else torch.from_numpy(np.ascontiguousarray(a))).cuda()
+    ids = dev(x["ids"])
+    q, k, v = dev(x["q"], True), dev(x["k"], True), dev(x["v"], True)
+    gen_ = torch.Generator(device="cuda").manual_seed(1006)
+    dout = torch.randn(q.shape, device="cuda", generator=gen_).to(torch.bfloat16)
+    is_sep, _, _ = sa.sep_mask_build(ids, dev(np.asarray(cfg.sep_ids, np.int32)), cfg.a, cfg.n)
+    rank, sep_pos, _ = sa.sep_index_compact(is_sep)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = sa.sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, cfg.a, cfg.n, scale, return_lse=True)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(k.shape, **f32)
+    delta = torch.empty((B, Hq, S), **f32)
+
+    def call():
+        sa.sep_attn_prefill_backward(q, k, v, out, dout, lse, is_sep, rank, sep_pos, cfg.a, cfg.n, scale,
+                                     dq=dq, dk=dk, dv=dv, delta=delta)
+
+    for _ in range(args.warmup):
+        call()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev[i][0].record(st)
+        call()
+        ev[i][1].record(st)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    useful = 2.5 * res["useful"]
+    tflops = useful / (ms * 1e-3) / 1e12
+    log(f"prefill backward: {useful / 1e9:.1f} useful GFLOP, {ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s, "
+        f"{tflops / PEAK_FP32_TFLOPS:.3f} of the fp32 peak)")
+    return {"workload": cfg.name, "entry": "sep_attn_prefill_backward", "arithmetic": "f32",
+            "inputs": "bf16", "us_per_call": round(ms * 1e3, 2), "useful_flop": useful,
+            "tflops": round(tflops, 2), "peak_fp32_tflops": PEAK_FP32_TFLOPS,
+            "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4)}
 
 
 def cpu_baseline_prefill(res, oracle, gen, budget_s=20.0):
@@ -412,7 +461,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--stream-steps", type=int, default=4_194_304)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "stream", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "backward", "decode", "stream", "copy"],
+                    default="all",
                     help="'copy' runs only a plain device copy of known size, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -436,8 +486,13 @@ def main():
         return
     secondary = {}
     res = None
-    if args.only in ("all", "prefill"):
+    if args.only in ("all", "prefill", "backward"):
         res = bench_prefill(args, torch, sa, configs, gen)
+    if args.only in ("all", "backward"):
+        secondary["prefill_backward"] = bench_backward(args, torch, sa, res)
+        if args.only == "backward":
+            print(json.dumps({"secondary": secondary}))
+            return
     if args.only in ("all", "decode"):
         secondary["batched_decode_b64"] = bench_batched(args, torch, sa, configs, gen)
     if args.only in ("all", "stream"):

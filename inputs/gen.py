@@ -22,7 +22,7 @@ from typing import Sequence
 
 import numpy as np
 
-TAG_IDS, TAG_Q, TAG_K, TAG_V, TAG_HK, TAG_HV = 0, 1, 2, 3, 4, 5
+TAG_IDS, TAG_Q, TAG_K, TAG_V, TAG_HK, TAG_HV, TAG_DO = 0, 1, 2, 3, 4, 5, 6   # TAG_DO: upstream gradient dL/dO
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -153,7 +153,8 @@ def normal_rows(seed: int, key: Sequence[int], rows: int, D: int, dtype: str) ->
 
 
 def prefill_head(cfg, b: int, tag: int, h: int) -> np.ndarray:
-    """One head of Q (tag TAG_Q) or K/V (TAG_K/TAG_V): [S, D] in storage format."""
+    """One head of Q (tag TAG_Q), K/V (TAG_K/TAG_V) or the upstream gradient
+    dL/dO (TAG_DO): [S, D] in storage format."""
     return normal_rows(cfg.seed, (b, tag, h), cfg.S, cfg.D, cfg.dtype)
 
 

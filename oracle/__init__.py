@@ -35,6 +35,7 @@ library routines, invariants and a closed form). No function here is
 """
 from .mask import (is_sep, sep_mask, mask_rows, compact, tile_class,  # noqa: F401
                    tile_class_slabs, visible_count)
-from .attention import attention, attention_backward, attention_rows, decode_attention  # noqa: F401
+from .attention import (attention, attention_backward, attention_backward_sampled, attention_rows,  # noqa: F401
+                        decode_attention)
 from .cache import (CacheSim, Entry, closed_form_positions, check_cache_params,  # noqa: F401
                     n_compactions, policy_positions)

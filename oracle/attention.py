@@ -117,6 +117,52 @@ def attention_rows(q_rows, k, v, M_rows, scale, kv_head_of):
     return out, lse
 
 
+def attention_backward_sampled(q, k, v, dout, out, M, scale, rows, keys, row_chunk: int = 512):
+    """Selected elements of attention_backward for one key/value head and the
+    G query heads that read it, at sizes where the [S, S] weights of every
+    head do not fit.
+
+    q, dout, out [G, S, D]; k, v [S, D]; M [S, S] bool; ``out`` is the
+    forward output the backward is handed (delta = rowsum(dout * out), as in
+    attention_backward). Returns dq[:, rows] [G, R, D], dk[keys] and
+    dv[keys] [J, D].
+
+    Same definitions as attention_backward, evaluated on rows and columns:
+    the lse of every query row comes from attention_rows (row chunks of M);
+    P_ij = exp(scale q_i.k_j - lse_i) where M[i, j], else 0; dP_ij =
+    dout_i.v_j; dS_ij = P_ij (dP_ij - delta_i). A query row gives dq_i =
+    scale sum_j dS_ij k_j; a key column gives dv_j = sum_h sum_i P_ij dout_i
+    and dk_j = scale sum_h sum_i dS_ij q_i."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    out = np.asarray(out, np.float64)
+    G, S, D = q.shape
+    rows = np.asarray(list(rows), dtype=np.int64)
+    keys = np.asarray(list(keys), dtype=np.int64)
+    lse = np.empty((G, S))
+    for r0 in range(0, S, row_chunk):
+        r1 = min(S, r0 + row_chunk)
+        _, lse[:, r0:r1] = attention_rows(q[:, r0:r1], k[None], v[None], M[r0:r1], scale, [0] * G)
+    delta = (dout * out).sum(axis=-1)
+    dq = np.empty((G, len(rows), D))
+    dk = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    Mc = M[:, keys]
+    for h in range(G):
+        x = scale * (q[h, rows] @ k.T)
+        x[~M[rows]] = -np.inf
+        Pr = np.exp(x - lse[h, rows][:, None])
+        dq[h] = scale * ((Pr * (dout[h, rows] @ v.T - delta[h, rows][:, None])) @ k)
+        x = scale * (q[h] @ k[keys].T)
+        x[~Mc] = -np.inf
+        Pc = np.exp(x - lse[h][:, None])
+        dv += Pc.T @ dout[h]
+        dk += scale * ((Pc * (dout[h] @ v[keys].T - delta[h][:, None])).T @ q[h])
+    return dq, dk, dv
+
+
 def decode_attention(q: np.ndarray, keys_k: np.ndarray, keys_v: np.ndarray, scale: float):
     """Attention of one decode step over an explicit key list, no further mask.
 

@@ -29,7 +29,7 @@ import pytest
 import torch
 
 import oracle
-from inputs import gen
+from inputs import configs, gen
 from kv_cache_compression_sep_amd import (sep_attn_prefill, sep_attn_prefill_backward, sep_index_compact,
                                           sep_mask_build)
 
@@ -149,3 +149,86 @@ def test_prefill_backward_repeat_is_stable():
     assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
     for x, y in zip(r1[2:4], r2[2:4]):
         assert np.max(np.abs(x - y)) <= 1e-5 * np.max(np.abs(x))
+
+
+def sampled_bounds(q, k, v, dout, out, M, scale, rows, keys):
+    """B_dq at the sampled rows and B_dk, B_dv at the sampled keys of one kv
+    head group (q, dout, out [G, S, D]; k, v [S, D]), with the exact lse."""
+    G, S, D = q.shape
+    lse = np.empty((G, S))
+    for r0 in range(0, S, 512):
+        _, lse[:, r0:r0 + 512] = oracle.attention_rows(q[:, r0:r0 + 512], k[None], v[None], M[r0:r0 + 512],
+                                                       scale, [0] * G)
+    bdelta = (np.abs(dout) * np.abs(out)).sum(-1)
+    bq = np.empty((G, len(rows), D))
+    bk = np.zeros((len(keys), D))
+    bv = np.zeros((len(keys), D))
+    for h in range(G):
+        x = scale * (q[h, rows] @ k.T)
+        x[~M[rows]] = -np.inf
+        Pr = np.exp(x - lse[h, rows][:, None])
+        bq[h] = scale * ((Pr * (np.abs(dout[h, rows]) @ np.abs(v).T + bdelta[h, rows][:, None])) @ np.abs(k))
+        x = scale * (q[h] @ k[keys].T)
+        x[~M[:, keys]] = -np.inf
+        Pc = np.exp(x - lse[h][:, None])
+        bk += scale * ((Pc * (np.abs(dout[h]) @ np.abs(v[keys]).T + bdelta[h][:, None])).T @ np.abs(q[h]))
+        bv += Pc.T @ np.abs(dout[h])
+    return bq, bk, bv
+
+
+@pytest.mark.timeout(900)
+def test_llama3_layer_workload_sampled():
+    """The Llama-3-8B layer workload (1 x 8192 tokens, 32/8 heads, D = 128,
+    bf16) in the benchmark's launch configuration: every head is on the GPU;
+    one kv head's group is host-generated and checked on sampled query rows
+    (first, last and random) and sampled keys (initial, early and late
+    separators, window keys, the last keys)."""
+    cfg = configs.LLAMA3_LAYER_PREFILL
+    B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+    G = Hq // Hkv
+    g = 5
+    heads = list(range(g * G, g * G + G))
+    scale = 1.0 / math.sqrt(D)
+    ids = np.stack([gen.prefill_ids(cfg, 0)])
+    torch.manual_seed(0)
+    bf = dict(device="cuda")
+    q = torch.randn((B, Hq, S, D), **bf).to(torch.bfloat16)
+    dout = torch.randn((B, Hq, S, D), **bf).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S, D), **bf).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S, D), **bf).to(torch.bfloat16)
+    xq = np.stack([gen.prefill_head(cfg, 0, gen.TAG_Q, h) for h in heads])
+    xdo = np.stack([gen.prefill_head(cfg, 0, gen.TAG_DO, h) for h in heads])
+    xk = gen.prefill_head(cfg, 0, gen.TAG_K, g)
+    xv = gen.prefill_head(cfg, 0, gen.TAG_V, g)
+    for i, h in enumerate(heads):
+        q[0, h] = to_dev(xq[i], "bf16")
+        dout[0, h] = to_dev(xdo[i], "bf16")
+    k[0, g] = to_dev(xk, "bf16")
+    v[0, g] = to_dev(xv, "bf16")
+    flags, _, _ = sep_mask_build(to_dev(ids), to_dev(np.asarray(cfg.sep_ids, np.int32)), cfg.a, cfg.n)
+    rank, sep_pos, _ = sep_index_compact(flags)
+    out, lse = sep_attn_prefill(q, k, v, flags, rank, sep_pos, cfg.a, cfg.n, scale, return_lse=True)
+    gq, gk, gv = sep_attn_prefill_backward(q, k, v, out, dout, lse, flags, rank, sep_pos, cfg.a, cfg.n, scale)
+    torch.cuda.synchronize()
+
+    f = oracle.is_sep(ids[0], cfg.sep_ids)
+    seps = np.flatnonzero(f[cfg.a:]) + cfg.a
+    band = np.flatnonzero(~f[cfg.a:]) + cfg.a
+    rng = np.random.default_rng(521)
+    rows = sorted(set(list(range(0, 64)) + list(range(S - 64, S)) + rng.integers(0, S, 128).tolist()))
+    keys = sorted(set(list(range(cfg.a)) + seps[:8].tolist() + rng.choice(seps, 24).tolist() +
+                      band[:8].tolist() + rng.choice(band, 48).tolist() + list(range(S - 8, S))))
+    got_q = from_dev(gq[0, heads][:, rows])
+    got_k = from_dev(gk[0, g, keys])
+    got_v = from_dev(gv[0, g, keys])
+    out_g = from_dev(out[0, heads])
+
+    M = oracle.sep_mask(f, cfg.a, cfg.n)
+    x64 = [gen.storage_to_f64(x, "bf16") for x in (xq, xk, xv, xdo)]
+    rq, rk, rv = oracle.attention_backward_sampled(x64[0], x64[1], x64[2], x64[3], out_g, M, scale, rows, keys)
+    bq, bk, bv = sampled_bounds(x64[0], x64[1], x64[2], x64[3], out_g, M, scale, rows, keys)
+    nterms = D + G * S
+    rel = math.expm1(LSE_TOL["bf16"]) + 8 * U32 + nterms * U32 / (1 - nterms * U32)
+    check_bound(got_q, rq, bq, rel, f"{cfg.name} dq")
+    check_bound(got_k, rk, bk, rel, f"{cfg.name} dk")
+    check_bound(got_v, rv, bv, rel, f"{cfg.name} dv")

@@ -289,3 +289,25 @@ def test_backward_delta_uses_the_given_output():
     c = oracle.attention_backward(q, k, v, M, 0.5, dout, out=exact + 0.01)
     assert np.allclose(c[3], a[3] + 0.01 * dout.sum(-1))
     assert np.array_equal(c[2], a[2])                     # dv does not involve delta
+
+
+@pytest.mark.parametrize("G,S,a,n,p_sep,chunk", [(3, 41, 2, 5, 0.2, 7), (1, 30, 0, 1, 0.0, 512),
+                                                  (4, 25, 30, 3, 0.5, 4)])
+def test_backward_sampled_matches_full_backward(G, S, a, n, p_sep, chunk):
+    """The row/column form agrees with attention_backward (itself pinned by
+    finite differences and autograd) on every sampled row and key, with a
+    stored output that differs from the exact one."""
+    rng = np.random.default_rng(G * 1000 + S)
+    q, k, v, flags = rand_case(rng, G, 1, S, 8, a, n, p_sep)
+    M = oracle.sep_mask(flags, a, n)
+    dout = rng.standard_normal((G, S, 8))
+    exact, _ = oracle.attention(q, k, v, M, 0.3)
+    stored = exact + 1e-3 * rng.standard_normal(exact.shape)
+    rq, rk, rv, _ = oracle.attention_backward(q, k, v, M, 0.3, dout, out=stored)
+    rows = sorted(set([0, S - 1] + rng.integers(0, S, 6).tolist()))
+    keys = sorted(set([0, 1, S - 1] + rng.integers(0, S, 6).tolist() + np.flatnonzero(flags)[:3].tolist()))
+    sq, sk, sv = oracle.attention_backward_sampled(q, k[0], v[0], dout, stored, M, 0.3, rows, keys,
+                                                   row_chunk=chunk)
+    assert np.allclose(sq, rq[:, rows], rtol=1e-12, atol=1e-12)
+    assert np.allclose(sk, rk[0, keys], rtol=1e-12, atol=1e-12)
+    assert np.allclose(sv, rv[0, keys], rtol=1e-12, atol=1e-12)
