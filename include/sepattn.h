@@ -148,12 +148,14 @@ int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
  *   delta  [B, Hq, S] float32 workspace, overwritten.
  *   dq     [B, Hq, S, D] float32 out; dk, dv [B, Hkv, S, D] float32 out
  *          (written, not accumulated).
+ * Shapes as for sep_attn_prefill, and S <= SEP_MAX_BACKWARD_S.
  * Arithmetic: fp32 throughout (bf16 inputs are widened exactly); dk and dv
  * of initial and separator keys are summed with fp32 atomics, so their
  * summation order varies between runs.
  * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
  * SEP_ERR_ALIGN, SEP_ERR_HIP.
  */
+#define SEP_MAX_BACKWARD_S 2097152
 int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const void* out,
                               const void* dout, const float* lse, int dtype, int B, int Hq, int Hkv,
                               int S, int D, const uint8_t* is_sep, const int32_t* rank,

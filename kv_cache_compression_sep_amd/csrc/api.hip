@@ -123,6 +123,7 @@ int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0) return SEP_ERR_SHAPE;
   if (Hq % Hkv != 0 || Hq / Hkv > 16) return SEP_ERR_SHAPE;
   if (D != 64 && D != 128) return SEP_ERR_SHAPE;
+  if (S > SEP_MAX_BACKWARD_S) return SEP_ERR_SHAPE;
   if (a < 0 || n < 1) return SEP_ERR_PARAM;
   if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||

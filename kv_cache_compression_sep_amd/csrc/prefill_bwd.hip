@@ -24,9 +24,9 @@
 //                 per lane, so dV^T += dO^T P and dK^T += Q^T dS take the
 //                 query rows from LDS. Plain stores: every row of dK and dV.
 //   dkdv_glob     the initial and separator keys, which every later query
-//                 sees: one workgroup per (kv head, 256-query chunk) walks the
-//                 gathered key tiles that start before the chunk's end and
-//                 adds its partial dK / dV with fp32 atomics, after dkdv_band.
+//                 sees: a work item is (kv head, 256-query chunk, tile of 128
+//                 gathered keys that start before the chunk's end); it adds
+//                 its partial dK / dV with fp32 atomics, after dkdv_band.
 #include "prefill.hpp"
 #include "internal.hpp"
 
@@ -39,6 +39,8 @@ constexpr int KTQ = 64;                // keys per tile (dq_kernel)
 constexpr int QB = 32;                 // query rows per tile (dk/dv kernels)
 constexpr int KB = BW * 32;            // keys per dk/dv workgroup
 constexpr int QCH = 256;               // query rows per dkdv_glob chunk
+constexpr int kMaxChunks = SEP_MAX_BACKWARD_S / QCH;
+static_assert(SEP_MAX_BACKWARD_S % QCH == 0, "whole chunks");
 
 struct BwdArgs {
   const void* q;
@@ -447,8 +449,14 @@ __global__ void __launch_bounds__(BT, 1) dkdv_band_kernel(BwdArgs P, int n_kt) {
   }
 }
 
+// Work items of dkdv_glob: (query chunk c, tile of KB global keys that start
+// before the chunk's end). A workgroup first counts the tiles of every chunk
+// of its sequence (from rank) into an exclusive prefix in LDS, then takes
+// items w = slot, slot + nslots, ... and finds each item's chunk by binary
+// search, so that the grid stays at the resident size whatever the separator
+// density.
 template <class T, int D>
-__global__ void __launch_bounds__(BT, 1) dkdv_glob_kernel(BwdArgs P, int n_qc) {
+__global__ void __launch_bounds__(BT, 1) dkdv_glob_kernel(BwdArgs P, int n_qc, int nslots) {
   constexpr int KS = D / 2;
   constexpr int DB = D / 32;
   constexpr int STR = D + 1;
@@ -456,33 +464,75 @@ __global__ void __launch_bounds__(BT, 1) dkdv_glob_kernel(BwdArgs P, int n_qc) {
   __shared__ float Ot[QB * STR];
   __shared__ float lse2[QB], dlt[QB];
   __shared__ int32_t kpos[KB];
+  __shared__ int32_t tstart[kMaxChunks + 1];
+  __shared__ int32_t wsum[BW];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int hsel = lane / 32;
-  // heavy chunks (late queries see more global keys) first
-  const int qc = n_qc - 1 - (blockIdx.x % n_qc);
-  const int bgi = blockIdx.x / n_qc;
+  const int BH = P.B * P.Hkv;
+  const int bgi = blockIdx.x % BH;                // a (sequence, kv head) per XCD where BH divides 8
+  const int slot = blockIdx.x / BH;
   const int g = bgi % P.Hkv;
   const int b = bgi / P.Hkv;
   const int S = P.S;
-  const int c0 = qc * QCH;
-  const int c1 = min(c0 + QCH, S);
   const int32_t* rk = P.rank + static_cast<int64_t>(b) * (S + 1);
   const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * S;
   const int ninit = min(P.a, S);
   const int rank_a = rk[ninit];
-  // global keys before the chunk's end: initial [0, min(a, c1)), then the
-  // separators in [a, c1)
-  const int n_in = min(ninit, c1);
-  const int n_gl = n_in + (c1 > ninit ? rk[c1] - rank_a : 0);
+  // global keys before the end c1 of a chunk: initial [0, min(a, c1)), then
+  // the separators in [a, c1)
+  auto n_global = [&](int c1) { return min(ninit, c1) + (c1 > ninit ? rk[c1] - rank_a : 0); };
+
+  // tiles per chunk -> exclusive prefix tstart[0 .. n_qc]
+  const int seg = (n_qc + BT - 1) / BT;
+  const int cb = min(tid * seg, n_qc);
+  const int ce = min(cb + seg, n_qc);
+  int local = 0;
+  for (int c = cb; c < ce; ++c) {
+    const int nt = (n_global(min((c + 1) * QCH, S)) + KB - 1) / KB;
+    tstart[c] = nt;
+    local += nt;
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  for (int c = cb; c < ce; ++c) {
+    const int nt = tstart[c];
+    tstart[c] = run;
+    run += nt;
+  }
+  if (tid == BT - 1) tstart[n_qc] = run;          // the last thread's running sum is the total
+  __syncthreads();
+  const int total = tstart[n_qc];
+
   const T* kb = reinterpret_cast<const T*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   const T* vb = reinterpret_cast<const T*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   float* dkb = P.dk + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   float* dvb = P.dv + static_cast<int64_t>(b * P.Hkv + g) * S * D;
 
-  for (int u0 = 0; u0 < n_gl; u0 += KB) {
-    __syncthreads();                              // kpos of the previous key tile is consumed
+  for (int w = slot; w < total; w += nslots) {
+    // chunk of item w: the last c with tstart[c] <= w (it has tiles: w < tstart[c + 1])
+    int lo = 0, hi = n_qc - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (tstart[mid] <= w) lo = mid;
+      else hi = mid - 1;
+    }
+    const int qc = lo;
+    const int u0 = (w - tstart[qc]) * KB;
+    const int c0 = qc * QCH;
+    const int c1 = min(c0 + QCH, S);
+    const int n_in = min(ninit, c1);
+    const int n_gl = n_global(c1);
+    __syncthreads();                              // kpos of the previous item is consumed
     for (int u = tid; u < KB; u += BT) {
       const int uu = u0 + u;
       kpos[u] = uu >= n_gl ? -1 : (uu < n_in ? uu : sp[rank_a + (uu - n_in)]);
@@ -499,7 +549,7 @@ __global__ void __launch_bounds__(BT, 1) dkdv_glob_kernel(BwdArgs P, int n_qc) {
       dv[db] = f32x16{};
     }
     const int jlo = kpos[0];                      // the tile's first (smallest) key
-    int wlo = kpos[32 * wave];                    // this wave's first key (-1: none)
+    const int wlo = kpos[32 * wave];              // this wave's first key (-1: none)
     const int qs = max(c0, jlo) / QB * QB;        // first query tile that can see a key
     for (int hh = 0; hh < P.G; ++hh) {
       const int64_t hrow = static_cast<int64_t>(b * P.Hq + g * P.G + hh) * S;
@@ -534,8 +584,11 @@ hipError_t launch_bwd(BwdArgs A, hipStream_t st) {
   hipLaunchKernelGGL((dq_kernel<T, D>), dim3(A.B * A.Hkv * A.n_hg * A.n_qt), dim3(BT), 0, st, A);
   const int n_kt = (A.S + KB - 1) / KB;
   hipLaunchKernelGGL((dkdv_band_kernel<T, D>), dim3(A.B * A.Hkv * n_kt), dim3(BT), 0, st, A, n_kt);
+  // twice the resident workgroups (one per CU: register bound) on 256 CUs
   const int n_qc = (A.S + QCH - 1) / QCH;
-  hipLaunchKernelGGL((dkdv_glob_kernel<T, D>), dim3(A.B * A.Hkv * n_qc), dim3(BT), 0, st, A, n_qc);
+  const int BH = A.B * A.Hkv;
+  const int nslots = BH >= 512 ? 1 : 512 / BH;
+  hipLaunchKernelGGL((dkdv_glob_kernel<T, D>), dim3(BH * nslots), dim3(BT), 0, st, A, n_qc, nslots);
   return hipGetLastError();
 }
 
