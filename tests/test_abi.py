@@ -107,6 +107,30 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, out=FAKE + 2) == E.SEP_ERR_ALIGN
 
 
+def _backward(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, dout=FAKE, lse=FAKE, dtype=1, B=1, Hq=32, Hkv=8, S=64,
+                D=128, is_sep=FAKE, rank=FAKE, sep_pos=FAKE, a=4, n=16, scale=0.088, delta=FAKE, dq=FAKE,
+                dk=FAKE, dv=FAKE, st=None)
+    args.update(kw)
+    return lib.sep_attn_prefill_backward(*args.values())
+
+
+def test_prefill_backward_argument_checks(lib):
+    E = _lib
+    for name in ("q", "dout", "lse", "delta", "dq", "dk", "dv", "sep_pos"):
+        assert _backward(lib, **{name: None}) == E.SEP_ERR_NULL, name
+    assert _backward(lib, dtype=7) == E.SEP_ERR_DTYPE
+    assert _backward(lib, Hq=30) == E.SEP_ERR_SHAPE
+    assert _backward(lib, D=96) == E.SEP_ERR_SHAPE
+    assert _backward(lib, S=0) == E.SEP_ERR_SHAPE
+    assert _backward(lib, S=2097152 + 1) == E.SEP_ERR_SHAPE     # past SEP_MAX_BACKWARD_S
+    assert _backward(lib, n=0) == E.SEP_ERR_PARAM
+    assert _backward(lib, a=-1) == E.SEP_ERR_PARAM
+    assert _backward(lib, scale=float("inf")) == E.SEP_ERR_PARAM
+    for name in ("out", "dout", "dq", "dk", "dv"):
+        assert _backward(lib, **{name: FAKE + 4}) == E.SEP_ERR_ALIGN, name
+
+
 def _cache(**kw):
     d = dict(a=4, s=64, p=64, w=256, B=1, Hkv=8, D=128, dtype=1, k=FAKE, v=FAKE, pos=FAKE,
              tok=FAKE, state=FAKE, policy=0)
