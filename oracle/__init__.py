@@ -27,6 +27,9 @@ Modules:
                 an explicit key list (decode).
   cache.py      list-based simulation of the four-block cache, and the
                 closed form of its state.
+  rope.py       rotary position embedding and the position shifting of
+                streaming decode (keys re-indexed by their place in the
+                cache).
 
 Every function is pinned by tests under ``tests/`` marked "not gpu"
 (brute force on tiny inputs, special cases that reduce to textbook or
@@ -37,5 +40,6 @@ from .mask import (is_sep, sep_mask, mask_rows, compact, tile_class,  # noqa: F4
                    tile_class_slabs, visible_count)
 from .attention import (attention, attention_backward, attention_backward_sampled, attention_rows,  # noqa: F401
                         decode_attention)
+from .rope import decode_attention_shifted, rope_angles, rotate, round_bf16  # noqa: F401
 from .cache import (CacheSim, Entry, closed_form_positions, check_cache_params,  # noqa: F401
                     n_compactions, policy_positions)
