@@ -281,6 +281,46 @@ int sep_cache_update(const sep_cache* cache, const void* k_new, const void* v_ne
 int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
                     int Hq, float scale, void* out, float* lse, hipStream_t stream);
 
+/*
+ * sep_rope_table - cos/sin table of rotary position embedding.
+ * [P1 "Streaming-SepLLM": streaming needs positional-encoding shifting (the
+ * Llama pos_shift module); RoPE as published: Su et al., RoFormer, §3.4]
+ *
+ *   table  [n_pos, D/2, 2] float32 out: table[p][i] = (cos(p theta_i),
+ *          sin(p theta_i)), theta_i = base^(-2 i / D), evaluated in fp64 and
+ *          rounded once to fp32. 16-byte aligned.
+ *   base   > 1 (500000 for Llama 3); D in {64, 128}; n_pos >= 1.
+ * Build it once per (base, D) and cache size; sep_attn_decode_rope reads it.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_ALIGN,
+ * SEP_ERR_HIP.
+ */
+int sep_rope_table(double base, int D, int n_pos, float* table, hipStream_t stream);
+
+/*
+ * sep_attn_decode_rope - sep_attn_decode with rotary position embedding and
+ * position shifting.
+ * [P1 "Streaming-SepLLM" and "Streaming 不是普通评测入口" (streaming needs
+ * positional-encoding shifting); RoFormer §3.4 for the rotation]
+ *
+ * The cache holds keys before rotation (as k_new is passed: unrotated), so
+ * positions are assigned at read time: the retained entries take positions
+ * 0 .. L-1 in cache order (initial block, then the separator ring oldest
+ * first, then the recent ring oldest first) and the current token, query
+ * and key, takes position L. Pair i of a head vector is (x_i, x_{i+D/2})
+ * (Llama's arrangement), rotated by p theta_i. The rotated query and keys
+ * are rounded to bf16 (round to nearest even) before the products; values
+ * are not rotated.
+ *   q, k_new, v_new, cache, Hq, scale, out, lse as for sep_attn_decode.
+ *   rope   sep_rope_table output for D = cache->D with rope_npos rows;
+ *          rope_npos >= (cache slots) + 1 = a + s + ring + 1, where ring is
+ *          p + w, or s + p + w under SEP_POLICY_DYNAMIC. 16-byte aligned.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_attn_decode_rope(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
+                         int Hq, float scale, const float* rope, int rope_npos, void* out, float* lse,
+                         hipStream_t stream);
+
 /* Static description of a status code. */
 const char* sep_status_string(int status);
 

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
 __all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
-           "sep_attn_decode",
+           "sep_attn_decode", "sep_attn_decode_rope", "sep_rope_table",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
            "SEP_POLICY_DYNAMIC", "SEP_POLICY_NO_ACCUM"]
 
@@ -237,6 +237,46 @@ def sep_cache_update(cache: SepCache, k_new, v_new, ids_new, sep_ids):
                                 _ptr(sep_ids) if sep_ids.numel() else None, sep_ids.numel(),
                                 _stream())
     _lib.check("sep_cache_update", code)
+
+
+def sep_rope_table(base: float, D: int, n_pos: int, *, out=None, device="cuda"):
+    """(cos, sin) of p * base^(-2i/D) for p < n_pos, i < D/2: float32 [n_pos, D/2, 2]."""
+    lib = _lib.load()
+    out = torch.empty((n_pos, D // 2, 2), dtype=torch.float32, device=device) if out is None else out
+    _need(out, "out", torch.float32, 3)
+    if out.shape != (n_pos, D // 2, 2):
+        raise ValueError("out must be [n_pos, D/2, 2]")
+    code = lib.sep_rope_table(float(base), D, n_pos, out.data_ptr(), _stream())
+    _lib.check("sep_rope_table", code)
+    return out
+
+
+def sep_attn_decode_rope(q, k_new, v_new, cache: SepCache, rope, scale: float | None = None, *, out=None,
+                         return_lse: bool = False, lse=None):
+    """sep_attn_decode with rotary embedding at shifted positions (cached keys
+    and k_new unrotated; `rope` from sep_rope_table with at least
+    cache.slots + 1 rows)."""
+    lib = _lib.load()
+    _need(q, "q", cache.dtype, 3)
+    _need(k_new, "k_new", cache.dtype, 3)
+    _need(v_new, "v_new", cache.dtype, 3)
+    _need(rope, "rope", torch.float32, 3)
+    B, Hq, D = q.shape
+    if (B, D) != (cache.B, cache.D) or k_new.shape != (B, cache.Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("shapes do not match the cache")
+    if rope.shape[1:] != (D // 2, 2):
+        raise ValueError("rope must be [n_pos, D/2, 2]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = cache.struct()
+    code = lib.sep_attn_decode_rope(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ctypes.byref(st), Hq,
+                                    float(scale), rope.data_ptr(), rope.shape[0], out.data_ptr(), _ptr(lse),
+                                    _stream())
+    _lib.check("sep_attn_decode_rope", code)
+    return (out, lse) if return_lse else out
 
 
 def sep_attn_decode(q, k_new, v_new, cache: SepCache, scale: float | None = None, *, out=None,

@@ -53,6 +53,9 @@ SIGNATURES = {
     "sep_cache_reset": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp]),
     "sep_cache_update": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp, c_vp, c_vp, c_int, c_vp,
                                  c_int, c_vp]),
+    "sep_rope_table": (c_int, [ctypes.c_double, c_int, c_int, c_vp, c_vp]),
+    "sep_attn_decode_rope": (c_int, [c_vp, c_vp, c_vp, ctypes.POINTER(SepCacheStruct), c_int, c_float, c_vp,
+                                     c_int, c_vp, c_vp, c_vp]),
     "sep_attn_decode": (c_int, [c_vp, c_vp, c_vp, ctypes.POINTER(SepCacheStruct), c_int, c_float,
                                 c_vp, c_vp, c_vp]),
     "sep_status_string": (ctypes.c_char_p, [c_int]),

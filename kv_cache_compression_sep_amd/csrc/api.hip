@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;   // 1.1: cache policies, 8-word state
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;   // 1.2: prefill backward, RoPE decode
 constexpr int kMaxSepCache = 8192;   // separator-ring cap (plan list lives in LDS)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -167,7 +167,34 @@ int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const s
   if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return SEP_ERR_ALIGN;
-  return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, out, lse, stream));
+  return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, nullptr, out, lse, stream));
+}
+
+int sep_rope_table(double base, int D, int n_pos, float* table, hipStream_t stream) {
+  if (table == nullptr) return SEP_ERR_NULL;
+  if (D != 64 && D != 128) return SEP_ERR_SHAPE;
+  if (n_pos < 1) return SEP_ERR_SHAPE;
+  if (!(base > 1.0) || !(base < 1e300)) return SEP_ERR_PARAM;
+  if (!aligned16(table)) return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_rope_table(base, D, n_pos, table, stream));
+}
+
+int sep_attn_decode_rope(const void* q, const void* k_new, const void* v_new, const sep_cache* cache,
+                         int Hq, float scale, const float* rope, int rope_npos, void* out, float* lse,
+                         hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != SEP_OK) return st;
+  st = check_cache_kv(cache);
+  if (st != SEP_OK) return st;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || out == nullptr || rope == nullptr)
+    return SEP_ERR_NULL;
+  if (cache->dtype != SEP_BF16) return SEP_ERR_DTYPE;
+  if (Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return SEP_ERR_SHAPE;
+  if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
+  if (rope_npos < sep::cache_slots(*cache) + 1) return SEP_ERR_PARAM;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) || !aligned16(rope))
+    return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, rope, out, lse, stream));
 }
 
 }  // extern "C"

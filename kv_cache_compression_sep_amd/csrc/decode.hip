@@ -20,6 +20,15 @@
 // then O^T += V^T P^T with V staged transposed in the wave's LDS slice. The
 // next slice's K and V rows are loaded while the current one is computed.
 // Waves merge through LDS at the end.
+//
+// With ROPE (sep_attn_decode_rope; P1 "Streaming-SepLLM": streaming needs
+// positional-encoding shifting; RoFormer §3.4 for the rotation), virtual
+// key u is exactly its shifted position: the cache holds unrotated keys and
+// key u is rotated by u theta_i when its slice is consumed, the query by
+// occ theta_i once; pair i is (x_i, x_{i+D/2}), which a lane holds in k-steps
+// ks and ks + NKS/2 of the same fragment, so the rotation is lane-local. The
+// cos/sin rows of the slice's keys are loaded with its K/V rows (they come
+// from L2: one table serves every sequence and head).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -36,11 +45,29 @@ struct DecodeArgs {
   const int64_t* state;
   uint16_t* out;
   float* lse;
+  const float* rope;                             // [n_pos][D/2] (cos, sin), ROPE only
   int a, s, p, w, rw, c, Hq, Hkv, G;
   float scale_log2;
 };
 
-template <int D, int NW>
+__device__ __forceinline__ float bf16lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Rotate the pairs (lo[e], hi[e]) of two bf16x8 fragments by the angles
+// whose (cos, sin) are cs[e] (as four f32x4 of two pairs each); results are
+// rounded to bf16.
+__device__ __forceinline__ void rotate_pairs(u32x4& lo, u32x4& hi, const f32x4 (&cs)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {                  // bf16 elements 2m, 2m + 1
+    const float x0 = bf16lo_f(lo[m]), x1 = bf16hi_f(lo[m]);
+    const float y0 = bf16lo_f(hi[m]), y1 = bf16hi_f(hi[m]);
+    const float c0 = cs[m][0], s0 = cs[m][1], c1 = cs[m][2], s1 = cs[m][3];
+    lo[m] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+    hi[m] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+  }
+}
+
+template <int D, int NW, bool ROPE>
 __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
   constexpr int NT = NW * kWave;
   constexpr int VSTR = kSlice + 8;               // V^T row stride (bf16)
@@ -120,6 +147,20 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
       if (hq >= G) v = u32x4{0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
+    if constexpr (ROPE) {                        // the query at position occ
+      const float* trow = A.rope + static_cast<int64_t>(occ) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks) {
+        f32x4 cs[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          cs[m] = *reinterpret_cast<const f32x4*>(trow + 2 * (32 * ks + 8 * (lane / 16) + 2 * m));
+        u32x4 lo = __builtin_bit_cast(u32x4, qf[ks]), hi = __builtin_bit_cast(u32x4, qf[ks + NKS / 2]);
+        rotate_pairs(lo, hi, cs);
+        qf[ks] = __builtin_bit_cast(bf16x8, lo);
+        qf[ks + NKS / 2] = __builtin_bit_cast(bf16x8, hi);
+      }
+    }
   }
 
   f32x4 oacc[NDB];
@@ -132,6 +173,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
   struct Regs {
     u32x4 k[2][NKS];
     u32x4 v[NPAIR][4];
+    f32x4 cs[ROPE ? 2 : 1][ROPE ? NKS / 2 : 1][4];   // (cos, sin) of the K pairs
   };
   auto load_slice = [&](int u0, Regs& R) {
 #pragma unroll
@@ -141,6 +183,14 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         R.k[gq][ks] = *reinterpret_cast<const u32x4*>(kr + 32 * ks + 8 * hh);
+      if constexpr (ROPE) {                      // key u sits at position u
+        const float* trow = A.rope + static_cast<int64_t>(u) * D;
+#pragma unroll
+        for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            R.cs[gq][ks][m] = *reinterpret_cast<const f32x4*>(trow + 2 * (32 * ks + 8 * hh + 2 * m));
+      }
     }
 #pragma unroll
     for (int j = 0; j < NPAIR; ++j) {
@@ -179,6 +229,12 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
         *reinterpret_cast<u32x2*>(vt + d * VSTR + col) = u32x2{w01e, w23e};
         *reinterpret_cast<u32x2*>(vt + (d + 1) * VSTR + col) = u32x2{w01o, w23o};
       }
+    }
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+        for (int ks = 0; ks < NKS / 2; ++ks) rotate_pairs(cur.k[gq][ks], cur.k[gq][ks + NKS / 2], cur.cs[gq][ks]);
     }
     // ---- scores S^T: lane l holds head l%16, keys 16*gq + 4*(l/16) + r
     f32x4 s[2];
@@ -271,11 +327,14 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
 
 template <int D, int NW>
 static void launch_one(const DecodeArgs& A, int Hkv, int B, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<D, NW>), dim3(Hkv, B), dim3(NW * kWave), 0, st, A);
+  if (A.rope != nullptr)
+    hipLaunchKernelGGL((decode_kernel<D, NW, true>), dim3(Hkv, B), dim3(NW * kWave), 0, st, A);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, NW, false>), dim3(Hkv, B), dim3(NW * kWave), 0, st, A);
 }
 
 hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
-                         int Hq, float scale, void* out, float* lse, hipStream_t st) {
+                         int Hq, float scale, const float* rope, void* out, float* lse, hipStream_t st) {
   DecodeArgs A;
   A.q = static_cast<const uint16_t*>(q);
   A.k_new = static_cast<const uint16_t*>(k_new);
@@ -285,6 +344,7 @@ hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, co
   A.state = c.state;
   A.out = static_cast<uint16_t*>(out);
   A.lse = lse;
+  A.rope = rope;
   A.a = c.a;
   A.s = c.s;  // the separator-ring branch is only reached when cnt > 0, i.e. s >= 1
   A.p = c.p;
@@ -305,6 +365,26 @@ hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, co
     if (wide) launch_one<64, 8>(A, c.Hkv, c.B, st);
     else launch_one<64, 4>(A, c.Hkv, c.B, st);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RoPE table
+__global__ void rope_table_kernel(double base, int D, int n_pos, float* table) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int h = D / 2;
+  if (e >= static_cast<int64_t>(n_pos) * h) return;
+  const int p = static_cast<int>(e / h);
+  const int i = static_cast<int>(e % h);
+  const double ang = static_cast<double>(p) * pow(base, -2.0 * i / D);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  *reinterpret_cast<f32x2*>(table + 2 * e) = f32x2{static_cast<float>(cs), static_cast<float>(sn)};
+}
+
+hipError_t launch_rope_table(double base, int D, int n_pos, float* table, hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(n_pos) * (D / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, base, D,
+                     n_pos, table);
   return hipGetLastError();
 }
 

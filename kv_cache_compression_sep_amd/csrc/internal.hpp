@@ -41,6 +41,7 @@ hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void
                                const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,
                                hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
-                         int Hq, float scale, void* out, float* lse, hipStream_t st);
+                         int Hq, float scale, const float* rope, void* out, float* lse, hipStream_t st);
+hipError_t launch_rope_table(double base, int D, int n_pos, float* table, hipStream_t st);
 
 }  // namespace sep

@@ -186,3 +186,23 @@ def test_decode_argument_checks(lib):
     assert dec(_cache(dtype=0)) == E.SEP_ERR_DTYPE
     assert dec(_cache(s=0)) == E.SEP_ERR_PARAM           # s = 0 needs p = 0
     assert dec(c, q=FAKE + 2) == E.SEP_ERR_ALIGN
+
+
+def test_rope_argument_checks(lib):
+    E = _lib
+    tab = lambda **kw: lib.sep_rope_table(kw.get("base", 500000.0), kw.get("D", 128), kw.get("n", 10),
+                                          kw.get("t", FAKE), None)
+    assert tab(t=None) == E.SEP_ERR_NULL
+    assert tab(D=96) == E.SEP_ERR_SHAPE
+    assert tab(n=0) == E.SEP_ERR_SHAPE
+    assert tab(base=1.0) == E.SEP_ERR_PARAM
+    assert tab(base=float("nan")) == E.SEP_ERR_PARAM
+    assert tab(t=FAKE + 8) == E.SEP_ERR_ALIGN
+    c = _cache()                                         # 4 + 64 + (64 + 256) slots
+    dec = lambda cc, **kw: lib.sep_attn_decode_rope(
+        FAKE, FAKE, FAKE, ctypes.byref(cc), 32, 0.1, kw.get("rope", FAKE), kw.get("npos", 389), FAKE, None, None)
+    assert dec(c, rope=None) == E.SEP_ERR_NULL
+    assert dec(c, npos=388) == E.SEP_ERR_PARAM           # fewer rows than slots + 1
+    assert dec(_cache(policy=1), npos=389) == E.SEP_ERR_PARAM   # dynamic ring: s + p + w slots
+    assert dec(c, rope=FAKE + 4) == E.SEP_ERR_ALIGN
+    assert dec(_cache(dtype=0)) == E.SEP_ERR_DTYPE

@@ -1,0 +1,121 @@
+"""GPU parity of sep_rope_table and sep_attn_decode_rope against the oracle.
+
+The table must equal fp64 cos/sin rounded to fp32 within one fp32 ulp. A
+decode step with position shifting must match oracle.decode_attention_shifted
+over the retained keys in cache order (CacheSim.keys(): initial, separators,
+recent window, each oldest first) plus the current token, within the bf16
+tolerance. Both sides round the rotated query and keys to bf16; they may
+differ where the fp32 rotation of the kernel and the fp64 rotation of the
+oracle fall on opposite sides of a bf16 rounding boundary, which moves one
+operand element by one bf16 ulp and the output far less than the tolerance.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache, SepError,
+                                          sep_attn_decode_rope, sep_rope_table)
+
+from .gpu_util import check_close, from_dev, to_dev
+from .test_gpu_cache_decode import SEP_IDS, Stream, sim_for
+from inputs import gen
+
+pytestmark = pytest.mark.gpu
+LLAMA3_ROPE_BASE = 500000.0
+
+
+@pytest.mark.parametrize("D,n_pos,base", [(128, 1000, LLAMA3_ROPE_BASE), (64, 3000, 10000.0), (128, 1, 10.0)])
+def test_rope_table(D, n_pos, base):
+    t = from_dev(sep_rope_table(base, D, n_pos))
+    ang = oracle.rope_angles(np.arange(n_pos), D, base)
+    ref = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32).astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(t - ref) <= ulp), np.max(np.abs(t - ref) / ulp)
+    assert np.mean(t == ref) > 0.999
+
+
+ROPE_CASES = [
+    # B, Hq, Hkv, D,  a, s,  p,  w,  T, policy
+    (2, 32, 8, 128, 4, 64, 64, 256, 700, 0),
+    (1, 8, 8, 64, 2, 5, 3, 11, 90, 0),
+    (3, 16, 1, 128, 0, 7, 9, 33, 300, 0),
+    (1, 12, 3, 64, 4, 20, 2, 40, 5, 0),       # cache still filling the initial block
+    (2, 4, 2, 128, 4, 0, 0, 50, 200, 0),      # StreamingLLM mode
+    (2, 32, 8, 128, 4, 64, 16, 96, 700, SEP_POLICY_DYNAMIC),
+    (1, 8, 2, 64, 2, 9, 5, 20, 300, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM),
+    (1, 16, 4, 128, 4, 256, 28, 512, 1500, 0),  # the batched workload's cache sizes
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=[str(c) for c in ROPE_CASES])
+def test_decode_rope_matches_oracle(case):
+    B, Hq, Hkv, D, a, s, p, w, T, policy = case
+    print(f"rope decode case {case}", flush=True)
+    st = Stream(zlib.crc32(repr(("rope", case)).encode()), B, Hq, Hkv, D, T + 24, 0.2)
+    d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
+    cache = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
+    table = sep_rope_table(LLAMA3_ROPE_BASE, D, cache.slots + 1)
+    sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
+    st.push_gpu(cache, 0, T, d_sep)
+    for b in range(B):
+        sims[b].push_many([oracle.Entry(t, int(st.ids[b, t])) for t in range(T)])
+    scale = 1.0 / math.sqrt(D)
+    for t in range(T, T + 24):
+        q = to_dev(np.ascontiguousarray(st.q[:, t]), "bf16")
+        kn = to_dev(np.ascontiguousarray(st.k[:, :, t]), "bf16")
+        vn = to_dev(np.ascontiguousarray(st.v[:, :, t]), "bf16")
+        out, lse = sep_attn_decode_rope(q, kn, vn, cache, table, scale, return_lse=True)
+        o = from_dev(out)
+        l_gpu = from_dev(lse)
+        for b in range(B):
+            keys = [e.pos for e in sims[b].keys()] + [t]
+            kk = gen.bf16_bits_to_f64(st.k[b][:, keys])
+            vv = gen.bf16_bits_to_f64(st.v[b][:, keys])
+            o_ref, l_ref = oracle.decode_attention_shifted(gen.bf16_bits_to_f64(st.q[b, t]), kk, vv, scale,
+                                                           LLAMA3_ROPE_BASE)
+            check_close(o[b], o_ref, "bf16", f"{case} step {t} b {b}")
+            assert np.max(np.abs(l_gpu[b] - l_ref)) < 1e-3
+        st.push_gpu(cache, t, t + 1, d_sep)
+        for b in range(B):
+            sims[b].push(oracle.Entry(t, int(st.ids[b, t])))
+
+
+def test_decode_rope_differs_from_unshifted_positions():
+    """The shift matters: the same step with the keys at their stream
+    positions (no shifting) gives a different output, which the GPU result
+    does not match."""
+    B, Hq, Hkv, D, a, s, p, w, T = 1, 8, 2, 128, 4, 16, 8, 32, 400
+    st = Stream(977, B, Hq, Hkv, D, T + 1, 0.2)
+    d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
+    cache = SepCache(B, Hkv, D, a, s, p, w)
+    table = sep_rope_table(LLAMA3_ROPE_BASE, D, cache.slots + 1)
+    sim = sim_for((a, s, p, w), 0)
+    st.push_gpu(cache, 0, T, d_sep)
+    sim.push_many([oracle.Entry(t, int(st.ids[0, t])) for t in range(T)])
+    out = sep_attn_decode_rope(to_dev(np.ascontiguousarray(st.q[:, T]), "bf16"),
+                               to_dev(np.ascontiguousarray(st.k[:, :, T]), "bf16"),
+                               to_dev(np.ascontiguousarray(st.v[:, :, T]), "bf16"), cache, table)
+    o = from_dev(out)[0]
+    keys = [e.pos for e in sim.keys()] + [T]
+    kk = gen.bf16_bits_to_f64(st.k[0][:, keys])
+    vv = gen.bf16_bits_to_f64(st.v[0][:, keys])
+    qq = gen.bf16_bits_to_f64(st.q[0, T])
+    qr = oracle.round_bf16(oracle.rotate(qq[:, None], [T], LLAMA3_ROPE_BASE)[:, 0])
+    kr = oracle.round_bf16(oracle.rotate(kk, keys, LLAMA3_ROPE_BASE))
+    unshifted, _ = oracle.decode_attention(qr, kr, vv, 1 / math.sqrt(D))
+    shifted, _ = oracle.decode_attention_shifted(qq, kk, vv, 1 / math.sqrt(D), LLAMA3_ROPE_BASE)
+    check_close(o, shifted, "bf16", "shifted")
+    assert np.max(np.abs(o - unshifted)) > 0.05
+
+
+def test_decode_rope_rejects_a_short_table():
+    cache = SepCache(1, 2, 128, 4, 16, 8, 32)
+    table = sep_rope_table(LLAMA3_ROPE_BASE, 128, cache.slots)      # one row short
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(SepError):
+        sep_attn_decode_rope(q, kv, kv, cache, table)
