@@ -12,10 +12,13 @@ The same run also measures the streaming rows of the path and reports them
 under "secondary":
   * batched decode (64 sequences with 32,768-token histories, cache
     4/256/28/512): bulk history ingest (sep_cache_update, GB/s) and 1024
-    decode + update steps (KV GB/s on algorithmic bytes);
+    decode + update steps (KV GB/s on algorithmic bytes); then the decode
+    with RoPE position shifting (sep_attn_decode_rope) against the plain one
+    on the final cache, and each cache policy;
   * streaming decode (batch 1, cache 4/64/64/256) over the 4,194,304-token
     stream: tokens/s of in-order decode + update steps, replayed from HIP
-    graphs of 256 steps;
+    graphs of 256 steps; then its first 65,536 steps with RoPE position
+    shifting;
   * prefill backward on the prefill workload (sep_attn_prefill_backward,
     fp32 arithmetic): useful TFLOP/s = 10 * D * visible pairs per query head
     (S = QK^T recomputed, dP = dO V^T, dQ, dK, dV) over its launch time,
@@ -303,6 +306,27 @@ def bench_batched(args, torch, sa, configs, gen):
     ms_steps = e0.elapsed_time(e1)
     ms_dec = float(sum(a.elapsed_time(b) for a, b in dec_ev))
     assert int(cache.state[0, 0]) == H + cfg.steps
+    # RoPE with position shifting (sep_attn_decode_rope) against the plain
+    # decode, 32 steps each on the same final cache
+    table = sa.sep_rope_table(500000.0, D, cache.slots + 1)
+    occ_f = _occupancy(cache)
+    dec_f = int(((occ_f + 1) * 2 * row).sum()) + 2 * B * Hq * D * 2
+    rope = {}
+    for name, fn in (("plain", lambda j: sa.sep_attn_decode(pq[j], pk[j], pv[j], cache, scale, out=out)),
+                     ("rope", lambda j: sa.sep_attn_decode_rope(pq[j], pk[j], pv[j], cache, table, scale,
+                                                                out=out))):
+        fn(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for j in range(32):
+            fn(j)
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 32
+        rope[name] = dict(decode_us=us, decode_GBps=dec_f / (us * 1e-6) / 1e9)
+    log(f"decode with RoPE shifting: {rope['rope']['decode_us']:.1f} us ({rope['rope']['decode_GBps']:.0f} GB/s) "
+        f"vs plain {rope['plain']['decode_us']:.1f} us ({rope['plain']['decode_GBps']:.0f} GB/s)")
     # the same history and 32 decode steps under the other cache policies
     # (the manager's trigger, accumulation off): ingest and decode rates on
     # their algorithmic bytes, and the mean occupancy they leave
@@ -339,6 +363,7 @@ def bench_batched(args, torch, sa, configs, gen):
         del pc
     res = dict(
         policies=policy,
+        rope_shifted_decode=rope,
         ingest_ms=ms_ingest, ingest_GBps=ingest_bytes / (ms_ingest * 1e-3) / 1e9,
         steps=cfg.steps, step_us=ms_steps * 1e3 / cfg.steps,
         kv_GBps=total_bytes / (ms_steps * 1e-3) / 1e9,
@@ -452,6 +477,43 @@ def bench_stream(args, torch, sa, configs, gen):
                us_per_step=ms * 1e3 / steps, final_state_matches_closed_form=bool(ok))
     log(f"stream: {steps} steps in {ms * 1e-3:.2f} s -> {res['tok_per_s']:.0f} tok/s "
         f"({res['us_per_step']:.2f} us/step), closed form {'ok' if ok else 'MISMATCH'}")
+    del graphs
+    # the first 65,536 steps again with RoPE position shifting
+    # (sep_attn_decode_rope), from graphs of the same shape
+    table = sa.sep_rope_table(500000.0, D, cache.slots + 1)
+    rsteps = min(steps, 65_536)
+    n_r = min(n_graphs, rsteps // chunk)
+
+    def run_chunk_rope(w):
+        for i in range(chunk):
+            t = w * chunk + i
+            sa.sep_attn_decode_rope(pq[t], pk[t], pv[t], cache, table, scale, out=out)
+            sa.sep_cache_update(cache, pk[t].view(1, Hkv, 1, D), pv[t].view(1, Hkv, 1, D),
+                                stage[i:i + 1].view(1, 1), sep)
+
+    rgraphs = []
+    with torch.cuda.stream(s_cap):
+        for w in range(n_r):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s_cap):
+                run_chunk_rope(w)
+            rgraphs.append(gr)
+    torch.cuda.synchronize()
+    cache.reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for c in range(rsteps // chunk):
+        t0 = c * chunk
+        stage.copy_(ids[t0:t0 + chunk], non_blocking=True)
+        rgraphs[c % n_r].replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_r = e0.elapsed_time(e1)
+    assert int(cache.state[0, 0]) == rsteps
+    res["rope_shifted"] = dict(steps=rsteps, tok_per_s=rsteps / (ms_r * 1e-3), us_per_step=ms_r * 1e3 / rsteps)
+    log(f"stream with RoPE shifting: {rsteps} steps -> {res['rope_shifted']['tok_per_s']:.0f} tok/s "
+        f"({res['rope_shifted']['us_per_step']:.2f} us/step)")
     return res
 
 

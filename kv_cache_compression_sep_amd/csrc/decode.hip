@@ -26,9 +26,9 @@
 // key u is exactly its shifted position: the cache holds unrotated keys and
 // key u is rotated by u theta_i when its slice is consumed, the query by
 // occ theta_i once; pair i is (x_i, x_{i+D/2}), which a lane holds in k-steps
-// ks and ks + NKS/2 of the same fragment, so the rotation is lane-local. The
-// cos/sin rows of the slice's keys are loaded with its K/V rows (they come
-// from L2: one table serves every sequence and head).
+// ks and ks + NKS/2 of the same fragment, so the rotation is lane-local. A
+// lane's keys advance by 32 NW positions per slice, so their angles advance
+// by one complex product per slice instead of a table load per key.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -68,7 +68,7 @@ __device__ __forceinline__ void rotate_pairs(u32x4& lo, u32x4& hi, const f32x4 (
 }
 
 template <int D, int NW, bool ROPE>
-__global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
+__global__ void __launch_bounds__(NW * 64, ROPE ? 8 / NW : 1) decode_kernel(DecodeArgs A) {
   constexpr int NT = NW * kWave;
   constexpr int VSTR = kSlice + 8;               // V^T row stride (bf16)
   constexpr int NDB = D / 16;                    // 16-row d-blocks of O^T
@@ -78,7 +78,8 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
   constexpr int VT_BYTES = NW * D * VSTR * 2;
   constexpr int RED_BYTES = NW * 16 * (D + 1) * 4;
   constexpr int ARENA = VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES;
-  __shared__ __attribute__((aligned(16))) char arena[ARENA];
+  constexpr int STEP_BYTES = ROPE ? 2 * 4 * (NKS / 2) * 4 * 16 : 0;   // RoPE angle steps, after the arena
+  __shared__ __attribute__((aligned(16))) char arena[ARENA + STEP_BYTES];
   __shared__ float red_m[NW][16];
   __shared__ float red_l[NW][16];
 
@@ -173,7 +174,6 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
   struct Regs {
     u32x4 k[2][NKS];
     u32x4 v[NPAIR][4];
-    f32x4 cs[ROPE ? 2 : 1][ROPE ? NKS / 2 : 1][4];   // (cos, sin) of the K pairs
   };
   auto load_slice = [&](int u0, Regs& R) {
 #pragma unroll
@@ -183,14 +183,6 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         R.k[gq][ks] = *reinterpret_cast<const u32x4*>(kr + 32 * ks + 8 * hh);
-      if constexpr (ROPE) {                      // key u sits at position u
-        const float* trow = A.rope + static_cast<int64_t>(u) * D;
-#pragma unroll
-        for (int ks = 0; ks < NKS / 2; ++ks)
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            R.cs[gq][ks][m] = *reinterpret_cast<const f32x4*>(trow + 2 * (32 * ks + 8 * hh + 2 * m));
-      }
     }
 #pragma unroll
     for (int j = 0; j < NPAIR; ++j) {
@@ -206,6 +198,45 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
   };
 
   const int iters = (L + NW * kSlice - 1) / (NW * kSlice);
+  // ROPE: (cos, sin) of this lane's pairs at its first key of the current
+  // slice, u = (it NW + wave) 32 + lane % 16; its second key (u + 16) takes
+  // one complex product with the angles of 16 positions. Between slices u
+  // grows by 32 NW, so the angles advance by one complex product with that
+  // row of the table; every 16th slice they are reloaded from the table,
+  // which keeps the fp32 drift of the products to a few ulp. The two step
+  // rows depend on the lane only through lane / 16 and sit in LDS.
+  f32x4 rc[ROPE ? NKS / 2 : 1][4];
+  // [16 | 32 NW][lane / 16][ks][m]
+  auto rstep = reinterpret_cast<f32x4(*)[4][NKS / 2 > 0 ? NKS / 2 : 1][4]>(arena + ARENA);
+  auto load_angles = [&](int it) {
+    const int u = min((it * NW + wave) * kSlice + lane % 16, L - 1);
+    const float* trow = A.rope + static_cast<int64_t>(u) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        rc[ks][m] = *reinterpret_cast<const f32x4*>(trow + 2 * (32 * ks + 8 * hh + 2 * m));
+  };
+  auto cmul = [](f32x4 a, f32x4 d) {
+    return f32x4{a[0] * d[0] - a[1] * d[1], a[1] * d[0] + a[0] * d[1], a[2] * d[2] - a[3] * d[3],
+                 a[3] * d[2] + a[2] * d[3]};
+  };
+  if constexpr (ROPE) {
+    load_angles(0);
+    constexpr int NST = 4 * (NKS / 2) * 4;
+    if (tid < 2 * NST) {
+      const int which = tid / NST, e = tid % NST;
+      const int h4 = e / ((NKS / 2) * 4), ks = (e / 4) % (NKS / 2), m = e % 4;
+      // row 16 exists when L > 16, row 32 NW when L > 32 NW; otherwise the
+      // keys that would use them are past the list and masked
+      const int row = which == 0 ? 16 : NW * kSlice;
+      f32x4 v = f32x4{1.f, 0.f, 1.f, 0.f};
+      if (L > row) v = *reinterpret_cast<const f32x4*>(A.rope + static_cast<int64_t>(row) * D +
+                                                         2 * (32 * ks + 8 * h4 + 2 * m));
+      rstep[which][h4][ks][m] = v;
+    }
+    __syncthreads();
+  }
   Regs cur;
   load_slice(wave * kSlice, cur);
   for (int it = 0; it < iters; ++it) {
@@ -232,9 +263,23 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeArgs A) {
     }
     if constexpr (ROPE) {
 #pragma unroll
-      for (int gq = 0; gq < 2; ++gq)
+      for (int ks = 0; ks < NKS / 2; ++ks) {
+        rotate_pairs(cur.k[0][ks], cur.k[0][ks + NKS / 2], rc[ks]);
+        f32x4 c16[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS / 2; ++ks) rotate_pairs(cur.k[gq][ks], cur.k[gq][ks + NKS / 2], cur.cs[gq][ks]);
+        for (int m = 0; m < 4; ++m) c16[m] = cmul(rc[ks][m], rstep[0][hh][ks][m]);
+        rotate_pairs(cur.k[1][ks], cur.k[1][ks + NKS / 2], c16);
+      }
+      if (it + 1 < iters) {
+        if ((it & 15) == 15) {
+          load_angles(it + 1);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < NKS / 2; ++ks)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) rc[ks][m] = cmul(rc[ks][m], rstep[1][hh][ks][m]);
+        }
+      }
     }
     // ---- scores S^T: lane l holds head l%16, keys 16*gq + 4*(l/16) + r
     f32x4 s[2];

@@ -48,6 +48,10 @@ ROPE_CASES = [
     (2, 32, 8, 128, 4, 64, 16, 96, 700, SEP_POLICY_DYNAMIC),
     (1, 8, 2, 64, 2, 9, 5, 20, 300, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM),
     (1, 16, 4, 128, 4, 256, 28, 512, 1500, 0),  # the batched workload's cache sizes
+    # long lists: more than 16 slices per wave, so the angles are reloaded
+    # from the table mid-list (8-wave workgroups, then 4-wave ones)
+    (1, 8, 2, 128, 4, 512, 64, 4096, 5000, 0),
+    (32, 8, 8, 64, 4, 128, 32, 2048, 2300, 0),
 ]
 
 
@@ -55,7 +59,7 @@ ROPE_CASES = [
 def test_decode_rope_matches_oracle(case):
     B, Hq, Hkv, D, a, s, p, w, T, policy = case
     print(f"rope decode case {case}", flush=True)
-    st = Stream(zlib.crc32(repr(("rope", case)).encode()), B, Hq, Hkv, D, T + 24, 0.2)
+    st = Stream(zlib.crc32(repr(("rope", case)).encode()), B, Hq, Hkv, D, T + 24, 0.1)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
     cache = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
     table = sep_rope_table(LLAMA3_ROPE_BASE, D, cache.slots + 1)
@@ -64,7 +68,7 @@ def test_decode_rope_matches_oracle(case):
     for b in range(B):
         sims[b].push_many([oracle.Entry(t, int(st.ids[b, t])) for t in range(T)])
     scale = 1.0 / math.sqrt(D)
-    for t in range(T, T + 24):
+    for t in range(T, T + (24 if B * T < 10000 else 6)):
         q = to_dev(np.ascontiguousarray(st.q[:, t]), "bf16")
         kn = to_dev(np.ascontiguousarray(st.k[:, :, t]), "bf16")
         vn = to_dev(np.ascontiguousarray(st.v[:, :, t]), "bf16")

@@ -8,8 +8,9 @@ K/V bytes of every block, in logical order) at every 4096th step.
 Batched decode, 64 sequences (32,768-token histories, a=4 s=256 p=28
 w=512): the histories are ingested with one bulk update, then 1024 decode +
 update steps run. Four sequences are compared in full (cache every 128
-steps, every decode output); for all 64 the cache positions and ids are
-compared with the closed form after the history and at the end.
+steps, every decode output, and the decode with RoPE position shifting
+every 128 steps); for all 64 the cache positions and ids are compared with
+the closed form after the history and at the end.
 """
 import math
 
@@ -19,11 +20,13 @@ import torch
 
 import oracle
 from inputs import configs, gen
-from kv_cache_compression_sep_amd import SepCache, sep_attn_decode, sep_cache_update
+from kv_cache_compression_sep_amd import (SepCache, sep_attn_decode, sep_attn_decode_rope, sep_cache_update,
+                                          sep_rope_table)
 
 from .gpu_util import check_close, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
+ROPE_BASE = 500000.0     # Llama 3
 
 
 def logical(cache, b):
@@ -149,12 +152,18 @@ def test_batched_decode_workload():
     print("[batched] history ingest matches", flush=True)
     scale = 1.0 / math.sqrt(D)
     outs = torch.empty((cfg.steps, B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    # every 128th step also runs with RoPE position shifting (Llama-3 base)
+    table = sep_rope_table(ROPE_BASE, D, cache.slots + 1)
+    rope_steps = list(range(0, cfg.steps, 128)) + [cfg.steps - 1]
+    routs = torch.empty((len(rope_steps), B, Hq, D), dtype=torch.bfloat16, device="cuda")
     snaps = {}
     for j in range(cfg.steps):
         qj = pq[:, j].contiguous()
         kj = pk[:, j].contiguous()
         vj = pv[:, j].contiguous()
         sep_attn_decode(qj, kj, vj, cache, scale, out=outs[j])
+        if j in rope_steps:
+            sep_attn_decode_rope(qj, kj, vj, cache, table, scale, out=routs[rope_steps.index(j)])
         sep_cache_update(cache, kj.view(B, Hkv, 1, D), vj.view(B, Hkv, 1, D),
                          d_ids[:, H + j:H + j + 1].contiguous(), d_sep)
         if (j + 1) % cfg.check_every == 0:
@@ -162,6 +171,7 @@ def test_batched_decode_workload():
                             cache.k.clone(), cache.v.clone())
     torch.cuda.synchronize()
     o_all = outs[:, checked].float().cpu().numpy().astype(np.float64)
+    r_all = routs[:, checked].float().cpu().numpy().astype(np.float64)
     print("[batched] gpu steps done", flush=True)
     for i, b in enumerate(checked):
         k_h, v_h, q_p, k_p, v_p = host[b]
@@ -173,6 +183,9 @@ def test_batched_decode_workload():
             vv = gen.bf16_bits_to_f64(vr(keys))
             o_ref, _ = oracle.decode_attention(gen.bf16_bits_to_f64(q_p[j]), kk, vv, scale)
             check_close(o_all[j, i], o_ref, "bf16", f"seq {b} step {j}")
+            if j in rope_steps:
+                r_ref, _ = oracle.decode_attention_shifted(gen.bf16_bits_to_f64(q_p[j]), kk, vv, scale, ROPE_BASE)
+                check_close(r_all[rope_steps.index(j), i], r_ref, "bf16", f"seq {b} step {j} rope")
             sims[b].push(oracle.Entry(t, int(ids[b, t])))
             if (j + 1) in snaps:
                 st, pos, tok, kc, vc = snaps[j + 1]
