@@ -148,20 +148,6 @@ __global__ void __launch_bounds__(NW * 64, ROPE ? 8 / NW : 1) decode_kernel(Deco
       if (hq >= G) v = u32x4{0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
-    if constexpr (ROPE) {                        // the query at position occ
-      const float* trow = A.rope + static_cast<int64_t>(occ) * D;
-#pragma unroll
-      for (int ks = 0; ks < NKS / 2; ++ks) {
-        f32x4 cs[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          cs[m] = *reinterpret_cast<const f32x4*>(trow + 2 * (32 * ks + 8 * (lane / 16) + 2 * m));
-        u32x4 lo = __builtin_bit_cast(u32x4, qf[ks]), hi = __builtin_bit_cast(u32x4, qf[ks + NKS / 2]);
-        rotate_pairs(lo, hi, cs);
-        qf[ks] = __builtin_bit_cast(bf16x8, lo);
-        qf[ks + NKS / 2] = __builtin_bit_cast(bf16x8, hi);
-      }
-    }
   }
 
   f32x4 oacc[NDB];
@@ -221,7 +207,23 @@ __global__ void __launch_bounds__(NW * 64, ROPE ? 8 / NW : 1) decode_kernel(Deco
     return f32x4{a[0] * d[0] - a[1] * d[1], a[1] * d[0] + a[0] * d[1], a[2] * d[2] - a[3] * d[3],
                  a[3] * d[2] + a[2] * d[3]};
   };
+  Regs cur;
+  load_slice(wave * kSlice, cur);               // the first slice's K/V in flight before the table reads
   if constexpr (ROPE) {
+    {                                            // the query at position occ
+      const float* trow = A.rope + static_cast<int64_t>(occ) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks) {
+        f32x4 cs[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          cs[m] = *reinterpret_cast<const f32x4*>(trow + 2 * (32 * ks + 8 * hh + 2 * m));
+        u32x4 lo = __builtin_bit_cast(u32x4, qf[ks]), hi = __builtin_bit_cast(u32x4, qf[ks + NKS / 2]);
+        rotate_pairs(lo, hi, cs);
+        qf[ks] = __builtin_bit_cast(bf16x8, lo);
+        qf[ks + NKS / 2] = __builtin_bit_cast(bf16x8, hi);
+      }
+    }
     load_angles(0);
     constexpr int NST = 4 * (NKS / 2) * 4;
     if (tid < 2 * NST) {
@@ -237,8 +239,6 @@ __global__ void __launch_bounds__(NW * 64, ROPE ? 8 / NW : 1) decode_kernel(Deco
     }
     __syncthreads();
   }
-  Regs cur;
-  load_slice(wave * kSlice, cur);
   for (int it = 0; it < iters; ++it) {
     const int u0 = (it * NW + wave) * kSlice;   // this wave's slice
     // ---- V rows -> transposed LDS slice. Quads q (keys 4q..4q+3) go to
