@@ -23,8 +23,9 @@ from the SepLLM pages. Citations use these tags:
 Modules:
   mask.py       separator flags, the 0/1 mask M, prefix-sum compaction,
                 tile classes.
-  attention.py  dense masked softmax attention (prefill) and attention over
-                an explicit key list (decode).
+  attention.py  dense masked softmax attention (prefill), its gradients,
+                attention over an explicit key list (decode) and of a chunk
+                of new tokens over a live cache.
   cache.py      list-based simulation of the four-block cache, and the
                 closed form of its state.
   rope.py       rotary position embedding and the position shifting of
@@ -39,7 +40,7 @@ library routines, invariants and a closed form). No function here is
 from .mask import (is_sep, sep_mask, mask_rows, compact, tile_class,  # noqa: F401
                    tile_class_slabs, visible_count)
 from .attention import (attention, attention_backward, attention_backward_sampled, attention_rows,  # noqa: F401
-                        decode_attention)
+                        chunk_attention, decode_attention)
 from .rope import decode_attention_shifted, rope_angles, rotate, round_bf16  # noqa: F401
 from .cache import (CacheSim, Entry, closed_form_positions, check_cache_params,  # noqa: F401
                     n_compactions, policy_positions)

@@ -163,6 +163,39 @@ def attention_backward_sampled(q, k, v, dout, out, M, scale, rows, keys, row_chu
     return dq, dk, dv
 
 
+def chunk_attention(cache_entries, q, k, v, ids, t: int, a: int, n: int, sep_ids, scale: float):
+    """Attention of a chunk of C new tokens over a live cache and the chunk.
+
+    P1 "SepAttention": build_generate_mask applies the prefill keep rule
+    (initial OR separator OR local window, AND causal) to the rows of new
+    queries, one row in plain decode, C rows here; P1 names a local window
+    for generation (generate_local_window_size) next to the prefill one, and
+    a window per layer, so n is an argument of each call. P2 §1.3: the cache
+    holds only what was retained, so the keys are the retained entries plus
+    the chunk.
+
+    cache_entries: the retained entries (any order), each an Entry with pos,
+    tok and k, v rows [Hkv, D]; q [Hq, C, D], k/v [Hkv, C, D], ids [C]: the
+    chunk, at positions t .. t+C-1. Query tau = t + i sees key j (position
+    p, token id x) iff p <= tau and (p < a or x is a separator or
+    tau - p < n). Returns O [Hq, C, D] and lse [Hq, C]."""
+    q = np.asarray(q, np.float64)
+    Hq, C, D = q.shape
+    Hkv = np.asarray(k).shape[0]
+    pos = np.array([e.pos for e in cache_entries] + list(range(t, t + C)), dtype=np.int64)
+    tok = np.array([e.tok for e in cache_entries] + list(np.asarray(ids)), dtype=np.int64)
+    kk = np.concatenate([np.asarray([e.k for e in cache_entries], np.float64).reshape(-1, Hkv, D)
+                         .transpose(1, 0, 2), np.asarray(k, np.float64)], axis=1)
+    vv = np.concatenate([np.asarray([e.v for e in cache_entries], np.float64).reshape(-1, Hkv, D)
+                         .transpose(1, 0, 2), np.asarray(v, np.float64)], axis=1)
+    sep = np.isin(tok, np.asarray(list(sep_ids), dtype=np.int64))
+    tau = np.arange(t, t + C, dtype=np.int64)[:, None]
+    p = pos[None, :]
+    M = (p <= tau) & ((p < a) | sep[None, :] | (tau - p < n))
+    G = Hq // Hkv
+    return attention_rows(q, kk, vv, M, scale, [h // G for h in range(Hq)])
+
+
 def decode_attention(q: np.ndarray, keys_k: np.ndarray, keys_v: np.ndarray, scale: float):
     """Attention of one decode step over an explicit key list, no further mask.
 

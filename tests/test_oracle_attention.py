@@ -311,3 +311,88 @@ def test_backward_sampled_matches_full_backward(G, S, a, n, p_sep, chunk):
     assert np.allclose(sq, rq[:, rows], rtol=1e-12, atol=1e-12)
     assert np.allclose(sk, rk[0, keys], rtol=1e-12, atol=1e-12)
     assert np.allclose(sv, rv[0, keys], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- chunk attention
+def _entries(ids, k, v, positions):
+    return [oracle.Entry(int(p), int(ids[p]), k[:, p], v[:, p]) for p in positions]
+
+
+def _chunk_case(rng, Hq, Hkv, T, D, p_sep):
+    ids = np.where(rng.random(T) < p_sep, rng.integers(0, 4, T), rng.integers(4, 100, T))
+    q = rng.standard_normal((Hq, T, D))
+    k = rng.standard_normal((Hkv, T, D))
+    v = rng.standard_normal((Hkv, T, D))
+    return ids, q, k, v
+
+
+@pytest.mark.parametrize("a,n,C", [(2, 5, 7), (0, 1, 12), (3, 40, 9)])
+def test_chunk_on_an_empty_cache_is_prefill(a, n, C):
+    rng = np.random.default_rng(a * 100 + n)
+    ids, q, k, v = _chunk_case(rng, 4, 2, C, 8, 0.3)
+    o, l = oracle.chunk_attention([], q, k, v, ids, 0, a, n, range(4), 0.4)
+    M = oracle.sep_mask(oracle.is_sep(ids, range(4)), a, n)
+    o2, l2 = oracle.attention(q, k, v, M, 0.4)
+    assert np.allclose(o, o2, atol=1e-13) and np.allclose(l, l2, atol=1e-13)
+
+
+@pytest.mark.parametrize("t,C,a,n", [(30, 10, 3, 6), (5, 20, 2, 3), (50, 1, 4, 9)])
+def test_chunk_without_eviction_is_prefill_rows(t, C, a, n):
+    """A cache that still holds every past token: the chunk's rows are rows
+    t..t+C-1 of the prefill over the whole sequence."""
+    rng = np.random.default_rng(t + C)
+    ids, q, k, v = _chunk_case(rng, 6, 3, t + C, 8, 0.25)
+    entries = _entries(ids, k, v, rng.permutation(t))          # any order
+    o, l = oracle.chunk_attention(entries, q[:, t:], k[:, t:], v[:, t:], ids[t:], t, a, n, range(4), 0.3)
+    M = oracle.sep_mask(oracle.is_sep(ids, range(4)), a, n)
+    o2, l2 = oracle.attention(q, k, v, M, 0.3)
+    assert np.allclose(o, o2[:, t:], atol=1e-12) and np.allclose(l, l2[:, t:], atol=1e-12)
+
+
+def test_chunk_of_one_with_a_wide_window_is_decode():
+    """C = 1 and a window past every retained entry: the decode step over
+    the cache's keys plus the token itself."""
+    rng = np.random.default_rng(3)
+    T = 200
+    ids, q, k, v = _chunk_case(rng, 4, 2, T + 1, 8, 0.2)
+    sim = oracle.CacheSim(2, 5, 4, 9, range(4))
+    sim.push_many([oracle.Entry(p, int(ids[p]), k[:, p], v[:, p]) for p in range(T)])
+    o, _ = oracle.chunk_attention(sim.keys(), q[:, T:], k[:, T:], v[:, T:], ids[T:], T, 2, T + 1, range(4), 0.5)
+    keys = [e.pos for e in sim.keys()] + [T]
+    o2, _ = oracle.decode_attention(q[:, T], k[:, keys], v[:, keys], 0.5)
+    assert np.allclose(o[:, 0], o2, atol=1e-13)
+
+
+def test_chunk_brute_force_loop():
+    """Tiny case with an arbitrary retained subset: a per-row Python loop."""
+    rng = np.random.default_rng(17)
+    t, C, a, n, D = 14, 5, 2, 3, 4
+    ids, q, k, v = _chunk_case(rng, 2, 1, t + C, D, 0.4)
+    kept = sorted(rng.choice(t, 8, replace=False).tolist())
+    o, _ = oracle.chunk_attention(_entries(ids, k, v, kept), q[:, t:], k[:, t:], v[:, t:], ids[t:], t, a, n,
+                                  range(4), 0.7)
+    for h in range(2):
+        for i in range(C):
+            tau = t + i
+            js = [p for p in kept + list(range(t, tau + 1))
+                  if p < a or ids[p] < 4 or tau - p < n]
+            s = [0.7 * float(np.dot(q[h, tau], k[0, p])) for p in js]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            ref = sum(wi / sum(w) * v[0, p] for wi, p in zip(w, js))
+            assert np.allclose(o[h, i], ref, atol=1e-12)
+
+
+def test_chunk_planted_mistakes_are_caught():
+    rng = np.random.default_rng(19)
+    t, C, a, n = 40, 12, 2, 5
+    ids, q, k, v = _chunk_case(rng, 2, 1, t + C, 8, 0.3)
+    kept = sorted(rng.choice(t, 25, replace=False).tolist())
+    good, _ = oracle.chunk_attention(_entries(ids, k, v, kept), q[:, t:], k[:, t:], v[:, t:], ids[t:], t, a, n,
+                                     range(4), 0.5)
+    wider, _ = oracle.chunk_attention(_entries(ids, k, v, kept), q[:, t:], k[:, t:], v[:, t:], ids[t:], t, a,
+                                      n + 1, range(4), 0.5)
+    assert not np.allclose(good, wider, atol=1e-6)             # the window's edge matters
+    nosep, _ = oracle.chunk_attention(_entries(ids, k, v, kept), q[:, t:], k[:, t:], v[:, t:], ids[t:], t, a,
+                                      n, [], 0.5)
+    assert not np.allclose(good, nosep, atol=1e-6)             # separators in the cache and the chunk
