@@ -282,6 +282,37 @@ int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const s
                     int Hq, float scale, void* out, float* lse, hipStream_t stream);
 
 /*
+ * sep_attn_prefill_chunk - a chunk of C new tokens attends the live cache
+ * and itself (chunked prefill into a cache).
+ * [P1 "SepAttention" (build_generate_mask: the prefill keep rule applied to
+ * the rows of new queries; a generation window, and a window per layer);
+ * P2 §1.3 (only the retained KV are read)]
+ *
+ *   q      [B, Hq, C, D]; k, v [B, Hkv, C, D] in cache->dtype (SEP_BF16
+ *          only); ids [B, C] int32: the chunk of each sequence, at
+ *          positions t .. t+C-1, t = its state word 0.
+ *   sep_ids [n_sep_ids] int32 device array (0..64 ids), as for
+ *          sep_cache_update.
+ *   n      >= 1: this call's window (the layer's generation window).
+ * Query tau = t + i sees a retained entry or chunk key at position p iff
+ * p <= tau and (p < a, or its token id is a separator, or tau - p < n).
+ * With C = 1 and n at least the cache's slot count this is sep_attn_decode.
+ * The cache is read, not written: insert the chunk afterwards with
+ * sep_cache_update(cache, k, v, ids, C, ...).
+ *   workspace  device memory of at least sep_chunk_workspace_bytes(cache, C)
+ *          bytes, 256-byte aligned, overwritten (the keys laid out as one
+ *          sequence per kv head, with flags and their compaction).
+ *   scale  > 0; out [B, Hq, C, D] (bf16); lse [B, Hq, C] float32 or NULL.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_ALIGN, SEP_ERR_WORKSPACE, SEP_ERR_HIP.
+ */
+size_t sep_chunk_workspace_bytes(const sep_cache* cache, int C);
+int sep_attn_prefill_chunk(const void* q, const void* k, const void* v, const int32_t* ids, int C,
+                           const int32_t* sep_ids, int n_sep_ids, const sep_cache* cache, int Hq, int n,
+                           float scale, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                           hipStream_t stream);
+
+/*
  * sep_rope_table - cos/sin table of rotary position embedding.
  * [P1 "Streaming-SepLLM": streaming needs positional-encoding shifting (the
  * Llama pos_shift module); RoPE as published: Su et al., RoFormer, §3.4]

@@ -24,7 +24,8 @@ from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
 __all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
-           "sep_attn_decode", "sep_attn_decode_rope", "sep_rope_table",
+           "sep_attn_decode", "sep_attn_decode_rope", "sep_rope_table", "sep_attn_prefill_chunk",
+           "chunk_workspace_bytes",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
            "SEP_POLICY_DYNAMIC", "SEP_POLICY_NO_ACCUM"]
 
@@ -237,6 +238,45 @@ def sep_cache_update(cache: SepCache, k_new, v_new, ids_new, sep_ids):
                                 _ptr(sep_ids) if sep_ids.numel() else None, sep_ids.numel(),
                                 _stream())
     _lib.check("sep_cache_update", code)
+
+
+def chunk_workspace_bytes(cache: "SepCache", C: int) -> int:
+    """Workspace bytes sep_attn_prefill_chunk needs for a chunk of C tokens."""
+    st = cache.struct()
+    return int(_lib.load().sep_chunk_workspace_bytes(ctypes.byref(st), C))
+
+
+def sep_attn_prefill_chunk(q, k, v, ids, cache: "SepCache", sep_ids, n: int, scale: float | None = None, *,
+                           workspace=None, out=None, return_lse: bool = False, lse=None):
+    """A chunk of C new tokens over the live cache and itself: q [B,Hq,C,D],
+    k/v [B,Hkv,C,D] (bf16), ids [B,C] int32, window n. The cache is not
+    modified (insert the chunk with sep_cache_update afterwards)."""
+    lib = _lib.load()
+    _need(q, "q", cache.dtype, 4)
+    _need(k, "k", cache.dtype, 4)
+    _need(v, "v", cache.dtype, 4)
+    _need(ids, "ids", torch.int32, 2)
+    _need(sep_ids, "sep_ids", torch.int32, 1)
+    B, Hq, C, D = q.shape
+    if (B, D) != (cache.B, cache.D) or k.shape != (B, cache.Hkv, C, D) or v.shape != k.shape:
+        raise ValueError("shapes do not match the cache")
+    if ids.shape != (B, C):
+        raise ValueError("ids must be [B, C]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = chunk_workspace_bytes(cache, C)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    st = cache.struct()
+    code = lib.sep_attn_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), ids.data_ptr(), C,
+                                      sep_ids.data_ptr(), sep_ids.numel(), ctypes.byref(st), Hq, n, float(scale),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      out.data_ptr(), _ptr(lse), _stream())
+    _lib.check("sep_attn_prefill_chunk", code)
+    return (out, lse) if return_lse else out
 
 
 def sep_rope_table(base: float, D: int, n_pos: int, *, out=None, device="cuda"):

@@ -53,6 +53,9 @@ SIGNATURES = {
     "sep_cache_reset": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp]),
     "sep_cache_update": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp, c_vp, c_vp, c_int, c_vp,
                                  c_int, c_vp]),
+    "sep_chunk_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SepCacheStruct), c_int]),
+    "sep_attn_prefill_chunk": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, ctypes.POINTER(SepCacheStruct),
+                                       c_int, c_int, c_float, c_vp, ctypes.c_size_t, c_vp, c_vp, c_vp]),
     "sep_rope_table": (c_int, [ctypes.c_double, c_int, c_int, c_vp, c_vp]),
     "sep_attn_decode_rope": (c_int, [c_vp, c_vp, c_vp, ctypes.POINTER(SepCacheStruct), c_int, c_float, c_vp,
                                      c_int, c_vp, c_vp, c_vp]),

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsepattn.so")
 SOURCES = ["api.hip", "mask.hip", "compact.hip", "prefill.hip", "prefill_bf16.hip", "prefill_bwd.hip",
-           "cache.hip", "decode.hip"]
+           "cache.hip", "decode.hip", "chunk.hip"]
 ARCH = os.environ.get("SEPATTN_ARCH", "gfx950")
 
 FLAGS = [

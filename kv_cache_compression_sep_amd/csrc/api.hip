@@ -55,7 +55,7 @@ const char* sep_status_string(int s) {
     case SEP_ERR_SHAPE: return "a size is out of range or inconsistent";
     case SEP_ERR_PARAM: return "a parameter breaks the Sep-Attention / cache contract";
     case SEP_ERR_DTYPE: return "dtype not supported by this entry point";
-    case SEP_ERR_WORKSPACE: return "reserved";
+    case SEP_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case SEP_ERR_HIP: return "HIP launch failure";
     case SEP_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     default: return "unknown status";
@@ -168,6 +168,36 @@ int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const s
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return SEP_ERR_ALIGN;
   return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, nullptr, out, lse, stream));
+}
+
+size_t sep_chunk_workspace_bytes(const sep_cache* cache, int C) {
+  if (check_cache(cache) != SEP_OK || C < 1) return 0;
+  return sep::chunk_workspace_bytes(*cache, C);
+}
+
+int sep_attn_prefill_chunk(const void* q, const void* k, const void* v, const int32_t* ids, int C,
+                           const int32_t* sep_ids, int n_sep_ids, const sep_cache* cache, int Hq, int n,
+                           float scale, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                           hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != SEP_OK) return st;
+  st = check_cache_kv(cache);
+  if (st != SEP_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || ids == nullptr || out == nullptr) return SEP_ERR_NULL;
+  if (n_sep_ids < 0 || n_sep_ids > SEP_MAX_SEP_IDS) return SEP_ERR_SHAPE;
+  if (n_sep_ids > 0 && sep_ids == nullptr) return SEP_ERR_NULL;
+  if (cache->dtype != SEP_BF16) return SEP_ERR_DTYPE;
+  if (C < 1) return SEP_ERR_SHAPE;
+  if (Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return SEP_ERR_SHAPE;
+  if (static_cast<int64_t>(sep::cache_slots(*cache)) + C > (1 << 24)) return SEP_ERR_SHAPE;
+  if (n < 1) return SEP_ERR_PARAM;
+  if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
+  if (workspace == nullptr || workspace_bytes < sep::chunk_workspace_bytes(*cache, C) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return SEP_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_prefill_chunk(q, k, v, ids, C, sep_ids, n_sep_ids, *cache, Hq, n, scale,
+                                              workspace, out, lse, stream));
 }
 
 int sep_rope_table(double base, int D, int n_pos, float* table, hipStream_t stream) {

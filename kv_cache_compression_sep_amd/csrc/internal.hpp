@@ -42,6 +42,10 @@ hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void
                                hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
                          int Hq, float scale, const float* rope, void* out, float* lse, hipStream_t st);
+size_t chunk_workspace_bytes(const sep_cache& c, int C);
+hipError_t launch_prefill_chunk(const void* q, const void* k, const void* v, const int32_t* ids, int C,
+                                const int32_t* sep_ids, int n_sep, const sep_cache& c, int Hq, int n,
+                                float scale, void* workspace, void* out, float* lse, hipStream_t st);
 hipError_t launch_rope_table(double base, int D, int n_pos, float* table, hipStream_t st);
 
 }  // namespace sep

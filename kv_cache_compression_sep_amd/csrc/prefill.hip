@@ -357,6 +357,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype
   A.Hq = Hq;
   A.Hkv = Hkv;
   A.S = S;
+  A.Skv = S;
+  A.q_base = 0;
+  A.key_lo = nullptr;
   A.a = a;
   A.n = n;
   A.G = Hq / Hkv;

@@ -1,6 +1,7 @@
 // Tile bookkeeping shared by the Sep-Attention prefill kernels.
 //
 // A workgroup owns query rows [q0, q1). With band_lo = max(q0 - n + 1, 0),
+// (or the first key row that may enter a band, in chunk mode),
 // every key j < band_lo is visible to all of these queries iff it is an
 // initial token (j < a) or a separator, and to none of them otherwise
 // (SepLLM pages: P2 §1.2 mask matrix; P1 "SepAttention", initial OR window
@@ -27,6 +28,12 @@ struct PrefillArgs {
   int B, Hq, Hkv, S, a, n;
   int G, HPW, QT, n_hg, n_qt;
   float scale_log2;
+  // Chunk mode (sep_attn_prefill_chunk): the keys are a longer sequence of
+  // Skv rows in which query row r sits at index q_base + r, and key rows
+  // below key_lo[b] are never band keys. Plain prefill: Skv = S, q_base = 0,
+  // key_lo = nullptr.
+  int Skv, q_base;
+  const int32_t* key_lo;
 };
 
 struct TileInfo {
@@ -34,9 +41,10 @@ struct TileInfo {
 };
 
 template <int KT>
-__device__ __forceinline__ TileInfo tile_info(const int32_t* rk, int S, int a, int n, int q0, int q1) {
+__device__ __forceinline__ TileInfo tile_info(const int32_t* rk, int S, int a, int n, int q0, int q1,
+                                              int key_lo = 0) {
   TileInfo ti;
-  ti.band_lo = max(q0 - n + 1, 0);
+  ti.band_lo = max(q0 - n + 1, key_lo);
   ti.n_init = min(a, ti.band_lo);
   ti.rank_a = rk[min(a, S)];
   const int n_sepg = (ti.band_lo > a) ? (rk[ti.band_lo] - ti.rank_a) : 0;

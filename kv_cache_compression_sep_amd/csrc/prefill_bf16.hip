@@ -173,7 +173,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   const int bg = pair / P.n_hg;
   const int g = bg % P.Hkv;
   const int b = bg / P.Hkv;
-  const int S = P.S;
+  const int S = P.S;                                   // query rows
+  const int Skv = P.Skv;                               // key rows (S, except in chunk mode)
+  const int qv = P.q_base;                             // key index of query row 0
   const int q0 = qt * P.QT;
   const int q1 = min(q0 + P.QT, S);
   const int hw = wave % P.HPW;
@@ -181,12 +183,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   const int h = g * P.G + hg * P.HPW + hw;
   const int qw0 = q0 + 32 * rb;                        // this wave's first query row
 
-  const int32_t* rk = P.rank + static_cast<int64_t>(b) * (S + 1);
-  const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * S;
-  const TileInfo ti = tile_info<KT>(rk, S, P.a, P.n, q0, q1);
+  const int32_t* rk = P.rank + static_cast<int64_t>(b) * (Skv + 1);
+  const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * Skv;
+  const int key_lo = P.key_lo == nullptr ? 0 : P.key_lo[b];
+  const TileInfo ti = tile_info<KT>(rk, Skv, P.a, P.n, qv + q0, qv + q1, key_lo);
 
-  const char* kb = reinterpret_cast<const char*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D * 2;
-  const char* vb = reinterpret_cast<const char*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D * 2;
+  const char* kb = reinterpret_cast<const char*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * Skv * D * 2;
+  const char* vb = reinterpret_cast<const char*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * Skv * D * 2;
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(P.q) + static_cast<int64_t>(b * P.Hq + h) * S * D;
 
   // ---- index slice of tile t into ring slot t % IDXR: wave 0 loads
@@ -203,11 +206,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       if (!band) {
         if (wave == 0) {
           base = sp;
-          off = 4u * min(max(ti.rank_a + t * KT + lane - ti.n_init, 0), S - 1);
+          off = 4u * min(max(ti.rank_a + t * KT + lane - ti.n_init, 0), Skv - 1);
           dst = lds_addr(idxr[t % IDXR][0]);
         }
       } else {
-        off = 4u * min(ti.band_lo + (t - ti.ntg) * KT + lane + wave, S);
+        off = 4u * min(ti.band_lo + (t - ti.ntg) * KT + lane + wave, Skv);
         dst = lds_addr(idxr[t % IDXR][wave]);
       }
     }
@@ -222,7 +225,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       const int r = ((wave * PW + i) * kWave + lane) / CPR;
       int key;
       if (band) {
-        key = min(ti.band_lo + (t - ti.ntg) * KT + r, S - 1);
+        key = min(ti.band_lo + (t - ti.ntg) * KT + r, Skv - 1);
       } else {
         const int u = t * KT + r;
         int gathered = idxr[t % IDXR][0][r];
@@ -287,9 +290,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   float m_run = -INFINITY, corr = 1.0f;
   bool resc = false;
-  const int qmax = min(qw0 + 31, S - 1);
+  const int qmax = qv + min(qw0 + 31, S - 1);          // key index of the wave's last query
   const int hsel = lane / 32;
-  const int qi = qw0 + lane % 32;
+  const int qrow = qw0 + lane % 32;                    // this lane's query row
+  const int qi = qv + qrow;                            // and its key index
+  const int qwv0 = qv + qw0;
 
   // per-lane LDS byte offsets of the QK reads (chunk 2*ks + hsel of rows
   // lane%32 [+32]) and of the transposed V reads (see pv below)
@@ -342,7 +347,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     const int jmin = ti.band_lo + (t - ti.ntg) * KT;
     int r0 = idxr[t % IDXR][0][lane], r1 = idxr[t % IDXR][1][lane];
     asm volatile("" : "+v"(r0), "+v"(r1));            // read both unconditionally (no branch)
-    return ballot((jmin + lane < S) & (r1 != r0));
+    return ballot((jmin + lane < Skv) & (r1 != r0));
   };
   // ---- V^T operand of PV MFMA i (16-key chunk kc = i / DB, d block
   //      db = i % DB) of the tile in V stage vst. O^T += V^T[:, chunk] . P^T:
@@ -402,7 +407,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     const bool band = t >= ti.ntg;
     const int jmin = band ? ti.band_lo + (t - ti.ntg) * KT : 0;
     const int nvalid = band ? KT : min(KT, ti.n_glob - t * KT);
-    const bool full = band ? (jmin + KT - 1 <= qw0 && jmin >= qmax - P.n + 1) : nvalid == KT;
+    const bool full = band ? (jmin + KT - 1 <= qwv0 && jmin >= qmax - P.n + 1) : nvalid == KT;
     if (!full) {
       const uint64_t vis = vis_word(band, qi, jmin, P.n, P.a, sepbits, nvalid) >> (4 * hsel);
 #pragma unroll
@@ -510,8 +515,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       *reinterpret_cast<u32x4*>(ob + static_cast<int64_t>(row) * D + 8 * c) =
           *reinterpret_cast<const u32x4*>(stg + r * OSTR + 8 * c);
   }
-  if (P.lse != nullptr && lane < 32 && qi < S)
-    P.lse[static_cast<int64_t>(b * P.Hq + h) * S + qi] = (m_run + fast_log2(l_tot)) * kLn2;
+  if (P.lse != nullptr && lane < 32 && qrow < S)
+    P.lse[static_cast<int64_t>(b * P.Hq + h) * S + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 }  // namespace

@@ -206,3 +206,26 @@ def test_rope_argument_checks(lib):
     assert dec(_cache(policy=1), npos=389) == E.SEP_ERR_PARAM   # dynamic ring: s + p + w slots
     assert dec(c, rope=FAKE + 4) == E.SEP_ERR_ALIGN
     assert dec(_cache(dtype=0)) == E.SEP_ERR_DTYPE
+
+
+def test_chunk_argument_checks(lib):
+    E = _lib
+    c = _cache()                                          # 4 + 64 + 320 slots, 8 kv heads, D = 128
+    need = lib.sep_chunk_workspace_bytes(ctypes.byref(c), 100)
+    assert need >= 2 * 8 * (388 + 100) * 128 * 2
+    assert lib.sep_chunk_workspace_bytes(ctypes.byref(c), 0) == 0
+    ch = lambda cc, **kw: lib.sep_attn_prefill_chunk(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("ids", FAKE), kw.get("C", 100), FAKE, kw.get("nsep", 4),
+        ctypes.byref(cc), kw.get("Hq", 32), kw.get("n", 64), 0.1, kw.get("ws", 1 << 20), kw.get("wsb", need),
+        FAKE, None, None)
+    assert ch(c, q=None) == E.SEP_ERR_NULL
+    assert ch(c, ids=None) == E.SEP_ERR_NULL
+    assert ch(c, nsep=65) == E.SEP_ERR_SHAPE
+    assert ch(c, C=0) == E.SEP_ERR_SHAPE
+    assert ch(c, Hq=12) == E.SEP_ERR_SHAPE
+    assert ch(c, n=0) == E.SEP_ERR_PARAM
+    assert ch(c, ws=None) == E.SEP_ERR_WORKSPACE
+    assert ch(c, wsb=need - 1) == E.SEP_ERR_WORKSPACE
+    assert ch(c, ws=(1 << 20) + 16) == E.SEP_ERR_WORKSPACE
+    assert ch(c, q=FAKE + 2) == E.SEP_ERR_ALIGN
+    assert ch(_cache(dtype=0)) == E.SEP_ERR_DTYPE
