@@ -19,6 +19,10 @@ under "secondary":
     stream: tokens/s of in-order decode + update steps, replayed from HIP
     graphs of 256 steps; then its first 65,536 steps with RoPE position
     shifting;
+  * chunked prefill: the prefill workload's 8192-token prompt streamed into
+    the streaming cache (4/64/64/256) in 4 chunks of 2048
+    (sep_attn_prefill_chunk, window 256, then sep_cache_update): prompt
+    tokens/s and useful TFLOP/s of the chunk attention;
   * prefill backward on the prefill workload (sep_attn_prefill_backward,
     fp32 arithmetic): useful TFLOP/s = 10 * D * visible pairs per query head
     (S = QK^T recomputed, dP = dO V^T, dQ, dK, dV) over its launch time,
@@ -205,6 +209,101 @@ def bench_backward(args, torch, sa, res):
             "inputs": "bf16", "us_per_call": round(ms * 1e3, 2), "useful_flop": useful,
             "tflops": round(tflops, 2), "peak_fp32_tflops": PEAK_FP32_TFLOPS,
             "frac_fp32_peak": round(tflops / PEAK_FP32_TFLOPS, 4)}
+
+
+def chunk_visible_pairs(pos, tok, flags_chunk, t, C, a, n, sep_set):
+    """Visible (query, key) pairs of one chunk of one sequence under the
+    generate-mask rule: retained entries (positions pos, ids tok; -1 = empty
+    slot) and the chunk's own keys."""
+    live = pos >= 0
+    p = pos[live].astype(np.int64)
+    sep = np.isin(tok[live], sep_set)
+    glob = (p < a) | sep
+    tau = np.arange(t, t + C, dtype=np.int64)
+    n_glob = int(glob.sum())
+    # cache entries: global ones for every query, the others inside the window
+    rest = np.sort(p[~glob])
+    cache_win = np.searchsorted(rest, tau - n + 1, side="left")
+    pairs = C * n_glob + int((len(rest) - cache_win).sum())
+    # chunk keys: causal, and initial or separator or inside the window
+    cg = flags_chunk | (np.arange(t, t + C) < a)
+    cg_before = np.concatenate([[0], np.cumsum(cg)])
+    i = np.arange(C)
+    lo = np.maximum(i - n + 1, 0)
+    pairs += int((cg_before[lo] + (i + 1 - lo)).sum())
+    return pairs
+
+
+def bench_chunk(args, torch, sa, configs, gen):
+    """The 8192-token Llama-3 layer prompt streamed into the streaming cache
+    (4/64/64/256) in 4 chunks of 2048: per chunk, sep_attn_prefill_chunk
+    (window 256) then sep_cache_update."""
+    cfg = configs.LLAMA3_LAYER_PREFILL
+    sc = configs.STREAM_DECODE
+    B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+    C = 2048
+    n = cfg.n
+    ids_h = np.stack([gen.prefill_ids(cfg, 0)])
+    ids = torch.from_numpy(ids_h).cuda()
+    sep = torch.tensor(cfg.sep_ids, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1007)
+    q = torch.randn((B, Hq, S, D), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S, D), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S, D), device="cuda", generator=g).to(torch.bfloat16)
+    chunks = [(c0, c0 + C) for c0 in range(0, S, C)]
+    qc = [q[:, :, c0:c1].contiguous() for c0, c1 in chunks]
+    kc = [k[:, :, c0:c1].contiguous() for c0, c1 in chunks]
+    vc = [v[:, :, c0:c1].contiguous() for c0, c1 in chunks]
+    ic = [ids[:, c0:c1].contiguous() for c0, c1 in chunks]
+    cache = sa.SepCache(B, Hkv, D, sc.a, sc.s, sc.p, sc.w)
+    ws = torch.empty((sa.chunk_workspace_bytes(cache, C),), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qc[0])
+    scale = 1.0 / math.sqrt(D)
+    # useful pairs from the cache states the chunks meet
+    sep_set = np.asarray(cfg.sep_ids)
+    pairs = 0
+    cache.reset()
+    for j, (c0, c1) in enumerate(chunks):
+        pos = cache.pos[0].cpu().numpy()
+        tok = cache.tok[0].cpu().numpy()
+        pairs += chunk_visible_pairs(pos, tok, np.isin(ids_h[0, c0:c1], sep_set), c0, C, sc.a, n, sep_set)
+        sa.sep_cache_update(cache, kc[j], vc[j], ic[j], sep)
+    useful = 4.0 * D * pairs * Hq
+    st = torch.cuda.current_stream()
+
+    def run():
+        cache.reset()
+        for j in range(len(chunks)):
+            ev_a[j][0].record(st)
+            sa.sep_attn_prefill_chunk(qc[j], kc[j], vc[j], ic[j], cache, sep, n, scale, workspace=ws, out=out)
+            ev_a[j][1].record(st)
+            sa.sep_cache_update(cache, kc[j], vc[j], ic[j], sep)
+
+    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in chunks]
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 20))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_attn = 0.0
+    e0.record(st)
+    for _ in range(reps):
+        run()
+        torch.cuda.synchronize()
+        t_attn += sum(a.elapsed_time(b) for a, b in ev_a)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_prompt = e0.elapsed_time(e1) / reps
+    ms_attn = t_attn / reps
+    res = dict(workload=f"{cfg.name} in chunks of {C} into cache {sc.a}/{sc.s}/{sc.p}/{sc.w}, window {n}",
+               visible_pairs_per_head=pairs, useful_flop=useful, prompt_ms=ms_prompt,
+               prompt_tok_per_s=S / (ms_prompt * 1e-3), chunk_attention_ms=ms_attn,
+               chunk_attention_tflops=useful / (ms_attn * 1e-3) / 1e12)
+    log(f"chunked prefill: {S} tokens in {len(chunks)} chunks, {ms_prompt * 1e3:.0f} us per prompt "
+        f"({res['prompt_tok_per_s']:.0f} tok/s), chunk attention {ms_attn * 1e3:.0f} us "
+        f"({res['chunk_attention_tflops']:.0f} useful TFLOP/s)")
+    return res
 
 
 def cpu_baseline_prefill(res, oracle, gen, budget_s=20.0):
@@ -523,7 +622,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--stream-steps", type=int, default=4_194_304)
-    ap.add_argument("--only", choices=["all", "prefill", "backward", "decode", "stream", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "backward", "chunk", "decode", "stream", "copy"],
                     default="all",
                     help="'copy' runs only a plain device copy of known size, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -555,6 +654,8 @@ def main():
         if args.only == "backward":
             print(json.dumps({"secondary": secondary}))
             return
+    if args.only in ("all", "chunk"):
+        secondary["chunked_prefill"] = bench_chunk(args, torch, sa, configs, gen)
     if args.only in ("all", "decode"):
         secondary["batched_decode_b64"] = bench_batched(args, torch, sa, configs, gen)
     if args.only in ("all", "stream"):

@@ -29,7 +29,7 @@
 namespace sep {
 namespace {
 
-constexpr int kRowsPerBlock = 64;
+constexpr int kRowsPerBlock = 32;
 
 struct ChunkArgs {
   const uint16_t* kc;
@@ -47,7 +47,7 @@ struct ChunkArgs {
   int n_sep, a, s, rw, slots, Hkv, C, V;
 };
 
-// grid (ceil(V / kRowsPerBlock), B * Hkv): the rows [x0, x0 + 64) of one
+// grid (ceil(V / kRowsPerBlock), B * Hkv): the rows [x0, x0 + 32) of one
 // (sequence, kv head); 16-byte chunks, D / 8 per row
 template <int D>
 __global__ void __launch_bounds__(256) context_kernel(ChunkArgs A) {
@@ -78,48 +78,70 @@ __global__ void __launch_bounds__(256) context_kernel(ChunkArgs A) {
   const int klo = A.slots - n_rec;
   if (g == 0 && blockIdx.x == 0 && threadIdx.x == 0) A.key_lo[b] = klo;
 
-  // source of row x: 0 padding, 1 cache slot, 2 chunk row; and its flag
-  auto source = [&](int x, int* src, int* row, int* flag) {
+  // source of row x: 0 padding, 1 cache slot, 2 chunk row
+  auto source = [&](int x, int* src, int* row) {
     if (x < n_init) {
-      *src = 1; *row = x; *flag = 1;
+      *src = 1; *row = x;
     } else if (x < n_init + cnt) {
       int r = s0 + (x - n_init);
       r = r >= A.s ? r - A.s : r;
-      *src = 1; *row = A.a + r; *flag = 1;
+      *src = 1; *row = A.a + r;
     } else if (x < klo) {
-      *src = 0; *row = 0; *flag = 0;
+      *src = 0; *row = 0;
     } else if (x < A.slots) {
       int r = r0 + (x - klo);
       r = r >= A.rw ? r - A.rw : r;
       *src = 1; *row = A.a + A.s + r;
-      *flag = in_set(A.tok[static_cast<int64_t>(b) * A.slots + *row], set, A.n_sep);
     } else {
-      const int c = x - A.slots;
-      *src = 2; *row = c;
-      *flag = in_set(A.ids[static_cast<int64_t>(b) * A.C + c], set, A.n_sep) || (t + c < A.a);
+      *src = 2; *row = x - A.slots;
     }
   };
+  // flags (kv head 0 only): initial and separator-ring entries 1, padding 0,
+  // recent entries and chunk tokens by their id (chunk tokens before a: 1)
+  if (g == 0) {
+    for (int x = x0 + threadIdx.x; x < min(x0 + kRowsPerBlock, A.V); x += blockDim.x) {
+      int src, row;
+      source(x, &src, &row);
+      bool flag = false;
+      if (x < n_init + cnt) flag = true;
+      else if (src == 1) flag = in_set(A.tok[static_cast<int64_t>(b) * A.slots + row], set, A.n_sep);
+      else if (src == 2) flag = in_set(A.ids[static_cast<int64_t>(b) * A.C + row], set, A.n_sep) || (t + row < A.a);
+      A.xflag[static_cast<int64_t>(b) * A.V + x] = static_cast<uint8_t>(flag);
+    }
+  }
 
   const int64_t cbase = static_cast<int64_t>(bg) * A.slots * D;
   const int64_t nbase = static_cast<int64_t>(bg) * A.C * D;
   const int64_t xbase = static_cast<int64_t>(bg) * A.V * D;
-  for (int e = threadIdx.x; e < kRowsPerBlock * CPR; e += blockDim.x) {
+  // every load of the thread first (one unconditional load per operand,
+  // from a computed address; padding rows read cache row 0 and store
+  // zeros), then the stores: kPer rows in flight
+  constexpr int kPer = kRowsPerBlock * CPR / 256;
+  u32x4 kk[kPer], vv[kPer];
+  bool pad[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int x = min(x0 + e / CPR, A.V - 1);
+    const int c = e % CPR;
+    int src, row;
+    source(x, &src, &row);
+    pad[i] = src == 0;
+    const uint16_t* kp = src == 2 ? A.k + nbase : A.kc + cbase;
+    const uint16_t* vp = src == 2 ? A.v + nbase : A.vc + cbase;
+    kk[i] = *reinterpret_cast<const u32x4*>(kp + static_cast<int64_t>(row) * D + 8 * c);
+    vv[i] = *reinterpret_cast<const u32x4*>(vp + static_cast<int64_t>(row) * D + 8 * c);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + 256 * i;
     const int x = x0 + e / CPR;
     const int c = e % CPR;
-    if (x >= A.V) break;
-    int src, row, flag;
-    source(x, &src, &row, &flag);
-    u32x4 kk = u32x4{0u, 0u, 0u, 0u}, vv = kk;
-    if (src == 1) {
-      kk = *reinterpret_cast<const u32x4*>(A.kc + cbase + static_cast<int64_t>(row) * D + 8 * c);
-      vv = *reinterpret_cast<const u32x4*>(A.vc + cbase + static_cast<int64_t>(row) * D + 8 * c);
-    } else if (src == 2) {
-      kk = *reinterpret_cast<const u32x4*>(A.k + nbase + static_cast<int64_t>(row) * D + 8 * c);
-      vv = *reinterpret_cast<const u32x4*>(A.v + nbase + static_cast<int64_t>(row) * D + 8 * c);
+    if (x < A.V) {
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(A.xk + xbase + static_cast<int64_t>(x) * D + 8 * c) = pad[i] ? z : kk[i];
+      *reinterpret_cast<u32x4*>(A.xv + xbase + static_cast<int64_t>(x) * D + 8 * c) = pad[i] ? z : vv[i];
     }
-    *reinterpret_cast<u32x4*>(A.xk + xbase + static_cast<int64_t>(x) * D + 8 * c) = kk;
-    *reinterpret_cast<u32x4*>(A.xv + xbase + static_cast<int64_t>(x) * D + 8 * c) = vv;
-    if (g == 0 && c == 0) A.xflag[static_cast<int64_t>(b) * A.V + x] = static_cast<uint8_t>(flag);
   }
 }
 
