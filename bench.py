@@ -93,6 +93,46 @@ def measured_traffic(kernel: str):
         return None
 
 
+def write_traffic(dirs):
+    """profiles/traffic.json from four rocprofv3 --pmc output folders: the
+    prefill's FETCH_SIZE and WRITE_SIZE, then the 1 GiB copy's (bench.py
+    --only copy). Host-only; records the current kernel source hash."""
+    import csv
+    import glob
+
+    def mean(d, kernel, counter):
+        vals = []
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {kernel} under {d}")
+        return sum(vals) / len(vals), len(vals)
+
+    pf, pw, cf, cw = dirs
+    fetch, nf = mean(pf, "prefill_bf16_kernel", "FETCH_SIZE")
+    write, nw = mean(pw, "prefill_bf16_kernel", "WRITE_SIZE")
+    cfetch, _ = mean(cf, "copyBuffer", "FETCH_SIZE")
+    cwrite, _ = mean(cw, "copyBuffer", "WRITE_SIZE")
+    fs = COPY_BYTES / 1024 / cfetch
+    ws = COPY_BYTES / 1024 / cwrite
+    hbm = int(round((fetch * fs + write * ws) * 1024))
+    from inputs import configs
+    cfg = configs.LLAMA3_LAYER_PREFILL
+    alg = 2 * (cfg.B * cfg.Hq * cfg.S * cfg.D * 2) + 2 * (cfg.B * cfg.Hkv * cfg.S * cfg.D * 2)
+    d = {"sep_attn_prefill": {"workload": cfg.name, "source_hash": kernel_source_hash(),
+                              "fetch_size_kib_per_dispatch": round(fetch, 1),
+                              "write_size_kib_per_dispatch": round(write, 1), "dispatches": [nf, nw],
+                              "copy_bytes": COPY_BYTES, "copy_fetch_size_kib": round(cfetch, 1),
+                              "copy_write_size_kib": round(cwrite, 1), "fetch_scale": round(fs, 4),
+                              "write_scale": round(ws, 4), "hbm_bytes_per_launch": hbm,
+                              "algorithmic_bytes_per_launch": alg}}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(d, fh, indent=1)
+    print(json.dumps(d))
+
+
 # ------------------------------------------------------------------ copy
 COPY_BYTES = 1 << 30
 
@@ -627,7 +667,13 @@ def main():
                     help="'copy' runs only a plain device copy of known size, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 --pmc folders (prefill FETCH_SIZE, "
+                         "prefill WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE) and exit; needs no GPU")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Sep-Attention path here has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)
