@@ -3,8 +3,9 @@
 
 One step = one pass of the prefill path on the Llama-3-8B single-layer
 workload (1 x 8192 tokens, 32 query / 8 KV heads, D = 128, bf16, a = 4,
-n = 256, separator probability 0.12): sep_mask_build -> sep_index_compact
--> sep_attn_prefill, inputs resident in HBM. The headline value is useful
+n = 256, separator probability 0.12): separator flags and their compaction
+(sep_mask_compact: sep_mask_build's flags and sep_index_compact in one
+launch) -> sep_attn_prefill, inputs resident in HBM. The headline value is useful
 TFLOP/s of that pass (useful FLOPs = 4 * D * visible (query, key) pairs,
 summed over query heads).
 
@@ -168,8 +169,9 @@ def bench_prefill(args, torch, sa, configs, gen):
     scale = 1.0 / math.sqrt(D)
 
     def step():
-        sa.sep_mask_build(ids, sep, cfg.a, cfg.n, is_sep=is_sep)
-        sa.sep_index_compact(is_sep, rank=rank, sep_pos=sep_pos, count=count)
+        # separator flags and their compaction (sep_mask_build's flags and
+        # sep_index_compact, fused in one launch), then the prefill
+        sa.sep_mask_compact(ids, sep, is_sep=is_sep, rank=rank, sep_pos=sep_pos, count=count)
         sa.sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, cfg.a, cfg.n, scale, out=out)
 
     for _ in range(args.warmup):
@@ -732,7 +734,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
                    "head_dim": cfg.D, "seq_len": cfg.S, "a": cfg.a, "n": cfg.n,
-                   "p_sep": cfg.p_sep, "step": "sep_mask_build+sep_index_compact+sep_attn_prefill"},
+                   "p_sep": cfg.p_sep, "step": "sep_mask_compact(flags+compaction)+sep_attn_prefill"},
         "roofline": {"kernel": "sep_attn_prefill", "bound": "mfma",
                      "achieved": round(res["tflops_kernel"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(res["tflops_kernel"] / PEAK_BF16_TFLOPS, 4),

@@ -106,6 +106,21 @@ int sep_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank, int32_
                       int32_t* count, hipStream_t stream);
 
 /*
+ * sep_mask_compact - the separator flags of sep_mask_build and the
+ * compaction of sep_index_compact in one launch (one workgroup per
+ * sequence), for callers that need no tile classes or dense mask.
+ * [as sep_mask_build and sep_index_compact]
+ *
+ *   ids [B, S] int32; sep_ids [n_sep_ids] int32 device array (0..64 ids).
+ *   is_sep [B, S] uint8 out; rank [B, S+1], sep_pos [B, S] int32 out; count
+ *   [B] int32 out or NULL: exactly what sep_mask_build (flags only) then
+ *   sep_index_compact write. ids, is_sep and rank 16-byte aligned.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_mask_compact(const int32_t* ids, int B, int S, const int32_t* sep_ids, int n_sep_ids, uint8_t* is_sep,
+                     int32_t* rank, int32_t* sep_pos, int32_t* count, hipStream_t stream);
+
+/*
  * sep_attn_prefill - Sep-Attention over a whole sequence.  [P2 §1.2 (scores
  * scaled, masked entries set to -inf, softmax, weighted sum of V); P1
  * "SepAttention" (initial OR window OR separator, AND causal); P1

@@ -23,7 +23,7 @@ import torch
 from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
-__all__ = ["sep_mask_build", "sep_index_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
+__all__ = ["sep_mask_build", "sep_index_compact", "sep_mask_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
            "sep_attn_decode", "sep_attn_decode_rope", "sep_rope_table", "sep_attn_prefill_chunk",
            "chunk_workspace_bytes",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
@@ -101,6 +101,24 @@ def sep_index_compact(is_sep, *, rank=None, sep_pos=None, count=None):
                                  count.data_ptr(), _stream())
     _lib.check("sep_index_compact", code)
     return rank, sep_pos, count
+
+
+def sep_mask_compact(ids, sep_ids, *, is_sep=None, rank=None, sep_pos=None, count=None):
+    """Flags and compaction in one launch: returns is_sep [B,S] u8, rank
+    [B,S+1] i32, sep_pos [B,S] i32, count [B] i32."""
+    lib = _lib.load()
+    _need(ids, "ids", torch.int32, 2)
+    _need(sep_ids, "sep_ids", torch.int32, 1)
+    B, S = ids.shape
+    dev = ids.device
+    is_sep = torch.empty((B, S), dtype=torch.uint8, device=dev) if is_sep is None else is_sep
+    rank = torch.empty((B, S + 1), dtype=torch.int32, device=dev) if rank is None else rank
+    sep_pos = torch.empty((B, S), dtype=torch.int32, device=dev) if sep_pos is None else sep_pos
+    count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
+    code = lib.sep_mask_compact(ids.data_ptr(), B, S, sep_ids.data_ptr(), sep_ids.numel(), is_sep.data_ptr(),
+                                rank.data_ptr(), sep_pos.data_ptr(), count.data_ptr(), _stream())
+    _lib.check("sep_mask_compact", code)
+    return is_sep, rank, sep_pos, count
 
 
 def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: float | None = None, *,

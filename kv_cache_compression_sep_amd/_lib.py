@@ -53,6 +53,7 @@ SIGNATURES = {
     "sep_cache_reset": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp]),
     "sep_cache_update": (c_int, [ctypes.POINTER(SepCacheStruct), c_vp, c_vp, c_vp, c_int, c_vp,
                                  c_int, c_vp]),
+    "sep_mask_compact": (c_int, [c_vp, c_int, c_int, c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "sep_chunk_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SepCacheStruct), c_int]),
     "sep_attn_prefill_chunk": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, ctypes.POINTER(SepCacheStruct),
                                        c_int, c_int, c_float, c_vp, ctypes.c_size_t, c_vp, c_vp, c_vp]),

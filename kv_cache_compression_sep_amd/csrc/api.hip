@@ -94,6 +94,16 @@ int sep_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank, int32_
   return hip_status(sep::launch_index_compact(is_sep, B, S, rank, sep_pos, count, stream));
 }
 
+int sep_mask_compact(const int32_t* ids, int B, int S, const int32_t* sep_ids, int n_sep_ids, uint8_t* is_sep,
+                     int32_t* rank, int32_t* sep_pos, int32_t* count, hipStream_t stream) {
+  if (ids == nullptr || is_sep == nullptr || rank == nullptr || sep_pos == nullptr) return SEP_ERR_NULL;
+  if (n_sep_ids < 0 || n_sep_ids > SEP_MAX_SEP_IDS) return SEP_ERR_SHAPE;
+  if (n_sep_ids > 0 && sep_ids == nullptr) return SEP_ERR_NULL;
+  if (B <= 0 || S <= 0) return SEP_ERR_SHAPE;
+  if (!aligned16(ids) || !aligned16(is_sep) || !aligned16(rank)) return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_mask_compact(ids, B, S, sep_ids, n_sep_ids, is_sep, rank, sep_pos, count, stream));
+}
+
 int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv,
                      int S, int D, const uint8_t* is_sep, const int32_t* rank,
                      const int32_t* sep_pos, int a, int n, float scale, void* out, float* lse,

@@ -7,6 +7,7 @@
 // 4096 flags (4 per thread). Inside a wave, the per-thread counts (0..4) are
 // prefix-summed with three ballots and mbcnt (one per bit of the count);
 // the 16 wave totals go through LDS. A running carry links the chunks.
+// mask_compact_kernel does the same walk from token ids.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -69,6 +70,96 @@ __global__ void __launch_bounds__(kCompactThreads)
     rk[S] = carry;
     if (count) count[b] = carry;
   }
+}
+
+// sep_mask_compact: the flags of sep_mask_build and the compaction above in
+// one launch. Same walk as compact_kernel; each thread reads its 4 ids (one
+// 16-byte load when the rows allow it), tests them against the separator
+// set in LDS, writes the 4 flags and then their ranks as one 16-byte store.
+__global__ void __launch_bounds__(kCompactThreads)
+    mask_compact_kernel(const int32_t* __restrict__ ids, int S, const int32_t* __restrict__ sep_ids, int n_sep,
+                        uint8_t* __restrict__ is_sep, int32_t* __restrict__ rank,
+                        int32_t* __restrict__ sep_pos, int32_t* __restrict__ count) {
+  __shared__ int32_t wave_tot[2][kCompactWaves];
+  __shared__ int32_t set[SEP_MAX_SEP_IDS];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave;
+  for (int i = tid; i < n_sep; i += kCompactThreads) set[i] = sep_ids[i];
+  __syncthreads();
+  const int32_t* id = ids + static_cast<int64_t>(b) * S;
+  uint8_t* f = is_sep + static_cast<int64_t>(b) * S;
+  int32_t* rk = rank + static_cast<int64_t>(b) * (S + 1);
+  int32_t* sp = sep_pos + static_cast<int64_t>(b) * S;
+  const bool vec = (S % 4) == 0;                  // rows of whole 16-byte groups (ids, rank)
+  int carry = 0;
+  int parity = 0;
+  for (int base = 0; base < S; base += 4 * kCompactThreads, parity ^= 1) {
+    const int j0 = base + 4 * tid;
+    int fl[4];
+    if (vec && j0 + 4 <= S) {
+      const int4 v = *reinterpret_cast<const int4*>(id + j0);
+      fl[0] = in_set(v.x, set, n_sep);
+      fl[1] = in_set(v.y, set, n_sep);
+      fl[2] = in_set(v.z, set, n_sep);
+      fl[3] = in_set(v.w, set, n_sep);
+      *reinterpret_cast<uchar4*>(f + j0) = make_uchar4(fl[0], fl[1], fl[2], fl[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fl[e] = (j0 + e < S) ? in_set(id[j0 + e], set, n_sep) : 0;
+        if (j0 + e < S) f[j0 + e] = static_cast<uint8_t>(fl[e]);
+      }
+    }
+    const int c = fl[0] + fl[1] + fl[2] + fl[3];
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+      const uint64_t m = ballot((c >> bit) & 1);
+      pre += static_cast<int>(mbcnt(m)) << bit;
+      tot += __popcll(m) << bit;
+    }
+    if ((tid % kWave) == 0) wave_tot[parity][wid] = tot;
+    __syncthreads();
+    int before = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < kCompactWaves; ++w) {
+      const int t = wave_tot[parity][w];
+      before += (w < wid) ? t : 0;
+      chunk += t;
+    }
+    const int r = carry + before + pre;
+    int rr[4];
+    rr[0] = r;
+    rr[1] = r + fl[0];
+    rr[2] = rr[1] + fl[1];
+    rr[3] = rr[2] + fl[2];
+    // rank rows start at b (S + 1): 16-byte aligned only when b (S + 1) % 4 == 0
+    if (vec && j0 + 4 <= S && ((static_cast<int64_t>(b) * (S + 1)) % 4) == 0) {
+      *reinterpret_cast<int4*>(rk + j0) = make_int4(rr[0], rr[1], rr[2], rr[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < S) rk[j0 + e] = rr[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j0 + e < S && fl[e]) sp[rr[e]] = j0 + e;
+    carry += chunk;
+  }
+  for (int j = carry + tid; j < S; j += kCompactThreads) sp[j] = -1;
+  if (tid == 0) {
+    rk[S] = carry;
+    if (count) count[b] = carry;
+  }
+}
+
+hipError_t launch_mask_compact(const int32_t* ids, int B, int S, const int32_t* sep_ids, int n_sep,
+                               uint8_t* is_sep, int32_t* rank, int32_t* sep_pos, int32_t* count,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(mask_compact_kernel, dim3(B), dim3(kCompactThreads), 0, st, ids, S, sep_ids, n_sep, is_sep,
+                     rank, sep_pos, count);
+  return hipGetLastError();
 }
 
 hipError_t launch_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank,

@@ -27,6 +27,8 @@ hipError_t launch_dense_mask(const uint8_t* is_sep, int B, int S, int a, int n, 
                              hipStream_t st);
 hipError_t launch_index_compact(const uint8_t* is_sep, int B, int S, int32_t* rank,
                                 int32_t* sep_pos, int32_t* count, hipStream_t st);
+hipError_t launch_mask_compact(const int32_t* ids, int B, int S, const int32_t* sep_ids, int n_sep,
+                               uint8_t* is_sep, int32_t* rank, int32_t* sep_pos, int32_t* count, hipStream_t st);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int dtype, int B, int Hq,
                           int Hkv, int S, int D, const uint8_t* is_sep, const int32_t* rank,
                           const int32_t* sep_pos, int a, int n, float scale, void* out, float* lse,

@@ -183,6 +183,18 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   const int h = g * P.G + hg * P.HPW + hw;
   const int qw0 = q0 + 32 * rb;                        // this wave's first query row
 
+  // ---- Q fragments first: their loads are in flight while rank is read
+  //      and the first index slices land
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(P.q) + static_cast<int64_t>(b * P.Hq + h) * S * D;
+  bf16x8 qf[KS];
+  {
+    const int qrow = min(qw0 + lane % 32, S - 1);
+    const uint16_t* p = qb + static_cast<int64_t>(qrow) * D + 8 * (lane / 32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 16 * ks));
+  }
+
   const int32_t* rk = P.rank + static_cast<int64_t>(b) * (Skv + 1);
   const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * Skv;
   const int key_lo = P.key_lo == nullptr ? 0 : P.key_lo[b];
@@ -190,7 +202,6 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
 
   const char* kb = reinterpret_cast<const char*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * Skv * D * 2;
   const char* vb = reinterpret_cast<const char*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * Skv * D * 2;
-  const uint16_t* qb = reinterpret_cast<const uint16_t*>(P.q) + static_cast<int64_t>(b * P.Hq + h) * S * D;
 
   // ---- index slice of tile t into ring slot t % IDXR: wave 0 loads
   //      sep_pos entries (global tiles) or rank[jmin + u]; wave 1 loads
@@ -252,15 +263,6 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   char* const kring = ring;
   char* const vring = ring + KSTAGES * TB;
 
-  // ---- Q fragments first, so that waiting for them never waits for tiles
-  bf16x8 qf[KS];
-  {
-    const int qrow = min(qw0 + lane % 32, S - 1);
-    const uint16_t* p = qb + static_cast<int64_t>(qrow) * D + 8 * (lane / 32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 16 * ks));
-  }
   for (int t = 0; t < IAHEAD; ++t) issue_index(t);
   compiler_fence();
   __builtin_amdgcn_s_waitcnt(0);                       // index slices 0..6 landed

@@ -229,3 +229,16 @@ def test_chunk_argument_checks(lib):
     assert ch(c, ws=(1 << 20) + 16) == E.SEP_ERR_WORKSPACE
     assert ch(c, q=FAKE + 2) == E.SEP_ERR_ALIGN
     assert ch(_cache(dtype=0)) == E.SEP_ERR_DTYPE
+
+
+def test_mask_compact_argument_checks(lib):
+    E = _lib
+    f = lambda **kw: lib.sep_mask_compact(kw.get("ids", FAKE), kw.get("B", 1), kw.get("S", 64), FAKE,
+                                          kw.get("nsep", 4), kw.get("flags", FAKE), kw.get("rank", FAKE), FAKE,
+                                          None, None)
+    assert f(ids=None) == E.SEP_ERR_NULL
+    assert f(rank=None) == E.SEP_ERR_NULL
+    assert f(S=0) == E.SEP_ERR_SHAPE
+    assert f(nsep=65) == E.SEP_ERR_SHAPE
+    assert f(flags=FAKE + 1) == E.SEP_ERR_ALIGN
+    assert f(ids=FAKE + 4) == E.SEP_ERR_ALIGN

@@ -4,6 +4,8 @@ Integer outputs must match bit for bit: separator flags, tile classes, the
 dense mask, ranks, compacted positions and counts. Cases: the three prefill
 workloads at full size (1 x 512, 1 x 8192, 1 x 131072 tokens) plus small and
 ragged shapes, all-separator, no-separator and single-token sequences.
+sep_mask_compact (flags and compaction in one launch) must write exactly
+the same four arrays.
 """
 import numpy as np
 import pytest
@@ -11,7 +13,7 @@ import torch
 
 import oracle
 from inputs import configs, gen
-from kv_cache_compression_sep_amd import sep_index_compact, sep_mask_build
+from kv_cache_compression_sep_amd import sep_index_compact, sep_mask_build, sep_mask_compact
 
 from .gpu_util import to_dev
 
@@ -98,3 +100,35 @@ def test_long_prefill_workload_flags_ranks_sampled_tiles():
     sample = sorted(set([0, 1, 2, 3, nqt - 2, nqt - 1] + rng.integers(0, nqt, 24).tolist()))
     _check_flags_tiles_compact(_ids_for(cfg), cfg.sep_ids, cfg.a, cfg.n, tiles=((64, 64),),
                                dense=False, qtile_sample=sample)
+
+
+def _check_fused(ids, sep_ids):
+    B, S = ids.shape
+    flags, rank, sep_pos, count = sep_mask_compact(to_dev(ids), to_dev(np.asarray(sep_ids, np.int32)))
+    torch.cuda.synchronize()
+    f_h, r_h, p_h, c_h = flags.cpu().numpy(), rank.cpu().numpy(), sep_pos.cpu().numpy(), count.cpu().numpy()
+    for b in range(B):
+        f_ref = oracle.is_sep(ids[b], sep_ids)
+        r_ref, p_ref, c_ref = oracle.compact(f_ref)
+        assert np.array_equal(f_h[b], f_ref.astype(np.uint8)), (S, b)
+        assert np.array_equal(r_h[b], r_ref), (S, b)
+        assert np.array_equal(p_h[b], p_ref), (S, b)
+        assert c_h[b] == c_ref
+
+
+def test_fused_mask_compact_small_and_ragged():
+    """Rows of S % 4 != 0 (scalar path), S % 4 == 0 with rank rows that are
+    or are not 16-byte aligned (B > 1), more than one 4096-flag chunk."""
+    for ids, _, _ in _small_cases():
+        _check_fused(ids, list(range(8)))
+    rng = np.random.default_rng(507)
+    for B, S in ((3, 8), (2, 4096), (4, 12288), (3, 4100)):
+        ids = np.where(rng.random((B, S)) < 0.2, rng.integers(0, 8, (B, S)),
+                       rng.integers(8, 1000, (B, S))).astype(np.int32)
+        _check_fused(ids, list(range(8)))
+    _check_fused(rng.integers(0, 20, (2, 333)).astype(np.int32), [])
+
+
+def test_fused_mask_compact_workloads():
+    for cfg in (configs.LLAMA3_LAYER_PREFILL, configs.LONG_PREFILL):
+        _check_fused(_ids_for(cfg), cfg.sep_ids)
