@@ -21,7 +21,11 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsepattn.so")
 SOURCES = ["api.hip", "mask.hip", "compact.hip", "prefill.hip", "prefill_bf16.hip", "prefill_bwd.hip",
-           "cache.hip", "decode.hip", "chunk.hip"]
+           "prefill_bwd_bf16.hip", "cache.hip", "decode.hip", "chunk.hip"]
+# Per-source code generation: the bf16 backward kernels keep their MFMA
+# accumulators in VGPRs (with AGPRs as the accumulators the compiler copies
+# them between the two files every tile).
+EXTRA_FLAGS = {"prefill_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = os.environ.get("SEPATTN_ARCH", "gfx950")
 
 FLAGS = [
@@ -50,7 +54,7 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
