@@ -260,17 +260,24 @@ __device__ __forceinline__ void kv_tile_bf16(const char* Qs, const char* Os, con
     sc = mfma32x32x16(row_operand<D>(Qs, lane % 32, ks, lane), kf[ks], sc);
     dp = mfma32x32x16(row_operand<D>(Os, lane % 32, ks, lane), vf[ks], dp);
   }
-  float p[16], ds[16];
+  // P and dS straight into bf16 pairs (the B operands), element r of the
+  // accumulator in word r / 2
+  u32x4 wp[2], wds[2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int il = 8 * (r / 4) + 4 * hsel + (r % 4);    // query row of element r
-    const float pv = visible(il) ? fast_exp2(__builtin_fmaf(sc[r], scale_log2, -lse[il] * kLog2e)) : 0.0f;
-    p[r] = pv;
-    ds[r] = pv * (dp[r] - dlt[il]);
+  for (int r = 0; r < 16; r += 2) {
+    float pv[2], dv2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int il = 8 * ((r + e) / 4) + 4 * hsel + ((r + e) % 4);   // query row of element r + e
+      pv[e] = visible(il) ? fast_exp2(__builtin_fmaf(sc[r + e], scale_log2, -lse[il] * kLog2e)) : 0.0f;
+      dv2[e] = pv[e] * (dp[r + e] - dlt[il]);
+    }
+    wp[r / 8][(r % 8) / 2] = pack_bf16x2(pv[0], pv[1]);
+    wds[r / 8][(r % 8) / 2] = pack_bf16x2(dv2[0], dv2[1]);
   }
 #pragma unroll
   for (int kcl = 0; kcl < 2; ++kcl) {
-    const bf16x8 bp = pack8(p + 8 * kcl), bds = pack8(ds + 8 * kcl);
+    const bf16x8 bp = __builtin_bit_cast(bf16x8, wp[kcl]), bds = __builtin_bit_cast(bf16x8, wds[kcl]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       dv[db] = mfma32x32x16(tr_operand<D>(Os, toff[db], kcl), bp, dv[db]);
