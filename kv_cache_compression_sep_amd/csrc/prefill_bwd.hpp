@@ -39,14 +39,15 @@ struct BwdArgs {
 };
 
 // Per-chunk tile counts of the global keys (ceil(n_global(chunk end) / KB))
-// as an exclusive prefix in tstart[0 .. n_qc]; returns the total. Every
-// thread of the workgroup calls it (two barriers).
-template <class NGlobal>
+// as an exclusive prefix in tstart[0 .. n_qc]; returns the total. Every one
+// of the NT threads of the workgroup calls it (two barriers); wsum holds
+// NT / 64 entries.
+template <int NT = BT, class NGlobal>
 __device__ int chunk_tile_prefix(NGlobal n_global, int S, int n_qc, int32_t* tstart, int32_t* wsum) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  const int seg = (n_qc + BT - 1) / BT;
+  const int seg = (n_qc + NT - 1) / NT;
   const int cb = min(tid * seg, n_qc);
   const int ce = min(cb + seg, n_qc);
   int local = 0;
@@ -70,7 +71,7 @@ __device__ int chunk_tile_prefix(NGlobal n_global, int S, int n_qc, int32_t* tst
     tstart[c] = run;
     run += nt;
   }
-  if (tid == BT - 1) tstart[n_qc] = run;          // the last thread's running sum is the total
+  if (tid == NT - 1) tstart[n_qc] = run;          // the last thread's running sum is the total
   __syncthreads();
   return tstart[n_qc];
 }

@@ -244,15 +244,28 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
 }
 
 // ---------------------------------------------------------------- dK, dV (bf16)
+// A workgroup holds 128 keys in 4 groups of 32 and splits d into D / 64
+// halves: wave w takes key group w % 4 and d columns [64 (w / 4), +64), so
+// that its dK and dV accumulators (32 keys x 64 d each) leave room for two
+// waves per SIMD. The scores need all of d, so the waves of one key group
+// compute S and dP alike.
+template <int D>
+struct KVGeo {
+  static constexpr int DSPLIT = D / 64;           // d halves
+  static constexpr int NWAVE = 4 * DSPLIT;
+  static constexpr int NTH = NWAVE * kWave;
+};
+
 // One query tile (32 rows of Q and dO, staged in LDS) against this wave's 32
 // keys (K^T and V^T fragments in registers): S = Q K^T and dP = dO V^T put
-// one key per lane; then dV^T += dO^T P and dK^T += Q^T dS over the 32 rows.
+// one key per lane; then dV^T += dO^T P and dK^T += Q^T dS over the 32 rows,
+// for the wave's two 32-column d blocks (transpose offsets toff).
 template <int D, class Vis>
 __device__ __forceinline__ void kv_tile_bf16(const char* Qs, const char* Os, const float* lse, const float* dlt,
                                              const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
-                                             const int (&toff)[D / 32][2], float scale_log2, int lane, Vis visible,
-                                             f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
-  constexpr int KS = D / 16, DB = D / 32;
+                                             const int (&toff)[2][2], float scale_log2, int lane, Vis visible,
+                                             f32x16 (&dk)[2], f32x16 (&dv)[2]) {
+  constexpr int KS = D / 16;
   const int hsel = lane / 32;
   f32x16 sc = {}, dp = {};
 #pragma unroll
@@ -279,7 +292,7 @@ __device__ __forceinline__ void kv_tile_bf16(const char* Qs, const char* Os, con
   for (int kcl = 0; kcl < 2; ++kcl) {
     const bf16x8 bp = __builtin_bit_cast(bf16x8, wp[kcl]), bds = __builtin_bit_cast(bf16x8, wds[kcl]);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < 2; ++db) {
       dv[db] = mfma32x32x16(tr_operand<D>(Os, toff[db], kcl), bp, dv[db]);
       dk[db] = mfma32x32x16(tr_operand<D>(Qs, toff[db], kcl), bds, dk[db]);
     }
@@ -318,11 +331,11 @@ __device__ __forceinline__ void bw_dma4(const void* base, uint32_t off, uint32_t
                :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
 
-template <int D>
+template <int D, int NW>
 struct QRing {
   static constexpr int CPR = BGeo<D>::CPR;
   static constexpr int TB = QB * D * 2;           // bytes of a 32-row Q (or dO) tile
-  static constexpr int PERW = TB / 1024 / BW;     // 1 KB DMA instructions per wave per tensor
+  static constexpr int PERW = TB / 1024 / NW;     // 1 KB DMA instructions per wave per tensor
   static constexpr int OPS = 2 * PERW + 2;        // + one dword op each for lse and delta
   static constexpr int NST = 4;
   static constexpr int AHEAD = NST - 1;
@@ -330,7 +343,7 @@ struct QRing {
   static constexpr int BYTES = NST * STAGE;
   static_assert(PERW >= 1, "tile too small for the wave count");
   char* ring;                                     // NST x [Q | dO | lse (64) | delta (64)]
-  char* junk;                                     // BW x 1 KB, targets of dummy ops
+  char* junk;                                     // NW x 1 KB, targets of dummy ops
   __device__ char* q(int t) const { return ring + (t % NST) * STAGE; }
   __device__ char* o(int t) const { return q(t) + TB; }
   __device__ float* l(int t) const { return reinterpret_cast<float*>(q(t) + 2 * TB); }
@@ -363,10 +376,9 @@ struct QRing {
 // Every global load and store of the workgroup issued before the call must
 // be complete or unrelated to vmcnt ordering: the call starts with a full
 // wait.
-template <int D, class TileOf, class Compute>
-__device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const QRing<D>& R, int nt, TileOf tile,
+template <class RG, class TileOf, class Compute>
+__device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R, int nt, TileOf tile,
                                                    Compute compute) {
-  using RG = QRing<D>;
   bw_fence();
   __builtin_amdgcn_s_waitcnt(0);
   bw_fence();
@@ -410,14 +422,28 @@ __device__ __forceinline__ void load_key_bf16(const uint16_t* kb, const uint16_t
   }
 }
 
+// This lane's transpose offsets for the two d blocks of d half dh.
 template <int D>
-__global__ void __launch_bounds__(BT, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_kt) {
-  constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char ringmem[QRing<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char junkmem[BW * 1024];
-  const QRing<D> R{ringmem, junkmem};
+__device__ __forceinline__ void half_offsets(int lane, int dh, int (&toff)[2][2]) {
+  int all[D / 32][2];
+  tr_offsets<D>(lane, all);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) toff[db][e] = all[2 * dh + db][e];
+}
+
+template <int D>
+__global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_kt) {
+  using KG = KVGeo<D>;
+  using Ring = QRing<D, KG::NWAVE>;
+  __shared__ __attribute__((aligned(1024))) char ringmem[Ring::BYTES];
+  __shared__ __attribute__((aligned(1024))) char junkmem[KG::NWAVE * 1024];
+  const Ring R{ringmem, junkmem};
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
+  const int kg = wave % 4;                        // key group
+  const int dh = wave / 4;                        // d half
   const int hsel = lane / 32;
   const int kt = blockIdx.x % n_kt;
   const int bgi = blockIdx.x / n_kt;
@@ -425,7 +451,7 @@ __global__ void __launch_bounds__(BT, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_
   const int b = bgi / P.Hkv;
   const int S = P.S;
   const int j0 = kt * KB;
-  const int j = j0 + 32 * wave + lane % 32;
+  const int j = j0 + 32 * kg + lane % 32;
   const int jc = min(j, S - 1);
   const uint8_t* fl = P.is_sep + static_cast<int64_t>(b) * S;
   const bool own = j < S && j >= P.a && fl[jc] == 0;    // initial and separator keys: dkdv_glob
@@ -433,11 +459,11 @@ __global__ void __launch_bounds__(BT, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   bf16x8 kf[D / 16], vf[D / 16];
   load_key_bf16<D>(kb, vb, jc, lane, kf, vf);
-  int toff[DB][2];
-  tr_offsets<D>(lane, toff);
-  f32x16 dk[DB], dv[DB];
+  int toff[2][2];
+  half_offsets<D>(lane, dh, toff);
+  f32x16 dk[2], dv[2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < 2; ++db) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
   }
@@ -446,12 +472,12 @@ __global__ void __launch_bounds__(BT, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_
   const int qend = static_cast<int>(qend64 < S ? qend64 : S);
   const int ntq = (qend - j0 + QB - 1) / QB;
   const int nt = P.G * ntq;
-  const int wj0 = j0 + 32 * wave;
+  const int wj0 = j0 + 32 * kg;
   auto tile = [&](int t, int64_t* hrow, int* qt0) {
     *hrow = static_cast<int64_t>(b * P.Hq + g * P.G + t / ntq) * S;
     *qt0 = j0 + (t % ntq) * QB;
   };
-  stream_query_tiles<D>(P, R, nt, tile, [&](int t) {
+  stream_query_tiles(P, R, nt, tile, [&](int t) {
     const int qt0 = j0 + (t % ntq) * QB;
     if (qt0 + QB - 1 < wj0 || static_cast<int64_t>(qt0) > static_cast<int64_t>(wj0) + 31 + P.n - 1) return;
     kv_tile_bf16<D>(R.q(t), R.o(t), R.l(t), R.d(t), kf, vf, toff, P.scale_log2, lane,
@@ -465,10 +491,10 @@ __global__ void __launch_bounds__(BT, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_
     float* dkr = P.dk + (static_cast<int64_t>(b * P.Hkv + g) * S + j) * D;
     float* dvr = P.dv + (static_cast<int64_t>(b * P.Hkv + g) * S + j) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int d = 32 * db + 8 * q + 4 * hsel;
+        const int d = 64 * dh + 32 * db + 8 * q + 4 * hsel;
         *reinterpret_cast<f32x4*>(dkr + d) = f32x4{dk[db][4 * q] * P.scale, dk[db][4 * q + 1] * P.scale,
                                                    dk[db][4 * q + 2] * P.scale, dk[db][4 * q + 3] * P.scale};
         *reinterpret_cast<f32x4*>(dvr + d) = f32x4{dv[db][4 * q], dv[db][4 * q + 1], dv[db][4 * q + 2],
@@ -478,20 +504,23 @@ __global__ void __launch_bounds__(BT, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_
 }
 
 template <int D>
-__global__ void __launch_bounds__(BT, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_qc, int nslots) {
-  constexpr int DB = D / 32;
-  static_assert(BW * 32 * D * 4 <= QRing<D>::BYTES, "the flush buffer aliases the ring");
-  __shared__ __attribute__((aligned(1024))) char ringmem[QRing<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char junkmem[BW * 1024];
+__global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_qc, int nslots) {
+  using KG = KVGeo<D>;
+  using Ring = QRing<D, KG::NWAVE>;
+  static_assert(KG::NWAVE * 32 * 64 * 4 <= Ring::BYTES, "the flush buffer aliases the ring");
+  __shared__ __attribute__((aligned(1024))) char ringmem[Ring::BYTES];
+  __shared__ __attribute__((aligned(1024))) char junkmem[KG::NWAVE * 1024];
   __shared__ int32_t kpos[KB];
   __shared__ int32_t tstart[kMaxChunks + 1];
-  __shared__ int32_t wsum[BW];
-  const QRing<D> R{ringmem, junkmem};
-  // one wave's partial dK or dV, key-major, column d ^ row: [BW][32][D]
+  __shared__ int32_t wsum[KG::NWAVE];
+  const Ring R{ringmem, junkmem};
+  // one wave's partial dK or dV, key-major, column (d - 64 dh) ^ row: [NWAVE][32][64]
   float* red = reinterpret_cast<float*>(ringmem);
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
+  const int kg = wave % 4;
+  const int dh = wave / 4;
   const int hsel = lane / 32;
   const int BH = P.B * P.Hkv;
   const int bgi = blockIdx.x % BH;
@@ -504,14 +533,14 @@ __global__ void __launch_bounds__(BT, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_
   const int ninit = min(P.a, S);
   const int rank_a = rk[ninit];
   auto n_global = [&](int c1) { return min(ninit, c1) + (c1 > ninit ? rk[c1] - rank_a : 0); };
-  const int total = chunk_tile_prefix(n_global, S, n_qc, tstart, wsum);
+  const int total = chunk_tile_prefix<KG::NTH>(n_global, S, n_qc, tstart, wsum);
 
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   float* dkb = P.dk + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   float* dvb = P.dv + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  int toff[DB][2];
-  tr_offsets<D>(lane, toff);
+  int toff[2][2];
+  half_offsets<D>(lane, dh, toff);
 
   for (int w = slot; w < total; w += nslots) {
     const int qc = chunk_of(tstart, n_qc, w);
@@ -521,22 +550,22 @@ __global__ void __launch_bounds__(BT, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_
     const int n_in = min(ninit, c1);
     const int n_gl = n_global(c1);
     __syncthreads();                              // kpos and the tiles of the previous item are consumed
-    for (int u = tid; u < KB; u += BT) {
+    for (int u = tid; u < KB; u += KG::NTH) {
       const int uu = u0 + u;
       kpos[u] = uu >= n_gl ? -1 : (uu < n_in ? uu : sp[rank_a + (uu - n_in)]);
     }
     __syncthreads();
-    const int j = kpos[32 * wave + lane % 32];    // this lane's key, -1 past the list
+    const int j = kpos[32 * kg + lane % 32];      // this lane's key, -1 past the list
     bf16x8 kf[D / 16], vf[D / 16];
     load_key_bf16<D>(kb, vb, j < 0 ? 0 : j, lane, kf, vf);
-    f32x16 dk[DB], dv[DB];
+    f32x16 dk[2], dv[2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < 2; ++db) {
       dk[db] = f32x16{};
       dv[db] = f32x16{};
     }
     const int jlo = kpos[0];
-    const int wlo = kpos[32 * wave];
+    const int wlo = kpos[32 * kg];
     const int qs0 = max(c0, jlo) / QB * QB;
     const int ntq = (c1 - qs0 + QB - 1) / QB;
     const int nt = P.G * ntq;
@@ -544,7 +573,7 @@ __global__ void __launch_bounds__(BT, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_
       *hrow = static_cast<int64_t>(b * P.Hq + g * P.G + t / ntq) * S;
       *qt0 = qs0 + (t % ntq) * QB;
     };
-    stream_query_tiles<D>(P, R, nt, tile, [&](int t) {
+    stream_query_tiles(P, R, nt, tile, [&](int t) {
       const int qt0 = qs0 + (t % ntq) * QB;
       if (wlo < 0 || qt0 + QB - 1 < wlo) return;
       kv_tile_bf16<D>(R.q(t), R.o(t), R.l(t), R.d(t), kf, vf, toff, P.scale_log2, lane,
@@ -560,23 +589,23 @@ __global__ void __launch_bounds__(BT, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int d = 32 * db + 8 * (r / 4) + 4 * hsel + (r % 4);
-          red[(wave * 32 + lane % 32) * D + (d ^ (lane % 32))] = which == 0 ? dk[db][r] * P.scale : dv[db][r];
+          const int dl = 32 * db + 8 * (r / 4) + 4 * hsel + (r % 4);       // column within the half
+          red[(wave * 32 + lane % 32) * 64 + (dl ^ (lane % 32))] = which == 0 ? dk[db][r] * P.scale : dv[db][r];
         }
       __syncthreads();
       float* dst = which == 0 ? dkb : dvb;
 #pragma unroll 4
       for (int pass = 0; pass < 16; ++pass) {
         const int row = 2 * pass + lane / 32;
-        const int jr = kpos[32 * wave + row];
+        const int jr = kpos[32 * kg + row];
         if (jr >= 0) {
 #pragma unroll
-          for (int e = 0; e < D / 32; ++e)
-            atomicAdd(dst + static_cast<int64_t>(jr) * D + 32 * e + lane % 32,
-                      red[(wave * 32 + row) * D + ((32 * e + lane % 32) ^ row)]);
+          for (int e = 0; e < 2; ++e)
+            atomicAdd(dst + static_cast<int64_t>(jr) * D + 64 * dh + 32 * e + lane % 32,
+                      red[(wave * 32 + row) * 64 + ((32 * e + lane % 32) ^ row)]);
         }
       }
       __syncthreads();
@@ -593,12 +622,16 @@ hipError_t launch_bf16_kernels(const BwdArgs& A, int D, hipStream_t st) {
   const int nslots = BH >= 512 ? 1 : 512 / BH;   // twice the resident workgroups on 256 CUs
   if (D == 128) {
     hipLaunchKernelGGL((dq_bf16_kernel<128>), dim3(A.B * A.Hkv * A.n_hg * A.n_qt), dim3(BT), 0, st, A);
-    hipLaunchKernelGGL((dkdv_band_bf16_kernel<128>), dim3(A.B * A.Hkv * n_kt), dim3(BT), 0, st, A, n_kt);
-    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<128>), dim3(BH * nslots), dim3(BT), 0, st, A, n_qc, nslots);
+    hipLaunchKernelGGL((dkdv_band_bf16_kernel<128>), dim3(A.B * A.Hkv * n_kt), dim3(KVGeo<128>::NTH), 0, st, A,
+                       n_kt);
+    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<128>), dim3(BH * nslots), dim3(KVGeo<128>::NTH), 0, st, A, n_qc,
+                       nslots);
   } else {
     hipLaunchKernelGGL((dq_bf16_kernel<64>), dim3(A.B * A.Hkv * A.n_hg * A.n_qt), dim3(BT), 0, st, A);
-    hipLaunchKernelGGL((dkdv_band_bf16_kernel<64>), dim3(A.B * A.Hkv * n_kt), dim3(BT), 0, st, A, n_kt);
-    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<64>), dim3(BH * nslots), dim3(BT), 0, st, A, n_qc, nslots);
+    hipLaunchKernelGGL((dkdv_band_bf16_kernel<64>), dim3(A.B * A.Hkv * n_kt), dim3(KVGeo<64>::NTH), 0, st, A,
+                       n_kt);
+    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<64>), dim3(BH * nslots), dim3(KVGeo<64>::NTH), 0, st, A, n_qc,
+                       nslots);
   }
   return hipGetLastError();
 }
