@@ -15,9 +15,10 @@
 // distinct banks. The data a tile's gather needs (its slice of sep_pos, or
 // for band tiles two shifted slices of rank whose difference gives the
 // separator bits) also arrives by LDS-DMA, seven tiles ahead, into an index
-// ring; the key rows of tile t + 4 are read from it in iteration t, one
-// iteration before their loads are issued, so that no load address waits
-// for LDS. So the key loop has no global load with a register result: every
+// ring; the gather entries of tile t + 4 are read from it in iteration t,
+// one iteration before its rows are formed and its loads issued, so that no
+// load address waits for LDS (LDS destinations are plain 32-bit offsets,
+// computed on the scalar unit). So the key loop has no global load with a register result: every
 // wait is explicit. Each wave issues exactly 1 + OPS loads per iteration (a
 // fixed dummy address past the last tile), waits with one exact vmcnt for
 // its own loads of K(t) and V(t - 1), and a plain barrier publishes them.
@@ -212,23 +213,30 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     const bool band = t >= ti.ntg;
     const int32_t* base = rk;                          // fixed dummy address
     uint32_t off = 0;
-    uint32_t dst = lds_addr(junk[wave]);
+    // LDS addresses as 32-bit integers (no generic-pointer arithmetic)
+    uint32_t dst = lds_addr(junk) + 4u * KT * wave;
     if (real && wave < 2) {
       if (!band) {
         if (wave == 0) {
           base = sp;
           off = 4u * min(max(ti.rank_a + t * KT + lane - ti.n_init, 0), Skv - 1);
-          dst = lds_addr(idxr[t % IDXR][0]);
+          dst = lds_addr(idxr) + 4u * KT * 2 * (t % IDXR);
         }
       } else {
         off = 4u * min(ti.band_lo + (t - ti.ntg) * KT + lane + wave, Skv);
-        dst = lds_addr(idxr[t % IDXR][wave]);
+        dst = lds_addr(idxr) + 4u * KT * (2 * (t % IDXR) + wave);
       }
     }
-    dma_x1(base, off, __builtin_amdgcn_readfirstlane(dst));
+    dma_x1(base, off, dst);
+  };
+  // the sep_pos entries this lane's rows of tile t would gather, from the
+  // tile's index slice (read for every tile, used for gathered ones)
+  auto read_gather = [&](int t, int (&g)[PW]) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) g[i] = idxr[t % IDXR][0][((wave * PW + i) * kWave + lane) / CPR];
   };
   // key rows this lane copies for tile t (row 0 past the last tile)
-  auto rows_of = [&](int t, int (&rows)[PW]) {
+  auto rows_from = [&](int t, const int (&g)[PW], int (&rows)[PW]) {
     const bool real = t < ti.ntiles;
     const bool band = t >= ti.ntg;
 #pragma unroll
@@ -239,16 +247,19 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
         key = min(ti.band_lo + (t - ti.ntg) * KT + r, Skv - 1);
       } else {
         const int u = t * KT + r;
-        int gathered = idxr[t % IDXR][0][r];
-        asm volatile("" : "+v"(gathered));             // read it unconditionally (no branch)
-        key = u < ti.n_init ? u : (u >= ti.n_glob ? 0 : gathered);
+        key = u < ti.n_init ? u : (u >= ti.n_glob ? 0 : g[i]);
       }
       rows[i] = real ? key : 0;
     }
   };
+  auto rows_of = [&](int t, int (&rows)[PW]) {
+    int g[PW];
+    read_gather(t, g);
+    rows_from(t, g, rows);
+  };
   // ---- LDS-DMA of the K (or V) rows of tile t into its ring stage
-  auto issue_rows = [&](const char* base, char* stage0, int t, const int (&rows)[PW], auto is_v) {
-    char* st = stage0 + (t % (decltype(is_v)::value ? VSTAGES : KSTAGES)) * TB;
+  auto issue_rows = [&](const char* base, uint32_t stage0, int t, const int (&rows)[PW], auto is_v) {
+    const uint32_t st = stage0 + (t % (decltype(is_v)::value ? VSTAGES : KSTAGES)) * TB;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int ins = wave * PW + i;                   // 1 KB block of the tile
@@ -257,28 +268,33 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       const int pos = sl % CPR;
       const int c = pos ^ (decltype(is_v)::value ? G::swz_v(r) : G::swz_k(r));   // chunk for that slot
       const uint32_t off = static_cast<uint32_t>(rows[i]) * (D * 2) + 16u * c;
-      dma_x4(base, off, __builtin_amdgcn_readfirstlane(lds_addr(st + ins * 1024)));
+      dma_x4(base, off, st + ins * 1024);
     }
   };
   char* const kring = ring;
   char* const vring = ring + KSTAGES * TB;
+  const uint32_t kring_lds = lds_addr(ring);
+  const uint32_t vring_lds = kring_lds + KSTAGES * TB;
 
   for (int t = 0; t < IAHEAD; ++t) issue_index(t);
   compiler_fence();
   __builtin_amdgcn_s_waitcnt(0);                       // index slices 0..6 landed
   __syncthreads();
-  int vrows[PW], knext[PW];                            // key rows of V(t + 2) and K(t + 3)
+  // key rows of V(t + 2), and the gather entries of tile t + 3, read one
+  // iteration before the rows are needed so that no LDS read is waited for
+  // in the load issue
+  int vrows[PW], graw[PW];
   {
     int r0[PW], r1[PW];
     rows_of(0, r0);
-    issue_rows(kb, kring, 0, r0, flag<false>{});
+    issue_rows(kb, kring_lds, 0, r0, flag<false>{});
     rows_of(1, r1);
-    issue_rows(kb, kring, 1, r1, flag<false>{});
-    issue_rows(vb, vring, 0, r0, flag<true>{});
+    issue_rows(kb, kring_lds, 1, r1, flag<false>{});
+    issue_rows(vb, vring_lds, 0, r0, flag<true>{});
     rows_of(2, vrows);
-    issue_rows(kb, kring, 2, vrows, flag<false>{});
-    issue_rows(vb, vring, 1, r1, flag<true>{});
-    rows_of(3, knext);
+    issue_rows(kb, kring_lds, 2, vrows, flag<false>{});
+    issue_rows(vb, vring_lds, 1, r1, flag<true>{});
+    read_gather(3, graw);
   }
 
   f32x16 oacc[DB];
@@ -321,11 +337,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     tile_barrier<G::OPS>(t);
     if (t < ti.ntiles) {
       issue_index(t + IAHEAD);
-      issue_rows(kb, kring, t + KAHEAD, knext, flag<false>{});
-      issue_rows(vb, vring, t + VAHEAD, vrows, flag<true>{});
+      int knext[PW];
+      rows_from(t + KAHEAD, graw, knext);
+      issue_rows(kb, kring_lds, t + KAHEAD, knext, flag<false>{});
+      issue_rows(vb, vring_lds, t + VAHEAD, vrows, flag<true>{});
 #pragma unroll
       for (int i = 0; i < PW; ++i) vrows[i] = knext[i];
-      rows_of(t + KAHEAD + 1, knext);                  // used in the next iteration
+      read_gather(t + KAHEAD + 1, graw);               // used in the next iteration
     }
   };
   // ---- the running max moved in the previous softmax: O to the new scale
