@@ -24,6 +24,9 @@ under "secondary":
     the streaming cache (4/64/64/256) in 4 chunks of 2048
     (sep_attn_prefill_chunk, window 256, then sep_cache_update): prompt
     tokens/s and useful TFLOP/s of the chunk attention;
+  * long prefill (1 x 131,072 tokens, 32q/8kv, D = 128, separators
+    closing runs of mean length 12, a = 4, n = 256): useful TFLOP/s of
+    sep_attn_prefill per launch;
   * prefill backward on the prefill workload (sep_attn_prefill_backward,
     bf16 MFMA with fp32 accumulation): useful TFLOP/s = 10 * D * visible
     pairs per query head (S = QK^T recomputed, dP = dO V^T, dQ, dK, dV) over
@@ -206,6 +209,48 @@ def bench_prefill(args, torch, sa, configs, gen):
         f"({tflops_step:.1f} TFLOP/s), prefill kernel {ms_kernel * 1e3:.1f} us ({tflops_kernel:.1f} TFLOP/s)")
     return dict(cfg=cfg, x=x, pairs=pairs, useful=useful, ms_step=ms_step, ms_kernel=ms_kernel,
                 tflops_step=tflops_step, tflops_kernel=tflops_kernel)
+
+
+def bench_long_prefill(args, torch, sa, configs, gen):
+    """sep_attn_prefill on the long prompt. The ids come from the seeded
+    generator (their runs set the structure); Q, K and V are N(0, 1) drawn on
+    the GPU from a seeded generator and rounded to bf16, the distribution of
+    the generator's host draws, which would take about a minute for these
+    0.8 G values."""
+    cfg = configs.LONG_PREFILL
+    B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+    ids = torch.from_numpy(np.stack([gen.prefill_ids(cfg, b) for b in range(B)])).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    q = torch.randn((B, Hq, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, Hkv, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, Hkv, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    sep = torch.tensor(cfg.sep_ids, dtype=torch.int32, device="cuda")
+    is_sep, rank, sep_pos, _ = sa.sep_mask_compact(ids, sep)
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+    run = lambda: sa.sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, cfg.a, cfg.n, scale, out=out)
+    run()
+    torch.cuda.synchronize()
+    pairs = sum(visible_pairs(rank[b].cpu().numpy().astype(np.int64), S, cfg.a, cfg.n) for b in range(B))
+    useful = 4.0 * D * pairs * Hq
+    st = torch.cuda.current_stream()
+    n = max(3, min(args.steps, 10))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(st)
+        run()
+        e1.record(st)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    tflops = useful / (ms * 1e-3) / 1e12
+    log(f"long prefill: {pairs} pairs/seq ({pairs / (S * (S + 1) / 2):.3f} of causal), "
+        f"{useful / 1e12:.2f} useful TFLOP, {ms:.2f} ms per launch ({tflops:.1f} TFLOP/s)")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return dict(workload=cfg.name, visible_pairs_per_head=pairs, useful_flop=useful, ms_per_launch=ms,
+                tflops=tflops, frac_peak=tflops / PEAK_BF16_TFLOPS,
+                inputs="ids seeded (runs); Q/K/V N(0,1) drawn on the GPU, bf16")
 
 
 def bench_backward(args, torch, sa, res):
@@ -695,7 +740,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--stream-steps", type=int, default=4_194_304)
-    ap.add_argument("--only", choices=["all", "prefill", "backward", "chunk", "decode", "stream", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "long", "backward", "chunk", "decode", "stream", "copy"],
                     default="all",
                     help="'copy' runs only a plain device copy of known size, the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -733,6 +778,8 @@ def main():
         if args.only == "backward":
             print(json.dumps({"secondary": secondary}))
             return
+    if args.only in ("all", "long"):
+        secondary["long_prefill"] = bench_long_prefill(args, torch, sa, configs, gen)
     if args.only in ("all", "chunk"):
         secondary["chunked_prefill"] = bench_chunk(args, torch, sa, configs, gen)
     if args.only in ("all", "decode"):
