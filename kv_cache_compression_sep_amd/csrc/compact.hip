@@ -85,20 +85,28 @@ __global__ void __launch_bounds__(kCompactThreads)
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int wid = tid / kWave;
-  for (int i = tid; i < n_sep; i += kCompactThreads) set[i] = sep_ids[i];
-  __syncthreads();
   const int32_t* id = ids + static_cast<int64_t>(b) * S;
   uint8_t* f = is_sep + static_cast<int64_t>(b) * S;
   int32_t* rk = rank + static_cast<int64_t>(b) * (S + 1);
   int32_t* sp = sep_pos + static_cast<int64_t>(b) * S;
   const bool vec = (S % 4) == 0;                  // rows of whole 16-byte groups (ids, rank)
+  // the ids of each chunk are loaded one chunk ahead (the first ones while
+  // the separator set is staged), so a load's latency overlaps the previous
+  // chunk's work
+  auto load4 = [&](int j0) -> int4 {
+    return (vec && j0 + 4 <= S) ? *reinterpret_cast<const int4*>(id + j0) : make_int4(0, 0, 0, 0);
+  };
+  int4 next = load4(4 * tid);
+  for (int i = tid; i < n_sep; i += kCompactThreads) set[i] = sep_ids[i];
+  __syncthreads();
   int carry = 0;
   int parity = 0;
   for (int base = 0; base < S; base += 4 * kCompactThreads, parity ^= 1) {
     const int j0 = base + 4 * tid;
+    const int4 v = next;
+    if (base + 4 * kCompactThreads < S) next = load4(j0 + 4 * kCompactThreads);
     int fl[4];
     if (vec && j0 + 4 <= S) {
-      const int4 v = *reinterpret_cast<const int4*>(id + j0);
       fl[0] = in_set(v.x, set, n_sep);
       fl[1] = in_set(v.y, set, n_sep);
       fl[2] = in_set(v.z, set, n_sep);
