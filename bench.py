@@ -17,9 +17,10 @@ under "secondary":
     with RoPE position shifting (sep_attn_decode_rope) against the plain one
     on the final cache, and each cache policy;
   * streaming decode (batch 1, cache 4/64/64/256) over the 4,194,304-token
-    stream: tokens/s of in-order decode + update steps, replayed from HIP
-    graphs of 256 steps; then its first 65,536 steps with RoPE position
-    shifting;
+    stream: tokens/s of in-order decode + update steps (sep_decode_update,
+    one launch per step), replayed from HIP graphs of 256 steps; then its
+    first 65,536 steps as the two calls sep_attn_decode + sep_cache_update,
+    and with RoPE position shifting;
   * chunked prefill: the prefill workload's 8192-token prompt streamed into
     the streaming cache (4/64/64/256) in 4 chunks of 2048
     (sep_attn_prefill_chunk, window 256, then sep_cache_update): prompt
@@ -622,6 +623,11 @@ def _occupancy(cache):
 
 # ------------------------------------------------------------------ stream
 def bench_stream(args, torch, sa, configs, gen):
+    """Streaming decode: in-order steps of one sequence, each the decode of
+    the new token over the cache, then its insertion (sep_decode_update: one
+    launch), replayed from HIP graphs of 256 steps. Also the same steps as
+    the two calls sep_attn_decode + sep_cache_update, and with RoPE position
+    shifting, over the first 65,536 steps."""
     cfg = configs.STREAM_DECODE
     Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
     steps = args.stream_steps
@@ -640,44 +646,56 @@ def bench_stream(args, torch, sa, configs, gen):
     cache = sa.SepCache(1, Hkv, D, cfg.a, cfg.s, cfg.p, cfg.w)
     out = torch.empty((1, Hq, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
-    n_graphs = min(P, steps) // chunk
-
-    def run_chunk(w):
-        for i in range(chunk):
-            t = w * chunk + i
-            sa.sep_attn_decode(pq[t], pk[t], pv[t], cache, scale, out=out)
-            sa.sep_cache_update(cache, pk[t].view(1, Hkv, 1, D), pv[t].view(1, Hkv, 1, D),
-                                stage[i:i + 1].view(1, 1), sep)
-
-    # capture one graph per pool window of `chunk` steps
+    table = sa.sep_rope_table(500000.0, D, cache.slots + 1)
     s_cap = torch.cuda.Stream()
-    graphs = []
-    tc0 = time.perf_counter()
-    with torch.cuda.stream(s_cap):
-        for w in range(n_graphs):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=s_cap):
-                run_chunk(w)
-            graphs.append(gr)
-    torch.cuda.synchronize()
-    cache.reset()
-    torch.cuda.synchronize()
-    log(f"stream: captured {n_graphs} graphs of {chunk} steps in {time.perf_counter() - tc0:.1f} s")
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record(st)
-    for c in range(steps // chunk):
-        t0 = c * chunk
-        stage.copy_(ids[t0:t0 + chunk], non_blocking=True)
-        graphs[c % n_graphs].replay()
-        if c % 2048 == 2047:
-            log(f"stream: {t0 + chunk} steps")
-    e1.record(st)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1)
-    assert int(cache.state[0, 0]) == steps
+
+    def fused(t, i):
+        sa.sep_decode_update(pq[t], pk[t], pv[t], stage[i:i + 1], cache, sep, scale, out=out)
+
+    def fused_rope(t, i):
+        sa.sep_decode_update(pq[t], pk[t], pv[t], stage[i:i + 1], cache, sep, scale, rope=table, out=out)
+
+    def two_calls(t, i):
+        sa.sep_attn_decode(pq[t], pk[t], pv[t], cache, scale, out=out)
+        sa.sep_cache_update(cache, pk[t].view(1, Hkv, 1, D), pv[t].view(1, Hkv, 1, D),
+                            stage[i:i + 1].view(1, 1), sep)
+
+    def capture(step, n):
+        # one graph per pool window of `chunk` steps
+        gs = []
+        with torch.cuda.stream(s_cap):
+            for w in range(n):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=s_cap):
+                    for i in range(chunk):
+                        step(w * chunk + i, i)
+                gs.append(gr)
+        torch.cuda.synchronize()
+        return gs
+
+    def replay(gs, nsteps, progress=False):
+        cache.reset()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        e0.record(st)
+        for c in range(nsteps // chunk):
+            t0 = c * chunk
+            stage.copy_(ids[t0:t0 + chunk], non_blocking=True)
+            gs[c % len(gs)].replay()
+            if progress and c % 2048 == 2047:
+                log(f"stream: {t0 + chunk} steps")
+        e1.record(st)
+        torch.cuda.synchronize()
+        assert int(cache.state[0, 0]) == nsteps
+        return e0.elapsed_time(e1), time.perf_counter() - wall0
+
+    n_graphs = min(P, steps) // chunk
+    tc0 = time.perf_counter()
+    graphs = capture(fused, n_graphs)
+    log(f"stream: captured {n_graphs} graphs of {chunk} steps in {time.perf_counter() - tc0:.1f} s")
+    ms, wall = replay(graphs, steps, progress=True)
     # closed-form check of the final positions and ids
     flags = np.isin(ids_h[:steps], np.asarray(cfg.sep_ids))
     K = _ncomp(steps, cfg)
@@ -690,47 +708,22 @@ def bench_stream(args, torch, sa, configs, gen):
     Rl = [cfg.a + cfg.s + (x - cfg.a) % (cfg.p + cfg.w) for x in range(max(cend, cfg.a), steps)]
     got = pos[list(range(cfg.a))].tolist() + pos[Sl].tolist() + pos[Rl].tolist()
     ok = got == want
-    res = dict(steps=steps, seconds=ms * 1e-3, wall_seconds=wall, tok_per_s=steps / (ms * 1e-3),
-               us_per_step=ms * 1e3 / steps, final_state_matches_closed_form=bool(ok))
+    res = dict(entry="sep_decode_update", steps=steps, seconds=ms * 1e-3, wall_seconds=wall,
+               tok_per_s=steps / (ms * 1e-3), us_per_step=ms * 1e3 / steps,
+               final_state_matches_closed_form=bool(ok))
     log(f"stream: {steps} steps in {ms * 1e-3:.2f} s -> {res['tok_per_s']:.0f} tok/s "
         f"({res['us_per_step']:.2f} us/step), closed form {'ok' if ok else 'MISMATCH'}")
     del graphs
-    # the first 65,536 steps again with RoPE position shifting
-    # (sep_attn_decode_rope), from graphs of the same shape
-    table = sa.sep_rope_table(500000.0, D, cache.slots + 1)
     rsteps = min(steps, 65_536)
     n_r = min(n_graphs, rsteps // chunk)
-
-    def run_chunk_rope(w):
-        for i in range(chunk):
-            t = w * chunk + i
-            sa.sep_attn_decode_rope(pq[t], pk[t], pv[t], cache, table, scale, out=out)
-            sa.sep_cache_update(cache, pk[t].view(1, Hkv, 1, D), pv[t].view(1, Hkv, 1, D),
-                                stage[i:i + 1].view(1, 1), sep)
-
-    rgraphs = []
-    with torch.cuda.stream(s_cap):
-        for w in range(n_r):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=s_cap):
-                run_chunk_rope(w)
-            rgraphs.append(gr)
-    torch.cuda.synchronize()
-    cache.reset()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
-    for c in range(rsteps // chunk):
-        t0 = c * chunk
-        stage.copy_(ids[t0:t0 + chunk], non_blocking=True)
-        rgraphs[c % n_r].replay()
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms_r = e0.elapsed_time(e1)
-    assert int(cache.state[0, 0]) == rsteps
-    res["rope_shifted"] = dict(steps=rsteps, tok_per_s=rsteps / (ms_r * 1e-3), us_per_step=ms_r * 1e3 / rsteps)
-    log(f"stream with RoPE shifting: {rsteps} steps -> {res['rope_shifted']['tok_per_s']:.0f} tok/s "
-        f"({res['rope_shifted']['us_per_step']:.2f} us/step)")
+    for name, step, what in (("two_launches", two_calls, "as sep_attn_decode + sep_cache_update"),
+                             ("rope_shifted", fused_rope, "with RoPE shifting")):
+        gs = capture(step, n_r)
+        ms_x, _ = replay(gs, rsteps)
+        del gs
+        res[name] = dict(steps=rsteps, tok_per_s=rsteps / (ms_x * 1e-3), us_per_step=ms_x * 1e3 / rsteps)
+        log(f"stream {what}: {rsteps} steps -> {res[name]['tok_per_s']:.0f} tok/s "
+            f"({res[name]['us_per_step']:.2f} us/step)")
     return res
 
 

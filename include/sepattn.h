@@ -223,7 +223,8 @@ int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const
  *          [2] sep_head      separator-ring slot the next separator takes;
  *          [3] sep_count     separators held (<= s);
  *          [4] n_compacted before the last sep_cache_update call;
- *          [5..7] reserved, 0.
+ *          [5..6] reserved, 0;
+ *          [7] arrival count of sep_decode_update, 0 between calls.
  *          The ring's entries, oldest first, are the slots
  *          a + (sep_head - sep_count + i) mod s, i = 0 .. sep_count-1.
  * An empty cache is state all zero and pos/tok all -1 (sep_cache_reset).
@@ -372,6 +373,31 @@ const char* sep_status_string(int status);
 
 /* Library version, as major*10000 + minor*100 + patch. */
 int sep_version(void);
+
+/*
+ * sep_decode_update - one streaming step: sep_attn_decode (or, with rope,
+ * sep_attn_decode_rope) of the new token, then sep_cache_update of that
+ * token (T = 1), in one call.
+ * [P1 "Streaming-SepLLM" (each step: the forward with the cache, then the
+ * cache update); P2 §1.3; P3 §3.3]
+ *
+ * Arguments are those of the two calls: q [B, Hq, D], k_new / v_new
+ * [B, Hkv, D] in cache->dtype (SEP_BF16 only), ids_new [B] int32, sep_ids
+ * [n_sep_ids] int32, scale > 0, rope NULL (plain decode) or the table of
+ * sep_rope_table with rope_npos >= slots + 1 rows, out [B, Hq, D] bf16, lse
+ * [B, Hq] float32 or NULL. The result (out, lse, and the cache's K/V, pos,
+ * tok and state) equals the two calls in that order, bit for bit.
+ * When B * Hkv < 256 and the separator ring holds at most 4096 entries it
+ * is one launch (each sequence's last kv-head workgroup to finish its decode
+ * runs the update, counting arrivals in state word 7, which is 0 between
+ * calls); otherwise it is the two launches. Calls on one cache must not
+ * overlap.
+ * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
+ * SEP_ERR_ALIGN, SEP_ERR_HIP.
+ */
+int sep_decode_update(const void* q, const void* k_new, const void* v_new, const int32_t* ids_new,
+                      const int32_t* sep_ids, int n_sep_ids, const sep_cache* cache, int Hq, float scale,
+                      const float* rope, int rope_npos, void* out, float* lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

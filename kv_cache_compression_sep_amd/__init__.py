@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
 __all__ = ["sep_mask_build", "sep_index_compact", "sep_mask_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
-           "sep_attn_decode", "sep_attn_decode_rope", "sep_rope_table", "sep_attn_prefill_chunk",
+           "sep_attn_decode", "sep_attn_decode_rope", "sep_decode_update", "sep_rope_table", "sep_attn_prefill_chunk",
            "chunk_workspace_bytes",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
            "SEP_POLICY_DYNAMIC", "SEP_POLICY_NO_ACCUM"]
@@ -334,6 +334,42 @@ def sep_attn_decode_rope(q, k_new, v_new, cache: SepCache, rope, scale: float | 
                                     float(scale), rope.data_ptr(), rope.shape[0], out.data_ptr(), _ptr(lse),
                                     _stream())
     _lib.check("sep_attn_decode_rope", code)
+    return (out, lse) if return_lse else out
+
+
+def sep_decode_update(q, k_new, v_new, ids_new, cache: SepCache, sep_ids, scale: float | None = None, *,
+                      rope=None, out=None, return_lse: bool = False, lse=None):
+    """One streaming step: the decode of q [B,Hq,D] with k_new/v_new
+    [B,Hkv,D] (bf16) over the cache (with `rope`, at shifted positions),
+    then the insertion of that token (ids_new [B] int32) into the cache;
+    equal to sep_attn_decode (or sep_attn_decode_rope) then
+    sep_cache_update, in one launch where the decode runs wide."""
+    lib = _lib.load()
+    _need(q, "q", cache.dtype, 3)
+    _need(k_new, "k_new", cache.dtype, 3)
+    _need(v_new, "v_new", cache.dtype, 3)
+    _need(ids_new, "ids_new", torch.int32, 1)
+    _need(sep_ids, "sep_ids", torch.int32, 1)
+    B, Hq, D = q.shape
+    if (B, D) != (cache.B, cache.D) or k_new.shape != (B, cache.Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("shapes do not match the cache")
+    if ids_new.shape != (B,):
+        raise ValueError("ids_new must be [B]")
+    if rope is not None:
+        _need(rope, "rope", torch.float32, 3)
+        if rope.shape[1:] != (D // 2, 2):
+            raise ValueError("rope must be [n_pos, D/2, 2]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = torch.empty_like(q) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = cache.struct()
+    code = lib.sep_decode_update(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ids_new.data_ptr(),
+                                 _ptr(sep_ids) if sep_ids.numel() else None, sep_ids.numel(), ctypes.byref(st),
+                                 Hq, float(scale), _ptr(rope), 0 if rope is None else rope.shape[0],
+                                 out.data_ptr(), _ptr(lse), _stream())
+    _lib.check("sep_decode_update", code)
     return (out, lse) if return_lse else out
 
 

@@ -62,6 +62,8 @@ SIGNATURES = {
                                      c_int, c_vp, c_vp, c_vp]),
     "sep_attn_decode": (c_int, [c_vp, c_vp, c_vp, ctypes.POINTER(SepCacheStruct), c_int, c_float,
                                 c_vp, c_vp, c_vp]),
+    "sep_decode_update": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, ctypes.POINTER(SepCacheStruct), c_int,
+                                  c_float, c_vp, c_int, c_vp, c_vp, c_vp]),
     "sep_status_string": (ctypes.c_char_p, [c_int]),
     "sep_version": (c_int, []),
 }

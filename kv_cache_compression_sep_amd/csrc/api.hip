@@ -237,4 +237,26 @@ int sep_attn_decode_rope(const void* q, const void* k_new, const void* v_new, co
   return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, rope, out, lse, stream));
 }
 
+int sep_decode_update(const void* q, const void* k_new, const void* v_new, const int32_t* ids_new,
+                      const int32_t* sep_ids, int n_sep_ids, const sep_cache* cache, int Hq, float scale,
+                      const float* rope, int rope_npos, void* out, float* lse, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != SEP_OK) return st;
+  st = check_cache_kv(cache);
+  if (st != SEP_OK) return st;
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || ids_new == nullptr || out == nullptr)
+    return SEP_ERR_NULL;
+  if (n_sep_ids < 0 || n_sep_ids > SEP_MAX_SEP_IDS) return SEP_ERR_SHAPE;
+  if (n_sep_ids > 0 && sep_ids == nullptr) return SEP_ERR_NULL;
+  if (cache->dtype != SEP_BF16) return SEP_ERR_DTYPE;
+  if (Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return SEP_ERR_SHAPE;
+  if (!(scale > 0.0f) || scale > 1e30f) return SEP_ERR_PARAM;
+  if (rope != nullptr && rope_npos < sep::cache_slots(*cache) + 1) return SEP_ERR_PARAM;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+      (rope != nullptr && !aligned16(rope)))
+    return SEP_ERR_ALIGN;
+  return hip_status(sep::launch_decode_update(q, k_new, v_new, ids_new, sep_ids, n_sep_ids, *cache, Hq, scale,
+                                              rope, out, lse, stream));
+}
+
 }  // extern "C"

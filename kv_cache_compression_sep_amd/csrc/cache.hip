@@ -31,6 +31,7 @@
 // sequence) copies K/V rows, reading the plan back from pos[] of the
 // separator ring. T == 1 runs one fused block per sequence.
 #include "common.hpp"
+#include "decode.hpp"
 #include "internal.hpp"
 
 #include <type_traits>
@@ -597,7 +598,7 @@ __device__ void update_block(const CacheArgs& A, const Set& S, PlanHead& ph, int
 }
 
 template <int MODE, bool DYN>
-__global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
+__device__ __forceinline__ void update_body(const CacheArgs& A) {
   extern __shared__ int32_t dyn[];
   __shared__ int32_t set_lds[SEP_MAX_SEP_IDS_];
   __shared__ int32_t set_tab[MODE == UPD_FUSED ? 1 : kHashSize];
@@ -680,6 +681,11 @@ __global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
       update_block<MODE, DYN>(A, L, ph, lpos, lid, wave_tot, sb);
     }
   }
+}
+
+template <int MODE, bool DYN>
+__global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
+  update_body<MODE, DYN>(A);
 }
 
 // K/V rows of a call with T > 1, grid (Hkv, B), one head per block; runs
@@ -777,9 +783,7 @@ static hipError_t launch_update_chunk(const sep_cache& c, const CacheArgs& A, si
   return hipGetLastError();
 }
 
-hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void* v_new,
-                               const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,
-                               hipStream_t st) {
+static CacheArgs cache_args(const sep_cache& c, const int32_t* sep_ids, int n_sep, int T) {
   CacheArgs A;
   A.k = static_cast<char*>(c.k);
   A.v = static_cast<char*>(c.v);
@@ -800,7 +804,18 @@ hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void
   A.tstride = T;
   A.dynamic = (c.policy & SEP_POLICY_DYNAMIC) ? 1 : 0;
   A.accumulate = (c.policy & SEP_POLICY_NO_ACCUM) ? 0 : 1;
-  const size_t dyn = 2 * sizeof(int32_t) * static_cast<size_t>(c.s > 0 ? c.s : 1);
+  return A;
+}
+
+static size_t update_dyn_bytes(const sep_cache& c) {
+  return 2 * sizeof(int32_t) * static_cast<size_t>(c.s > 0 ? c.s : 1);
+}
+
+hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void* v_new,
+                               const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,
+                               hipStream_t st) {
+  CacheArgs A = cache_args(c, sep_ids, n_sep, T);
+  const size_t dyn = update_dyn_bytes(c);
   const size_t row_bytes = static_cast<size_t>(c.D) * A.esize;
   // a dynamic-trigger plan covers the ring plus the new tokens in one
   // bitmap of kSpan positions, so a long call runs as consecutive chunks
@@ -816,6 +831,77 @@ hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------- decode + update
+// One streaming step in one launch: every workgroup (kv head g, sequence b)
+// runs the decode of sep_attn_decode (8 waves), and the last of a sequence's
+// Hkv workgroups to finish then runs the single-token update of
+// sep_cache_update for that sequence, all heads (SepLLM pages: P1
+// "Streaming-SepLLM", the forward with the cache, then the update). The
+// update rewrites K/V rows and the state words that the other workgroups
+// read, so it waits until all of them are done: each workgroup, once all its
+// waves have consumed what they loaded, adds one to an arrival counter in
+// state word kArriveWord with a device-scope atomic, and the workgroup that
+// brings it to Hkv resets it and updates. No other workgroup reads anything
+// the update writes, so no release or acquire fence is needed; the next
+// launch sees the update at the kernel boundary.
+constexpr int kArriveWord = 7;
+
+template <int D, bool ROPE, bool DYN>
+__global__ void __launch_bounds__(kUpdThreads) decode_update_kernel(DecodeArgs A, CacheArgs U) {
+  static_assert(kUpdThreads == 8 * kWave, "the decode runs with 8 waves here");
+  __shared__ int last;
+  decode_body<D, 8, ROPE>(A);
+  __syncthreads();
+  const int64_t sw = kStateWords * static_cast<int64_t>(blockIdx.y);
+  if (threadIdx.x == 0) {
+    unsigned long long* arrive = reinterpret_cast<unsigned long long*>(U.state + sw + kArriveWord);
+    last = atomicAdd(arrive, 1ull) == static_cast<unsigned long long>(U.Hkv - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x == 0) U.state[sw + kArriveWord] = 0;
+  update_body<UPD_FUSED, DYN>(U);
+}
+
+// LDS the fused kernel may add for the update's position / id lists
+constexpr size_t kFusedDynMax = 32 * 1024;
+
+template <int D, bool ROPE>
+static void launch_fused(const sep_cache& c, const DecodeArgs& A, const CacheArgs& U, size_t dyn, hipStream_t st) {
+  if (U.dynamic)
+    hipLaunchKernelGGL((decode_update_kernel<D, ROPE, true>), dim3(c.Hkv, c.B), dim3(kUpdThreads), dyn, st, A, U);
+  else
+    hipLaunchKernelGGL((decode_update_kernel<D, ROPE, false>), dim3(c.Hkv, c.B), dim3(kUpdThreads), dyn, st, A, U);
+}
+
+hipError_t launch_decode_update(const void* q, const void* k_new, const void* v_new, const int32_t* ids_new,
+                                const int32_t* sep_ids, int n_sep, const sep_cache& c, int Hq, float scale,
+                                const float* rope, void* out, float* lse, hipStream_t st) {
+  const size_t dyn = update_dyn_bytes(c);
+  // the fused launch covers the few-pairs case, where the decode runs with 8
+  // waves; otherwise the two launches it stands for
+  if (!decode_uses_wide(c) || dyn > kFusedDynMax) {
+    hipError_t e = launch_decode(q, k_new, v_new, c, Hq, scale, rope, out, lse, st);
+    if (e != hipSuccess) return e;
+    return launch_cache_update(c, k_new, v_new, ids_new, 1, sep_ids, n_sep, st);
+  }
+  const DecodeArgs A = decode_args(q, k_new, v_new, c, Hq, scale, rope, out, lse);
+  CacheArgs U = cache_args(c, sep_ids, n_sep, 1);
+  U.T = 1;
+  U.k_new = static_cast<const char*>(k_new);
+  U.v_new = static_cast<const char*>(v_new);
+  U.ids_new = ids_new;
+  const bool r = rope != nullptr;
+  if (c.D == 128) {
+    if (r) launch_fused<128, true>(c, A, U, dyn, st);
+    else launch_fused<128, false>(c, A, U, dyn, st);
+  } else {
+    if (r) launch_fused<64, true>(c, A, U, dyn, st);
+    else launch_fused<64, false>(c, A, U, dyn, st);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sep

@@ -42,6 +42,11 @@ hipError_t launch_cache_reset(const sep_cache& c, hipStream_t st);
 hipError_t launch_cache_update(const sep_cache& c, const void* k_new, const void* v_new,
                                const int32_t* ids_new, int T, const int32_t* sep_ids, int n_sep,
                                hipStream_t st);
+// decode then single-token update in one launch where the decode runs wide
+// (else the two launches)
+hipError_t launch_decode_update(const void* q, const void* k_new, const void* v_new, const int32_t* ids_new,
+                                const int32_t* sep_ids, int n_sep, const sep_cache& c, int Hq, float scale,
+                                const float* rope, void* out, float* lse, hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k_new, const void* v_new, const sep_cache& c,
                          int Hq, float scale, const float* rope, void* out, float* lse, hipStream_t st);
 size_t chunk_workspace_bytes(const sep_cache& c, int C);

@@ -208,6 +208,25 @@ def test_rope_argument_checks(lib):
     assert dec(_cache(dtype=0)) == E.SEP_ERR_DTYPE
 
 
+def test_decode_update_argument_checks(lib):
+    E = _lib
+    c = _cache()                                         # 4 + 64 + (64 + 256) slots, 8 kv heads
+    du = lambda cc, **kw: lib.sep_decode_update(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("ids", FAKE), FAKE, kw.get("nsep", 4), ctypes.byref(cc),
+        kw.get("Hq", 32), kw.get("scale", 0.1), kw.get("rope", None), kw.get("npos", 0), kw.get("out", FAKE),
+        None, None)
+    assert du(c, q=None) == E.SEP_ERR_NULL
+    assert du(c, ids=None) == E.SEP_ERR_NULL
+    assert du(c, out=None) == E.SEP_ERR_NULL
+    assert du(c, nsep=65) == E.SEP_ERR_SHAPE
+    assert du(c, Hq=12) == E.SEP_ERR_SHAPE                # not a multiple of Hkv = 8
+    assert du(c, scale=0.0) == E.SEP_ERR_PARAM
+    assert du(c, rope=FAKE, npos=388) == E.SEP_ERR_PARAM  # fewer rows than slots + 1
+    assert du(c, q=FAKE + 4) == E.SEP_ERR_ALIGN
+    assert du(c, rope=FAKE + 4, npos=389) == E.SEP_ERR_ALIGN
+    assert du(_cache(dtype=0)) == E.SEP_ERR_DTYPE
+
+
 def test_chunk_argument_checks(lib):
     E = _lib
     c = _cache()                                          # 4 + 64 + 320 slots, 8 kv heads, D = 128
