@@ -164,9 +164,20 @@ int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
  *   dq     [B, Hq, S, D] float32 out; dk, dv [B, Hkv, S, D] float32 out
  *          (written, not accumulated).
  * Shapes as for sep_attn_prefill, and S <= SEP_MAX_BACKWARD_S.
- * Arithmetic: fp32 throughout (bf16 inputs are widened exactly); dk and dv
- * of initial and separator keys are summed with fp32 atomics, so their
- * summation order varies between runs.
+ * Arithmetic, by dtype:
+ *   SEP_F32   products on the fp32 MFMA; every operand, P, dP, dS and
+ *             accumulator in fp32.
+ *   SEP_BF16  products on the bf16 MFMA with fp32 accumulation: q, k, v,
+ *             dout enter as bf16 (exactly); scores, P, dP and dS are
+ *             computed in fp32, and P (for dv) and dS (for dq, dk) are
+ *             rounded to bf16 (round to nearest even) before their products.
+ *   Each element of dq, dk, dv lies within (e^d - 1 + r + g) * A of the
+ *   exact gradient, where A is the same sum taken over absolute values, d
+ *   the forward's log-sum-exp error (2.5e-3 bf16, 1e-5 fp32), r = 2^-9 for
+ *   bf16 (0 for fp32) and g = m u / (1 - m u) with u = 2^-24 and m = D + G S
+ *   (G = Hq / Hkv): the bound the parity tests apply.
+ * dk and dv of initial and separator keys are summed with fp32 atomics, so
+ * their summation order varies between runs.
  * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
  * SEP_ERR_ALIGN, SEP_ERR_HIP.
  */

@@ -51,6 +51,25 @@ def _need(t, name, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _need_shape(t, name, shape, dtype, device=None):
+    """t must be a contiguous GPU tensor of exactly this shape and dtype (and
+    on `device` when given): the C ABI cannot see tensor sizes, so a wrong
+    size here would make a kernel read or write out of bounds."""
+    _need(t, name, dtype)
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _out(t, name, shape, dtype, device):
+    """The caller's output tensor after checking it, or a new one."""
+    if t is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=device)
+    _need_shape(t, name, shape, dtype, device)
+    return t
+
+
 def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return SEP_BF16
@@ -72,15 +91,17 @@ def sep_mask_build(ids, sep_ids, a: int, n: int, *, is_sep=None, tiles: tuple | 
     _need(sep_ids, "sep_ids", torch.int32, 1)
     B, S = ids.shape
     dev = ids.device
-    if is_sep is None:
-        is_sep = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    is_sep = _out(is_sep, "is_sep", (B, S), torch.uint8, dev)
     tq = tk = 0
     if tiles is not None:
-        tq, tk = tiles
-        if tile_class is None:
-            tile_class = torch.empty((B, -(-S // tq), -(-S // tk)), dtype=torch.uint8, device=dev)
-    if dense and dense_mask is None:
-        dense_mask = torch.empty((B, S, S), dtype=torch.uint8, device=dev)
+        tq, tk = (int(x) for x in tiles)
+        if tq < 1 or tk < 1:
+            raise ValueError("tiles must be positive")
+        tile_class = _out(tile_class, "tile_class", (B, -(-S // tq), -(-S // tk)), torch.uint8, dev)
+    elif tile_class is not None:
+        raise ValueError("tile_class needs tiles=(tq, tk)")
+    if dense or dense_mask is not None:
+        dense_mask = _out(dense_mask, "dense_mask", (B, S, S), torch.uint8, dev)
     code = lib.sep_mask_build(ids.data_ptr(), B, S, _ptr(sep_ids) if sep_ids.numel() else None,
                               sep_ids.numel(), a, n, is_sep.data_ptr(), _ptr(tile_class), tq, tk,
                               _ptr(dense_mask), _stream())
@@ -94,9 +115,9 @@ def sep_index_compact(is_sep, *, rank=None, sep_pos=None, count=None):
     _need(is_sep, "is_sep", torch.uint8, 2)
     B, S = is_sep.shape
     dev = is_sep.device
-    rank = torch.empty((B, S + 1), dtype=torch.int32, device=dev) if rank is None else rank
-    sep_pos = torch.empty((B, S), dtype=torch.int32, device=dev) if sep_pos is None else sep_pos
-    count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
+    rank = _out(rank, "rank", (B, S + 1), torch.int32, dev)
+    sep_pos = _out(sep_pos, "sep_pos", (B, S), torch.int32, dev)
+    count = _out(count, "count", (B,), torch.int32, dev)
     code = lib.sep_index_compact(is_sep.data_ptr(), B, S, rank.data_ptr(), sep_pos.data_ptr(),
                                  count.data_ptr(), _stream())
     _lib.check("sep_index_compact", code)
@@ -111,14 +132,21 @@ def sep_mask_compact(ids, sep_ids, *, is_sep=None, rank=None, sep_pos=None, coun
     _need(sep_ids, "sep_ids", torch.int32, 1)
     B, S = ids.shape
     dev = ids.device
-    is_sep = torch.empty((B, S), dtype=torch.uint8, device=dev) if is_sep is None else is_sep
-    rank = torch.empty((B, S + 1), dtype=torch.int32, device=dev) if rank is None else rank
-    sep_pos = torch.empty((B, S), dtype=torch.int32, device=dev) if sep_pos is None else sep_pos
-    count = torch.empty((B,), dtype=torch.int32, device=dev) if count is None else count
-    code = lib.sep_mask_compact(ids.data_ptr(), B, S, sep_ids.data_ptr(), sep_ids.numel(), is_sep.data_ptr(),
-                                rank.data_ptr(), sep_pos.data_ptr(), count.data_ptr(), _stream())
+    is_sep = _out(is_sep, "is_sep", (B, S), torch.uint8, dev)
+    rank = _out(rank, "rank", (B, S + 1), torch.int32, dev)
+    sep_pos = _out(sep_pos, "sep_pos", (B, S), torch.int32, dev)
+    count = _out(count, "count", (B,), torch.int32, dev)
+    code = lib.sep_mask_compact(ids.data_ptr(), B, S, _ptr(sep_ids) if sep_ids.numel() else None,
+                                sep_ids.numel(), is_sep.data_ptr(), rank.data_ptr(), sep_pos.data_ptr(),
+                                count.data_ptr(), _stream())
     _lib.check("sep_mask_compact", code)
     return is_sep, rank, sep_pos, count
+
+
+def _need_index(is_sep, rank, sep_pos, B, S, dev):
+    _need_shape(is_sep, "is_sep", (B, S), torch.uint8, dev)
+    _need_shape(rank, "rank", (B, S + 1), torch.int32, dev)
+    _need_shape(sep_pos, "sep_pos", (B, S), torch.int32, dev)
 
 
 def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: float | None = None, *,
@@ -131,16 +159,15 @@ def sep_attn_prefill(q, k, v, is_sep, rank, sep_pos, a: int, n: int, scale: floa
         raise ValueError("q, k, v must share a dtype")
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
-        raise ValueError("k/v must be [B, Hkv, S, D] matching q")
-    _need(is_sep, "is_sep", torch.uint8, 2)
-    _need(rank, "rank", torch.int32, 2)
-    _need(sep_pos, "sep_pos", torch.int32, 2)
+    dev = q.device
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or k.device != dev or v.device != dev:
+        raise ValueError("k/v must be [B, Hkv, S, D] matching q, on q's device")
+    _need_index(is_sep, rank, sep_pos, B, S, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", q.shape, q.dtype, dev)
+    if return_lse or lse is not None:
+        lse = _out(lse, "lse", (B, Hq, S), torch.float32, dev)
     code = lib.sep_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, Hq,
                                 Hkv, S, D, is_sep.data_ptr(), rank.data_ptr(), sep_pos.data_ptr(),
                                 a, n, float(scale), out.data_ptr(), _ptr(lse), _stream())
@@ -159,19 +186,20 @@ def sep_attn_prefill_backward(q, k, v, out, dout, lse, is_sep, rank, sep_pos, a:
         raise ValueError("q, k, v, out, dout must share a dtype")
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
+    dev = q.device
     if k.shape != (B, Hkv, S, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("k/v must be [B, Hkv, S, D]; out/dout [B, Hq, S, D]")
-    _need(lse, "lse", torch.float32, 3)
-    _need(is_sep, "is_sep", torch.uint8, 2)
-    _need(rank, "rank", torch.int32, 2)
-    _need(sep_pos, "sep_pos", torch.int32, 2)
+    if any(t.device != dev for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must be on one device")
+    _need_shape(lse, "lse", (B, Hq, S), torch.float32, dev)
+    _need_index(is_sep, rank, sep_pos, B, S, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    f32 = dict(dtype=torch.float32, device=q.device)
-    dq = torch.empty((B, Hq, S, D), **f32) if dq is None else dq
-    dk = torch.empty((B, Hkv, S, D), **f32) if dk is None else dk
-    dv = torch.empty((B, Hkv, S, D), **f32) if dv is None else dv
-    delta = torch.empty((B, Hq, S), **f32) if delta is None else delta
+    f32 = torch.float32
+    dq = _out(dq, "dq", (B, Hq, S, D), f32, dev)
+    dk = _out(dk, "dk", (B, Hkv, S, D), f32, dev)
+    dv = _out(dv, "dv", (B, Hkv, S, D), f32, dev)
+    delta = _out(delta, "delta", (B, Hq, S), f32, dev)
     code = lib.sep_attn_prefill_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          dout.data_ptr(), lse.data_ptr(), _dtype_code(q), B, Hq, Hkv, S, D,
                                          is_sep.data_ptr(), rank.data_ptr(), sep_pos.data_ptr(), a, n,
@@ -210,27 +238,31 @@ class SepCache:
         self.state = torch.zeros((B, STATE_WORDS), dtype=torch.int64, device=dev)
 
     def struct(self) -> _lib.SepCacheStruct:
+        """The sep_cache view of this cache, after checking that its tensors
+        still have the shapes the C side will assume."""
+        dev = self.k.device
+        _need_shape(self.k, "cache.k", (self.B, self.Hkv, self.slots, self.D), self.dtype, dev)
+        _need_shape(self.v, "cache.v", (self.B, self.Hkv, self.slots, self.D), self.dtype, dev)
+        _need_shape(self.pos, "cache.pos", (self.B, self.slots), torch.int32, dev)
+        _need_shape(self.tok, "cache.tok", (self.B, self.slots), torch.int32, dev)
+        _need_shape(self.state, "cache.state", (self.B, STATE_WORDS), torch.int64, dev)
         return _lib.SepCacheStruct(self.a, self.s, self.p, self.w, self.B, self.Hkv, self.D,
                                    _dtype_code(self.k), self.k.data_ptr(), self.v.data_ptr(),
                                    self.pos.data_ptr(), self.tok.data_ptr(), self.state.data_ptr(),
                                    self.policy)
-
-    def slots_of(self, b: int):
-        """Slots of sequence b's retained entries per block, oldest first:
-        (initial, separator ring, recent ring), from its state words."""
-        t, ncomp, head, cnt = [int(x) for x in self.state[b, :4].cpu().numpy()]
-        a, s = self.a, self.s
-        I = list(range(min(a, t)))
-        S = [a + (head - cnt + i) % s for i in range(cnt)] if s > 0 else []
-        cend = a + ncomp
-        R = [a + s + (x - a) % self.ring for x in range(max(cend, a), t)] if t > a else []
-        return I, S, R
 
     def reset(self):
         sep_cache_reset(self)
 
     def n_seen(self):
         return self.state[:, 0]
+
+
+def _need_same_device(cache, **tensors):
+    dev = cache.k.device
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be on the cache's device {dev}, got {t.device}")
 
 
 def sep_cache_reset(cache: SepCache):
@@ -250,6 +282,7 @@ def sep_cache_update(cache: SepCache, k_new, v_new, ids_new, sep_ids):
         raise ValueError("k_new/v_new must be [B, Hkv, T, D] of the cache")
     if ids_new.shape != (B, T):
         raise ValueError("ids_new must be [B, T]")
+    _need_same_device(cache, k_new=k_new, v_new=v_new, ids_new=ids_new, sep_ids=sep_ids)
     st = cache.struct()
     code = lib.sep_cache_update(ctypes.byref(st), k_new.data_ptr(), v_new.data_ptr(),
                                 ids_new.data_ptr(), T,
@@ -282,12 +315,20 @@ def sep_attn_prefill_chunk(q, k, v, ids, cache: "SepCache", sep_ids, n: int, sca
         raise ValueError("ids must be [B, C]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _need_same_device(cache, q=q, k=k, v=v, ids=ids, sep_ids=sep_ids)
+    dev = q.device
     need = chunk_workspace_bytes(cache, C)
     if workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+        if workspace.device != dev:
+            raise ValueError("workspace must be on the cache's device")
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    out = _out(out, "out", q.shape, q.dtype, dev)
+    if return_lse or lse is not None:
+        lse = _out(lse, "lse", (B, Hq, C), torch.float32, dev)
     st = cache.struct()
     code = lib.sep_attn_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), ids.data_ptr(), C,
                                       sep_ids.data_ptr(), sep_ids.numel(), ctypes.byref(st), Hq, n, float(scale),
@@ -300,10 +341,8 @@ def sep_attn_prefill_chunk(q, k, v, ids, cache: "SepCache", sep_ids, n: int, sca
 def sep_rope_table(base: float, D: int, n_pos: int, *, out=None, device="cuda"):
     """(cos, sin) of p * base^(-2i/D) for p < n_pos, i < D/2: float32 [n_pos, D/2, 2]."""
     lib = _lib.load()
-    out = torch.empty((n_pos, D // 2, 2), dtype=torch.float32, device=device) if out is None else out
-    _need(out, "out", torch.float32, 3)
-    if out.shape != (n_pos, D // 2, 2):
-        raise ValueError("out must be [n_pos, D/2, 2]")
+    dev = out.device if isinstance(out, torch.Tensor) else torch.device(device)
+    out = _out(out, "out", (n_pos, D // 2, 2), torch.float32, dev)
     code = lib.sep_rope_table(float(base), D, n_pos, out.data_ptr(), _stream())
     _lib.check("sep_rope_table", code)
     return out
@@ -324,11 +363,12 @@ def sep_attn_decode_rope(q, k_new, v_new, cache: SepCache, rope, scale: float | 
         raise ValueError("shapes do not match the cache")
     if rope.shape[1:] != (D // 2, 2):
         raise ValueError("rope must be [n_pos, D/2, 2]")
+    _need_same_device(cache, q=q, k_new=k_new, v_new=v_new, rope=rope)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    if return_lse or lse is not None:
+        lse = _out(lse, "lse", (B, Hq), torch.float32, q.device)
     st = cache.struct()
     code = lib.sep_attn_decode_rope(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ctypes.byref(st), Hq,
                                     float(scale), rope.data_ptr(), rope.shape[0], out.data_ptr(), _ptr(lse),
@@ -359,11 +399,12 @@ def sep_decode_update(q, k_new, v_new, ids_new, cache: SepCache, sep_ids, scale:
         _need(rope, "rope", torch.float32, 3)
         if rope.shape[1:] != (D // 2, 2):
             raise ValueError("rope must be [n_pos, D/2, 2]")
+    _need_same_device(cache, q=q, k_new=k_new, v_new=v_new, ids_new=ids_new, sep_ids=sep_ids, rope=rope)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    if return_lse or lse is not None:
+        lse = _out(lse, "lse", (B, Hq), torch.float32, q.device)
     st = cache.struct()
     code = lib.sep_decode_update(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ids_new.data_ptr(),
                                  _ptr(sep_ids) if sep_ids.numel() else None, sep_ids.numel(), ctypes.byref(st),
@@ -383,11 +424,12 @@ def sep_attn_decode(q, k_new, v_new, cache: SepCache, scale: float | None = None
     B, Hq, D = q.shape
     if (B, D) != (cache.B, cache.D) or k_new.shape != (B, cache.Hkv, D) or v_new.shape != k_new.shape:
         raise ValueError("shapes do not match the cache")
+    _need_same_device(cache, q=q, k_new=k_new, v_new=v_new)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    out = torch.empty_like(q) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    if return_lse or lse is not None:
+        lse = _out(lse, "lse", (B, Hq), torch.float32, q.device)
     st = cache.struct()
     code = lib.sep_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), ctypes.byref(st),
                                Hq, float(scale), out.data_ptr(), _ptr(lse), _stream())

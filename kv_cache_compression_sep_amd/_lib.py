@@ -12,7 +12,7 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("SEPATTN_LIB", os.path.join(HERE, "libsepattn.so"))
+LIB_PATH = os.path.join(HERE, "libsepattn.so")
 
 c_int = ctypes.c_int
 c_float = ctypes.c_float
@@ -78,13 +78,13 @@ class SepError(RuntimeError):
         self.code = code
 
 
-def load(path: str | None = None) -> ctypes.CDLL:
-    """Load libsepattn.so once; raise if it is not there."""
+def load() -> ctypes.CDLL:
+    """Load the package's own libsepattn.so once; raise if it is not there."""
     global _lib
     with _lock:
-        if _lib is not None and path is None:
+        if _lib is not None:
             return _lib
-        p = path or LIB_PATH
+        p = LIB_PATH
         if not os.path.exists(p):
             raise RuntimeError(
                 f"libsepattn.so not found at {p}; build it with "
@@ -94,8 +94,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        if path is None:
-            _lib = lib
+        _lib = lib
         return lib
 
 

@@ -38,7 +38,7 @@ library routines, invariants and a closed form). No function here is
 "parity unpinned".
 """
 from .mask import (is_sep, sep_mask, mask_rows, compact, tile_class,  # noqa: F401
-                   tile_class_slabs, visible_count)
+                   tile_class_slabs)
 from .attention import (attention, attention_backward, attention_backward_sampled, attention_rows,  # noqa: F401
                         chunk_attention, decode_attention)
 from .rope import decode_attention_shifted, rope_angles, rotate, round_bf16  # noqa: F401

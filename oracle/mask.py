@@ -60,11 +60,6 @@ def mask_rows(flags: np.ndarray, a: int, n: int, rows: Sequence[int]) -> np.ndar
     return keep & (j <= i)
 
 
-def visible_count(M: np.ndarray) -> int:
-    """Number of (query, key) pairs with M = 1."""
-    return int(np.count_nonzero(M))
-
-
 def compact(flags: np.ndarray):
     """Prefix-sum stream compaction of the separator flags of one sequence.
 

@@ -51,3 +51,19 @@ def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") ->
         f"{what}: max err {err.max():.3e} (bound at worst {bound[worst]:.3e}, ref {ref[worst]:.4f}, "
         f"got {got[worst]:.4f} at {worst})")
     return float(err.max())
+
+
+def slots_of(cache, b: int, state=None):
+    """Slots of sequence b's retained entries per block, oldest first:
+    (initial, separator ring, recent ring), from its state words (the slot
+    layout of sep_cache in include/sepattn.h). ``state`` overrides the
+    cache's own state tensor (for a snapshot)."""
+    st = cache.state if state is None else state
+    t, ncomp, head, cnt = [int(x) for x in st[b, :4].cpu().numpy()]
+    a, s = cache.a, cache.s
+    I = list(range(min(a, t)))
+    S = [a + (head - cnt + i) % s for i in range(cnt)] if s > 0 else []
+    cend = a + ncomp
+    R = [a + s + (x - a) % cache.ring for x in range(max(cend, a), t)] if t > a else []
+    return I, S, R
+

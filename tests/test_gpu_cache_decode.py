@@ -20,7 +20,7 @@ from inputs import configs, gen
 from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache,
                                           sep_attn_decode, sep_cache_update)
 
-from .gpu_util import check_close, from_dev, to_dev
+from .gpu_util import check_close, from_dev, slots_of, to_dev
 
 pytestmark = pytest.mark.gpu
 SEP_IDS = list(range(8))
@@ -45,7 +45,7 @@ class Stream:
 
 
 def live_slots(cache, b):
-    return cache.slots_of(b)
+    return slots_of(cache, b)
 
 
 def check_cache(cache, sims, stream):
