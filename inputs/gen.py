@@ -199,3 +199,22 @@ def history_kv(cfg, b: int):
     v = np.stack([normal_rows(cfg.seed, (b, TAG_HV, g), cfg.history, cfg.D, cfg.dtype)
                   for g in range(cfg.Hkv)])
     return k, v
+
+
+# ---------------------------------------------------------------- on the device
+def device_normal(shape, seed: int, tag: int, dtype: str = "bf16", device="cuda"):
+    """A [shape] tensor ~ N(0,1) drawn on the GPU by torch's generator seeded
+    with (seed, tag), rounded once to the storage dtype (bf16: torch's
+    round-to-nearest-even from float32). For large workloads whose host draw
+    would take minutes; tests copy back the rows the oracle reads. Same
+    distribution as ``normal_rows``, not the same values."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + int(tag))
+    x = torch.randn(tuple(shape), generator=g, device=device)
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    if dtype == "f32":
+        return x
+    raise ValueError(dtype)
+

@@ -27,3 +27,18 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _device_guards(request):
+    """Check the guard bytes of every guarded output after each GPU test."""
+    if "gpu" not in request.keywords:
+        yield
+        return
+    from . import gpu_util
+    gpu_util.reset_guards()
+    yield
+    import torch
+    torch.cuda.synchronize()
+    gpu_util.check_guards()
+

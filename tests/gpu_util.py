@@ -13,6 +13,62 @@ import torch
 
 from inputs import gen
 
+# ---------------------------------------------------------------- guard canaries
+# Device outputs are placed inside a larger allocation whose bytes before and
+# after the tensor hold a fixed pattern; after each GPU test the patterns are
+# compared (tests/conftest.py), so a kernel that writes outside its output is
+# caught even when the write lands in memory no other check reads.
+GUARD_BYTES = 4096          # a multiple of 256: the tensor keeps the allocation's alignment
+GUARD_PATTERN = 0xA5
+_guards = []
+
+
+def guarded_empty(shape, dtype, fill=None, device="cuda") -> torch.Tensor:
+    """A contiguous device tensor of `shape`/`dtype` with guard bytes around
+    it; filled with `fill` when given (else the guard pattern)."""
+    shape = tuple(int(x) for x in shape)
+    esz = torch.empty((), dtype=dtype).element_size()
+    n = int(np.prod(shape)) if shape else 1
+    body = -(-n * esz // 256) * 256
+    buf = torch.full((GUARD_BYTES + body + GUARD_BYTES,), GUARD_PATTERN, dtype=torch.uint8, device=device)
+    t = buf[GUARD_BYTES:GUARD_BYTES + n * esz].view(dtype).view(shape)
+    if fill is not None:
+        t.fill_(fill)
+    _guards.append((buf, n * esz, f"{tuple(shape)} {dtype}"))
+    return t
+
+
+def guarded_like(x: torch.Tensor) -> torch.Tensor:
+    t = guarded_empty(x.shape, x.dtype, device=x.device)
+    t.copy_(x)
+    return t
+
+
+def reset_guards():
+    _guards.clear()
+
+
+def check_guards():
+    """Assert that no guard byte of any guarded tensor changed."""
+    bad = []
+    for buf, nbytes, what in _guards:
+        head = buf[:GUARD_BYTES]
+        tail = buf[GUARD_BYTES + nbytes:]
+        if bool((head != GUARD_PATTERN).any()) or bool((tail != GUARD_PATTERN).any()):
+            bad.append(what)
+    _guards.clear()
+    assert not bad, f"a kernel wrote outside its output: guard bytes changed around {bad}"
+
+
+def guarded_cache(*args, **kw):
+    """A SepCache whose k, v, pos, tok and state live in guarded buffers."""
+    from kv_cache_compression_sep_amd import SepCache
+    c = SepCache(*args, **kw)
+    c.k, c.v = guarded_like(c.k), guarded_like(c.v)
+    c.pos, c.tok, c.state = guarded_like(c.pos), guarded_like(c.tok), guarded_like(c.state)
+    return c
+
+
 TOL = {"bf16": 1e-2, "f32": 1e-5}
 
 

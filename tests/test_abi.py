@@ -261,3 +261,42 @@ def test_mask_compact_argument_checks(lib):
     assert f(nsep=65) == E.SEP_ERR_SHAPE
     assert f(flags=FAKE + 1) == E.SEP_ERR_ALIGN
     assert f(ids=FAKE + 4) == E.SEP_ERR_ALIGN
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+@pytest.mark.timeout(600)
+def test_validation_under_address_and_undefined_behavior_sanitizers(tmp_path):
+    """api.hip's argument validation, compiled for the host only with ASan and
+    UBSan (no recovery) and linked against stand-in launchers that count
+    calls (tests/abi_host/stubs.hip), driven through every entry point's
+    status codes by tests/abi_host/driver.cpp."""
+    hipcc = _hipcc()
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    here = os.path.join(ROOT, "tests", "abi_host")
+    csrc = os.path.join(ROOT, "kv_cache_compression_sep_amd", "csrc")
+    inc = [f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}"]
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all"]
+    objs = []
+    for src in (os.path.join(csrc, "api.hip"), os.path.join(here, "stubs.hip"), os.path.join(here, "driver.cpp")):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        lang = ["-x", "hip", "--cuda-host-only"]          # host code only; the driver needs HIP's headers
+        cmd = [hipcc, *lang, "-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", *san, *inc, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-4000:]
+        objs.append(obj)
+    exe = str(tmp_path / "abi_driver")
+    r = subprocess.run([hipcc, *san, *objs, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "abi validation ok" in r.stdout

@@ -20,7 +20,7 @@ from inputs import configs, gen
 from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache,
                                           sep_attn_decode, sep_cache_update)
 
-from .gpu_util import check_close, from_dev, slots_of, to_dev
+from .gpu_util import check_close, from_dev, guarded_cache, guarded_empty, slots_of, to_dev
 
 pytestmark = pytest.mark.gpu
 SEP_IDS = list(range(8))
@@ -107,7 +107,7 @@ def single_token_updates(params, policy):
     a, s, p, w = params
     T = min(3 * (a + s + p + w) + 50, 1400)
     st = Stream(zlib.crc32(repr(params).encode()), 2, 4, 2, 64, T, 0.3)
-    cache = SepCache(2, 2, 64, a, s, p, w, policy=policy)
+    cache = guarded_cache(2, 2, 64, a, s, p, w, policy=policy)
     sims = [sim_for(params, policy) for _ in range(2)]
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
     every = max(1, T // 60)
@@ -154,8 +154,8 @@ def bulk_equals_single(params, mode, policy):
     T = min(4 * (a + s + p + w) + 77, 2000)
     st = Stream(zlib.crc32(repr(params).encode()) + 1, 3, 4, 2, 128, T, 0.25)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    one = SepCache(3, 2, 128, a, s, p, w, policy=policy)
-    bulk = SepCache(3, 2, 128, a, s, p, w, policy=policy)
+    one = guarded_cache(3, 2, 128, a, s, p, w, policy=policy)
+    bulk = guarded_cache(3, 2, 128, a, s, p, w, policy=policy)
     for t in range(T):
         st.push_gpu(one, t, t + 1, d_sep)
     cuts = _cuts(T, mode, params, np.random.default_rng(T))
@@ -192,7 +192,7 @@ def test_decode_matches_oracle(case):
     policy = case[9] if len(case) > 9 else 0
     st = Stream(zlib.crc32(repr(case).encode()), B, Hq, Hkv, D, T + 40, 0.2)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    cache = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
+    cache = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy)
     sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     st.push_gpu(cache, 0, T, d_sep)
     for b in range(B):
@@ -202,7 +202,9 @@ def test_decode_matches_oracle(case):
         q = to_dev(np.ascontiguousarray(st.q[:, t]), "bf16")
         kn = to_dev(np.ascontiguousarray(st.k[:, :, t]), "bf16")
         vn = to_dev(np.ascontiguousarray(st.v[:, :, t]), "bf16")
-        out, lse = sep_attn_decode(q, kn, vn, cache, scale, return_lse=True)
+        out, lse = sep_attn_decode(q, kn, vn, cache, scale, return_lse=True,
+                                   out=guarded_empty((B, Hq, D), torch.bfloat16),
+                                   lse=guarded_empty((B, Hq), torch.float32))
         o = from_dev(out)
         l_gpu = from_dev(lse)
         for b in range(B):

@@ -25,7 +25,7 @@ from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCU
                                           sep_attn_decode_rope, sep_cache_update, sep_decode_update,
                                           sep_rope_table)
 
-from .gpu_util import check_close, from_dev, to_dev
+from .gpu_util import check_close, from_dev, guarded_cache, guarded_empty, to_dev
 from .test_gpu_cache_decode import SEP_IDS, Stream, check_cache, sim_for
 
 pytestmark = pytest.mark.gpu
@@ -49,8 +49,8 @@ def test_fused_step_equals_two_calls_and_oracle(case):
     print(f"decode+update case {case}", flush=True)
     st = Stream(zlib.crc32(repr(("fused", case)).encode()), B, Hq, Hkv, D, T0 + steps, 0.25)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    fused = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
-    plain = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
+    fused = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy)
+    plain = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy)
     sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     if T0 > 0:
         st.push_gpu(fused, 0, T0, d_sep)
@@ -64,7 +64,9 @@ def test_fused_step_equals_two_calls_and_oracle(case):
         kn = to_dev(np.ascontiguousarray(st.k[:, :, t]), "bf16")
         vn = to_dev(np.ascontiguousarray(st.v[:, :, t]), "bf16")
         ids = to_dev(np.ascontiguousarray(st.ids[:, t]))
-        of, lf = sep_decode_update(q, kn, vn, ids, fused, d_sep, scale, rope=table, return_lse=True)
+        of, lf = sep_decode_update(q, kn, vn, ids, fused, d_sep, scale, rope=table, return_lse=True,
+                                   out=guarded_empty((B, Hq, D), torch.bfloat16),
+                                   lse=guarded_empty((B, Hq), torch.float32))
         if rope:
             op, lp = sep_attn_decode_rope(q, kn, vn, plain, table, scale, return_lse=True)
         else:

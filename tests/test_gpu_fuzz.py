@@ -1,0 +1,184 @@
+"""Randomised small cases over the whole path, each run twice.
+
+Prefill: S in [1, 300], a in [0, 8], n in [1, S + 5], separator probability
+in {0, 0.05, 0.5, 1}, GQA ratio in {1, 2, 4, 8}, D in {64, 128}, both dtypes.
+Flags, tile classes, the dense mask, ranks, compacted positions and counts
+must equal the oracle bit for bit; outputs and log-sum-exps must be within
+tolerance of it. Cache: a in [0, 8], s, p, w in [1, 70] (p + 1 > 64 crosses a
+wavefront) or StreamingLLM mode, every policy, bulk and single updates,
+decode + update steps.
+
+Each case runs twice on fresh buffers and every output of the two runs must
+be identical bit for bit (no kernel of the forward path uses atomics whose
+order could vary): a race in a ballot or scan shows up as a difference. The
+loop stops at its first failing case, which it prints before running.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from inputs import gen
+from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, sep_attn_prefill,
+                                          sep_cache_update, sep_decode_update, sep_index_compact, sep_mask_build)
+
+from .gpu_util import check_close, from_dev, guarded_cache, guarded_empty, slots_of, to_dev
+
+pytestmark = pytest.mark.gpu
+SEP = list(range(8))
+LSE_TOL = {"bf16": 2.5e-3, "f32": 1e-5}
+
+
+def _prefill_once(ids, q, k, v, a, n, dtype, tq, tk):
+    B, Hq, S, D = q.shape
+    d_ids = to_dev(ids)
+    d_sep = to_dev(np.asarray(SEP, np.int32))
+    flags, tc, dm = sep_mask_build(d_ids, d_sep, a, n, tiles=(tq, tk), is_sep=guarded_empty((B, S), torch.uint8),
+                                   tile_class=guarded_empty((B, -(-S // tq), -(-S // tk)), torch.uint8),
+                                   dense_mask=guarded_empty((B, S, S), torch.uint8))
+    rank, sep_pos, count = sep_index_compact(flags, rank=guarded_empty((B, S + 1), torch.int32),
+                                             sep_pos=guarded_empty((B, S), torch.int32),
+                                             count=guarded_empty((B,), torch.int32))
+    odt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out, lse = sep_attn_prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), flags, rank, sep_pos, a, n,
+                                1.0 / math.sqrt(D), return_lse=True, out=guarded_empty((B, Hq, S, D), odt),
+                                lse=guarded_empty((B, Hq, S), torch.float32))
+    torch.cuda.synchronize()
+    res = {name: t.cpu() for name, t in (("flags", flags), ("tiles", tc), ("dense", dm), ("rank", rank),
+                                          ("sep_pos", sep_pos), ("count", count), ("lse", lse))}
+    res["out"] = out.view(torch.int16).cpu() if dtype == "bf16" else out.cpu()
+    return res, out
+
+
+def test_fuzz_prefill_path_twice():
+    rng = np.random.default_rng(20241203)
+    for case in range(48):
+        B = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 301))
+        a = int(rng.integers(0, 9))
+        n = int(rng.integers(1, S + 6))
+        p_sep = float(rng.choice([0.0, 0.05, 0.5, 1.0]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.integers(1, 3))
+        D = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        tq, tk = int(rng.integers(1, 130)), int(rng.integers(1, 130))
+        desc = dict(case=case, B=B, S=S, a=a, n=n, p_sep=p_sep, Hq=G * Hkv, Hkv=Hkv, D=D, dtype=dtype, tiles=(tq, tk))
+        print(f"fuzz prefill {desc}", flush=True)
+        ids = np.where(rng.random((B, S)) < p_sep, rng.integers(0, 8, (B, S)),
+                       rng.integers(8, 1000, (B, S))).astype(np.int32)
+        q = gen.round_storage(rng.standard_normal((B, G * Hkv, S, D)), dtype)
+        k = gen.round_storage(rng.standard_normal((B, Hkv, S, D)), dtype)
+        v = gen.round_storage(rng.standard_normal((B, Hkv, S, D)), dtype)
+        first, out = _prefill_once(ids, q, k, v, a, n, dtype, tq, tk)
+        second, _ = _prefill_once(ids, q, k, v, a, n, dtype, tq, tk)
+        for name in first:
+            assert torch.equal(first[name], second[name]), (desc, name, "differs between two runs")
+        o = from_dev(out)
+        scale = 1.0 / math.sqrt(D)
+        for b in range(B):
+            f_ref = oracle.is_sep(ids[b], SEP)
+            M = oracle.sep_mask(f_ref, a, n)
+            r_ref, p_ref, c_ref = oracle.compact(f_ref)
+            assert np.array_equal(first["flags"][b].numpy(), f_ref.astype(np.uint8)), desc
+            assert np.array_equal(first["dense"][b].numpy(), M.astype(np.uint8)), desc
+            assert np.array_equal(first["tiles"][b].numpy(), oracle.tile_class(M, tq, tk)), desc
+            assert np.array_equal(first["rank"][b].numpy(), r_ref), desc
+            assert np.array_equal(first["sep_pos"][b].numpy(), p_ref), desc
+            assert int(first["count"][b]) == c_ref, desc
+            o_ref, l_ref = oracle.attention(gen.storage_to_f64(q[b], dtype), gen.storage_to_f64(k[b], dtype),
+                                            gen.storage_to_f64(v[b], dtype), M, scale)
+            check_close(o[b], o_ref, dtype, str(desc))
+            assert np.max(np.abs(first["lse"][b].numpy() - l_ref)) < LSE_TOL[dtype], desc
+
+
+def _cache_case(rng):
+    a = int(rng.integers(0, 9))
+    if rng.random() < 0.15:
+        s = p = 0
+        policy = 0
+    else:
+        s, p = int(rng.integers(1, 71)), int(rng.integers(1, 71))
+        policy = int(rng.choice([0, SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM]))
+    w = int(rng.integers(1, 71))
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    T0 = int(rng.integers(0, 301))
+    steps = int(rng.integers(1, 25))
+    p_sep = float(rng.choice([0.0, 0.05, 0.5, 1.0]))
+    return dict(a=a, s=s, p=p, w=w, policy=policy, B=B, Hkv=Hkv, Hq=G * Hkv, D=D, T0=T0, steps=steps, p_sep=p_sep)
+
+
+def _cache_run(c, ids, k, v, q, cuts, d_sep):
+    """Bulk-ingest the first T0 tokens in the given chunks, then decode +
+    update `steps` tokens one by one. Returns everything it wrote."""
+    B, Hkv, D, Hq = c["B"], c["Hkv"], c["D"], c["Hq"]
+    cache = guarded_cache(B, Hkv, D, c["a"], c["s"], c["p"], c["w"], policy=c["policy"])
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        sep_cache_update(cache, to_dev(np.ascontiguousarray(k[:, :, t0:t1]), "bf16"),
+                         to_dev(np.ascontiguousarray(v[:, :, t0:t1]), "bf16"),
+                         to_dev(np.ascontiguousarray(ids[:, t0:t1])), d_sep)
+    outs = []
+    T0 = cuts[-1]
+    for t in range(T0, T0 + c["steps"]):
+        o, lse = sep_decode_update(to_dev(np.ascontiguousarray(q[:, t]), "bf16"),
+                                   to_dev(np.ascontiguousarray(k[:, :, t]), "bf16"),
+                                   to_dev(np.ascontiguousarray(v[:, :, t]), "bf16"),
+                                   to_dev(np.ascontiguousarray(ids[:, t])), cache, d_sep, return_lse=True,
+                                   out=guarded_empty((B, Hq, D), torch.bfloat16),
+                                   lse=guarded_empty((B, Hq), torch.float32))
+        outs.append((o.view(torch.int16).cpu(), lse.cpu()))
+    torch.cuda.synchronize()
+    return cache, outs
+
+
+def test_fuzz_cache_path_twice():
+    rng = np.random.default_rng(20241204)
+    d_sep = to_dev(np.asarray(SEP, np.int32))
+    for case in range(40):
+        c = _cache_case(rng)
+        print(f"fuzz cache case {case}: {c}", flush=True)
+        B, Hkv, Hq, D, T0, steps = c["B"], c["Hkv"], c["Hq"], c["D"], c["T0"], c["steps"]
+        T = T0 + steps
+        ids = np.where(rng.random((B, T)) < c["p_sep"], rng.integers(0, 8, (B, T)),
+                       rng.integers(8, 1000, (B, T))).astype(np.int32)
+        k = gen.round_storage(rng.standard_normal((B, Hkv, T, D)), "bf16")
+        v = gen.round_storage(rng.standard_normal((B, Hkv, T, D)), "bf16")
+        q = gen.round_storage(rng.standard_normal((B, T, Hq, D)), "bf16")
+        cuts = sorted(set([0, T0] + rng.integers(0, T0 + 1, int(rng.integers(0, 4))).tolist()))
+        one, outs1 = _cache_run(c, ids, k, v, q, cuts, d_sep)
+        two, outs2 = _cache_run(c, ids, k, v, q, cuts, d_sep)
+        for name in ("pos", "tok", "state"):
+            assert torch.equal(getattr(one, name), getattr(two, name)), (c, name, "differs between two runs")
+        for (o1, l1), (o2, l2) in zip(outs1, outs2):
+            assert torch.equal(o1, o2) and torch.equal(l1, l2), (c, "decode differs between two runs")
+        kc1, kc2 = one.k.view(torch.int16).cpu().numpy(), two.k.view(torch.int16).cpu().numpy()
+        vc1, vc2 = one.v.view(torch.int16).cpu().numpy(), two.v.view(torch.int16).cpu().numpy()
+        scale = 1.0 / math.sqrt(D)
+        for b in range(B):
+            sim = oracle.CacheSim(c["a"], c["s"], c["p"], c["w"], SEP, dynamic=bool(c["policy"] & SEP_POLICY_DYNAMIC),
+                                  accumulate=not (c["policy"] & SEP_POLICY_NO_ACCUM))
+            sim.push_many([oracle.Entry(t, int(ids[b, t])) for t in range(T0)])
+            for j, t in enumerate(range(T0, T)):
+                keys = [e.pos for e in sim.keys()] + [t]
+                o_ref, l_ref = oracle.decode_attention(gen.bf16_bits_to_f64(q[b, t]),
+                                                       gen.bf16_bits_to_f64(k[b][:, keys]),
+                                                       gen.bf16_bits_to_f64(v[b][:, keys]), scale)
+                o_gpu = gen.bf16_bits_to_f64(outs1[j][0][b].numpy().view(np.uint16))
+                check_close(o_gpu, o_ref, "bf16", f"{c} b {b} step {t}")
+                assert np.max(np.abs(outs1[j][1][b].numpy() - l_ref)) < 1e-3, (c, b, t)
+                sim.push(oracle.Entry(t, int(ids[b, t])))
+            pos = one.pos[b].cpu().numpy()
+            tok = one.tok[b].cpu().numpy()
+            for slots, want in zip(slots_of(one, b), sim.positions()):
+                assert pos[slots].tolist() == want, (c, b)
+                assert tok[slots].tolist() == [int(ids[b, x]) for x in want], (c, b)
+                if want:
+                    assert np.array_equal(kc1[b][:, slots], k[b][:, want].view(np.int16)), (c, b)
+                    assert np.array_equal(vc1[b][:, slots], v[b][:, want].view(np.int16)), (c, b)
+                    assert np.array_equal(kc2[b][:, slots], kc1[b][:, slots]), (c, b)
+                    assert np.array_equal(vc2[b][:, slots], vc1[b][:, slots]), (c, b)

@@ -15,7 +15,7 @@ import oracle
 from inputs import configs, gen
 from kv_cache_compression_sep_amd import sep_index_compact, sep_mask_build, sep_mask_compact
 
-from .gpu_util import to_dev
+from .gpu_util import guarded_empty, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,10 @@ def _check_flags_tiles_compact(ids, sep_ids, a, n, tiles=((64, 64), (32, 64), (1
     d_sep = to_dev(np.asarray(sep_ids, np.int32))
     want_dense = dense if dense is not None else S <= 2048
     for tq, tk in tiles:
-        flags, tc, dm = sep_mask_build(d_ids, d_sep, a, n, tiles=(tq, tk), dense=want_dense)
+        flags, tc, dm = sep_mask_build(
+            d_ids, d_sep, a, n, tiles=(tq, tk), is_sep=guarded_empty((B, S), torch.uint8),
+            tile_class=guarded_empty((B, -(-S // tq), -(-S // tk)), torch.uint8),
+            dense_mask=guarded_empty((B, S, S), torch.uint8) if want_dense else None)
         torch.cuda.synchronize()
         flags_h = flags.cpu().numpy()
         tc_h = tc.cpu().numpy()
@@ -59,7 +62,9 @@ def _check_flags_tiles_compact(ids, sep_ids, a, n, tiles=((64, 64), (32, 64), (1
             if want_dense:
                 M = oracle.sep_mask(f_ref, a, n)
                 assert np.array_equal(dm[b].cpu().numpy(), M.astype(np.uint8))
-    rank, sep_pos, count = sep_index_compact(flags)
+    rank, sep_pos, count = sep_index_compact(flags, rank=guarded_empty((B, S + 1), torch.int32),
+                                             sep_pos=guarded_empty((B, S), torch.int32),
+                                             count=guarded_empty((B,), torch.int32))
     torch.cuda.synchronize()
     rank_h, pos_h, cnt_h = rank.cpu().numpy(), sep_pos.cpu().numpy(), count.cpu().numpy()
     for b in range(B):
@@ -104,7 +109,10 @@ def test_long_prefill_workload_flags_ranks_sampled_tiles():
 
 def _check_fused(ids, sep_ids):
     B, S = ids.shape
-    flags, rank, sep_pos, count = sep_mask_compact(to_dev(ids), to_dev(np.asarray(sep_ids, np.int32)))
+    flags, rank, sep_pos, count = sep_mask_compact(
+        to_dev(ids), to_dev(np.asarray(sep_ids, np.int32)), is_sep=guarded_empty((B, S), torch.uint8),
+        rank=guarded_empty((B, S + 1), torch.int32), sep_pos=guarded_empty((B, S), torch.int32),
+        count=guarded_empty((B,), torch.int32))
     torch.cuda.synchronize()
     f_h, r_h, p_h, c_h = flags.cpu().numpy(), rank.cpu().numpy(), sep_pos.cpu().numpy(), count.cpu().numpy()
     for b in range(B):

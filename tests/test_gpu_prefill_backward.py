@@ -36,7 +36,7 @@ from inputs import configs, gen
 from kv_cache_compression_sep_amd import (sep_attn_prefill, sep_attn_prefill_backward, sep_index_compact,
                                           sep_mask_build)
 
-from .gpu_util import from_dev, to_dev
+from .gpu_util import from_dev, guarded_empty, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -52,9 +52,13 @@ def run_gpu(ids, q, k, v, dout, sep_ids, a, n, dtype, scale):
     tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
     out, lse = sep_attn_prefill(tq, tk, tv, flags, rank, sep_pos, a, n, scale, return_lse=True)
     B, Hq, S, _ = q.shape
-    delta = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    Hkv, D = k.shape[1], q.shape[3]
+    f32 = torch.float32
+    delta = guarded_empty((B, Hq, S), f32)
     gq, gk, gv = sep_attn_prefill_backward(tq, tk, tv, out, to_dev(dout, dtype), lse, flags, rank, sep_pos,
-                                           a, n, scale, delta=delta)
+                                           a, n, scale, delta=delta, dq=guarded_empty((B, Hq, S, D), f32),
+                                           dk=guarded_empty((B, Hkv, S, D), f32),
+                                           dv=guarded_empty((B, Hkv, S, D), f32))
     torch.cuda.synchronize()
     return from_dev(out), from_dev(gq), from_dev(gk), from_dev(gv), from_dev(delta)
 

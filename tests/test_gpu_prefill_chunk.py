@@ -24,7 +24,7 @@ from inputs import gen
 from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache, SepError,
                                           chunk_workspace_bytes, sep_attn_decode, sep_attn_prefill_chunk)
 
-from .gpu_util import check_close, from_dev, to_dev
+from .gpu_util import check_close, from_dev, guarded_empty, to_dev
 from .test_gpu_cache_decode import SEP_IDS, Stream, sim_for
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,11 @@ def check_chunk(st, cache, sims, t0, t1, n, d_sep, tag):
     a = cache.a
     scale = 1.0 / math.sqrt(st.D)
     q, k, v, ids = chunk_inputs(st, t0, t1)
-    out, lse = sep_attn_prefill_chunk(q, k, v, ids, cache, d_sep, n, scale, return_lse=True)
+    B, Hq, C, D = q.shape
+    ws = guarded_empty((chunk_workspace_bytes(cache, C),), torch.uint8)
+    out, lse = sep_attn_prefill_chunk(q, k, v, ids, cache, d_sep, n, scale, return_lse=True, workspace=ws,
+                                      out=guarded_empty((B, Hq, C, D), torch.bfloat16),
+                                      lse=guarded_empty((B, Hq, C), torch.float32))
     o = from_dev(out)
     l_gpu = from_dev(lse)
     for b in range(st.B):
