@@ -12,6 +12,7 @@ chunks of 1 to 1030 tokens (several query tiles, ragged tails), windows of
 with a wide window equals sep_attn_decode, and two windows on one cache
 (a model's layers) each match the oracle.
 """
+import ctypes
 import math
 import zlib
 
@@ -21,7 +22,7 @@ import torch
 
 import oracle
 from inputs import gen
-from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache, SepError,
+from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache, _lib,
                                           chunk_workspace_bytes, sep_attn_decode, sep_attn_prefill_chunk)
 
 from .gpu_util import check_close, from_dev, guarded_empty, to_dev
@@ -150,6 +151,15 @@ def test_chunk_rejects_a_small_workspace():
     kv = torch.zeros((1, 2, C, 128), dtype=torch.bfloat16, device="cuda")
     ids = torch.zeros((1, C), dtype=torch.int32, device="cuda")
     sep = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    ws = torch.empty((chunk_workspace_bytes(cache, C) - 256,), dtype=torch.uint8, device="cuda")
-    with pytest.raises(SepError):
+    need = chunk_workspace_bytes(cache, C)
+    ws = torch.empty((need - 256,), dtype=torch.uint8, device="cuda")
+    # the binding refuses it before any C call ...
+    with pytest.raises(ValueError):
         sep_attn_prefill_chunk(q, kv, kv, ids, cache, sep, 8, workspace=ws)
+    # ... and so does the C entry point, which launches nothing then
+    out = torch.empty_like(q)
+    st = cache.struct()
+    code = _lib.load().sep_attn_prefill_chunk(q.data_ptr(), kv.data_ptr(), kv.data_ptr(), ids.data_ptr(), C,
+                                              sep.data_ptr(), 1, ctypes.byref(st), 8, 8, 0.088, ws.data_ptr(),
+                                              need - 256, out.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+    assert code == _lib.SEP_ERR_WORKSPACE
