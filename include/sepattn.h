@@ -410,6 +410,31 @@ int sep_decode_update(const void* q, const void* k_new, const void* v_new, const
                       const int32_t* sep_ids, int n_sep_ids, const sep_cache* cache, int Hq, float scale,
                       const float* rope, int rope_npos, void* out, float* lse, hipStream_t stream);
 
+/*
+ * sep_attn_prefill_backward_noalloc - sep_attn_prefill_backward without the
+ * delta workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops that forbid hipMalloc).
+ *
+ * Arguments, results, arithmetic and status codes are those of
+ * sep_attn_prefill_backward. The per-row sums delta live instead in a fixed
+ * device array inside the library (one copy per GPU, held until the process
+ * ends) of SEP_NOALLOC_MAX_ROWS floats (16 MiB): B * Hq * S must not exceed
+ * SEP_NOALLOC_MAX_ROWS, else SEP_ERR_WORKSPACE and nothing is launched. The
+ * array's address is looked up on the first call from each device, which
+ * must be the calling thread's current device and the device of `stream`.
+ * Nothing is allocated or freed, by this call or by any call it makes.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (concurrent streams, or threads) race on it and must be serialised by
+ * the caller. The array holds no state between calls (delta is rewritten in
+ * full before it is read).
+ */
+#define SEP_NOALLOC_MAX_ROWS (1 << 22)
+int sep_attn_prefill_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                      const void* dout, const float* lse, int dtype, int B, int Hq, int Hkv,
+                                      int S, int D, const uint8_t* is_sep, const int32_t* rank,
+                                      const int32_t* sep_pos, int a, int n, float scale, float* dq, float* dk,
+                                      float* dv, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

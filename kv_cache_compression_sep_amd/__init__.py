@@ -24,6 +24,7 @@ from . import _lib
 from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 
 __all__ = ["sep_mask_build", "sep_index_compact", "sep_mask_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
+           "sep_attn_prefill_backward_noalloc", "SEP_NOALLOC_MAX_ROWS",
            "sep_attn_decode", "sep_attn_decode_rope", "sep_decode_update", "sep_rope_table", "sep_attn_prefill_chunk",
            "chunk_workspace_bytes",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
@@ -208,6 +209,41 @@ def sep_attn_prefill_backward(q, k, v, out, dout, lse, is_sep, rank, sep_pos, a:
     _lib.check("sep_attn_prefill_backward", code)
     return dq, dk, dv
 
+
+def sep_attn_prefill_backward_noalloc(q, k, v, out, dout, lse, is_sep, rank, sep_pos, a: int, n: int,
+                                      scale: float | None, dq, dk, dv):
+    """sep_attn_prefill_backward with its per-row workspace in a fixed device
+    array of the library (no allocation by the library or by this binding;
+    the caller passes dq, dk, dv). B * Hq * S <= SEP_NOALLOC_MAX_ROWS; calls
+    that overlap on one GPU race on the array."""
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, None, 4)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise ValueError("q, k, v, out, dout must share a dtype")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k/v must be [B, Hkv, S, D]; out/dout [B, Hq, S, D]")
+    if any(t.device != dev for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out, dout must be on one device")
+    _need_shape(lse, "lse", (B, Hq, S), torch.float32, dev)
+    _need_index(is_sep, rank, sep_pos, B, S, dev)
+    _need_shape(dq, "dq", (B, Hq, S, D), torch.float32, dev)
+    _need_shape(dk, "dk", (B, Hkv, S, D), torch.float32, dev)
+    _need_shape(dv, "dv", (B, Hkv, S, D), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    code = lib.sep_attn_prefill_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                 dout.data_ptr(), lse.data_ptr(), _dtype_code(q), B, Hq, Hkv, S, D,
+                                                 is_sep.data_ptr(), rank.data_ptr(), sep_pos.data_ptr(), a, n,
+                                                 float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream())
+    _lib.check("sep_attn_prefill_backward_noalloc", code)
+    return dq, dk, dv
+
+
+SEP_NOALLOC_MAX_ROWS = 1 << 22
 
 # cache policies (sep_cache.policy in include/sepattn.h)
 SEP_POLICY_DYNAMIC = 1     # compress when the whole cache exceeds c = a + s + p + w

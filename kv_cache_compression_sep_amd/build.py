@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsepattn.so")
 SOURCES = ["api.hip", "mask.hip", "compact.hip", "prefill.hip", "prefill_bf16.hip", "prefill_bwd.hip",
-           "prefill_bwd_bf16.hip", "cache.hip", "decode.hip", "chunk.hip"]
+           "prefill_bwd_bf16.hip", "cache.hip", "decode.hip", "chunk.hip", "noalloc.hip"]
 # Per-source code generation: the bf16 backward kernels keep their MFMA
 # accumulators in VGPRs (with AGPRs as the accumulators the compiler copies
 # them between the two files every tile).

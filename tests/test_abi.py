@@ -300,3 +300,24 @@ def test_validation_under_address_and_undefined_behavior_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "abi validation ok" in r.stdout
+
+
+def test_noalloc_backward_argument_checks(lib):
+    """The no-alloc backward checks its arguments like the backward, then
+    refuses more query rows than its fixed array holds, all before any HIP
+    call."""
+    f = lib.sep_attn_prefill_backward_noalloc
+
+    def call(S=64, q=FAKE, dq=FAKE, B=1, Hq=32):
+        return f(q, FAKE, FAKE, FAKE, FAKE, FAKE, 1, B, Hq, 8, S, 128, FAKE, FAKE, FAKE, 4, 16, 0.088, dq, FAKE,
+                 FAKE, None)
+    rows = 1 << 22
+    assert call(q=None) == _lib.SEP_ERR_NULL
+    assert call(dq=None) == _lib.SEP_ERR_NULL
+    assert call(dq=FAKE + 4) == _lib.SEP_ERR_ALIGN
+    assert call(S=0) == _lib.SEP_ERR_SHAPE
+    assert call(S=rows // 32 + 1) == _lib.SEP_ERR_WORKSPACE
+    assert call(S=rows // 64 + 1, B=2) == _lib.SEP_ERR_WORKSPACE
+    assert call(S=2_000_000, B=2_000_000, Hq=2_000_000 // 8 * 8) == _lib.SEP_ERR_SHAPE   # group > 16 first
+    assert call(S=1 << 21, B=1 << 30, Hq=16) == _lib.SEP_ERR_WORKSPACE
+
