@@ -238,6 +238,15 @@ int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const
  *          [7] arrival count of sep_decode_update, 0 between calls.
  *          The ring's entries, oldest first, are the slots
  *          a + (sep_head - sep_count + i) mod s, i = 0 .. sep_count-1.
+ *   work   device work buffer of work_bytes bytes (256-byte aligned), or
+ *          NULL. With few (sequence, kv head) pairs (B * Hkv < 256) and
+ *          work_bytes >= sep_decode_work_bytes(cache, Hq), the decode calls
+ *          (sep_attn_decode, sep_attn_decode_rope, sep_decode_update) split
+ *          each list over several workgroups and keep their partial results
+ *          here; otherwise one workgroup reads each list and work is unused.
+ *          Either way the result of a given (cache, Hq) is deterministic,
+ *          and the three calls agree bit for bit. Decode calls that share a
+ *          work buffer must not overlap.
  * An empty cache is state all zero and pos/tok all -1 (sep_cache_reset).
  * K/V rows of empty slots are never read.
  * Contract [P1 "Streaming 参数约束"]: a >= 0, w >= 1, and either s >= 1 and
@@ -253,7 +262,17 @@ typedef struct {
   int32_t* tok;
   int64_t* state;
   int32_t policy;
+  void* work;
+  size_t work_bytes;
 } sep_cache;
+
+/*
+ * sep_decode_work_bytes - the work buffer (sep_cache.work) the decode calls
+ * need to split their lists for Hq query heads: 0 when they never split
+ * (B * Hkv >= 256) or the cache is invalid. Split decode [P2 §1.3, only the
+ * retained KV are read: more workgroups read each list at once].
+ */
+size_t sep_decode_work_bytes(const sep_cache* cache, int Hq);
 
 /*
  * sep_cache_reset - make every sequence of the cache empty (state = 0,
@@ -301,7 +320,8 @@ int sep_cache_update(const sep_cache* cache, const void* k_new, const void* v_ne
  *          cache as it is (tokens before it) plus itself; call
  *          sep_cache_update afterwards to insert it.
  *   scale  > 0; out [B, Hq, D] (bf16); lse [B, Hq] float32 out or NULL.
- * Reads the cache, never writes it; needs no workspace.
+ * Reads the cache, never writes its blocks or state (only, in split mode,
+ * the work buffer; see sep_cache).
  * Returns SEP_OK, SEP_ERR_NULL, SEP_ERR_SHAPE, SEP_ERR_PARAM, SEP_ERR_DTYPE,
  * SEP_ERR_ALIGN, SEP_ERR_HIP.
  */

@@ -26,7 +26,7 @@ from ._lib import SepError, SEP_BF16, SEP_F32  # noqa: F401
 __all__ = ["sep_mask_build", "sep_index_compact", "sep_mask_compact", "sep_attn_prefill", "sep_attn_prefill_backward",
            "sep_attn_prefill_backward_noalloc", "SEP_NOALLOC_MAX_ROWS",
            "sep_attn_decode", "sep_attn_decode_rope", "sep_decode_update", "sep_rope_table", "sep_attn_prefill_chunk",
-           "chunk_workspace_bytes",
+           "chunk_workspace_bytes", "decode_work_bytes",
            "sep_cache_update", "sep_cache_reset", "SepCache", "SepError", "library_version",
            "SEP_POLICY_DYNAMIC", "SEP_POLICY_NO_ACCUM"]
 
@@ -255,10 +255,15 @@ class SepCache:
     """A batch of four-block caches in device memory (layout: see sep_cache
     in include/sepattn.h). ``policy`` combines SEP_POLICY_DYNAMIC and
     SEP_POLICY_NO_ACCUM; the recent ring has p + w slots, or s + p + w under
-    SEP_POLICY_DYNAMIC."""
+    SEP_POLICY_DYNAMIC. With ``split`` (the default) the cache also carries
+    the work buffer that lets decode split each list over several workgroups
+    when there are few (sequence, kv head) pairs (sized for up to 16 query
+    heads per kv head)."""
+
+    MAX_GROUP = 16
 
     def __init__(self, B: int, Hkv: int, D: int, a: int, s: int, p: int, w: int,
-                 dtype=torch.bfloat16, device="cuda", policy: int = 0):
+                 dtype=torch.bfloat16, device="cuda", policy: int = 0, split: bool = True):
         self.B, self.Hkv, self.D = B, Hkv, D
         self.a, self.s, self.p, self.w = a, s, p, w
         self.policy = int(policy)
@@ -272,6 +277,11 @@ class SepCache:
         self.pos = torch.full((B, self.slots), -1, dtype=torch.int32, device=dev)
         self.tok = torch.full((B, self.slots), -1, dtype=torch.int32, device=dev)
         self.state = torch.zeros((B, STATE_WORDS), dtype=torch.int64, device=dev)
+        self.work = None
+        if split:
+            need = decode_work_bytes(self, Hkv * self.MAX_GROUP)
+            if need:
+                self.work = torch.empty((need,), dtype=torch.uint8, device=dev)
 
     def struct(self) -> _lib.SepCacheStruct:
         """The sep_cache view of this cache, after checking that its tensors
@@ -282,10 +292,16 @@ class SepCache:
         _need_shape(self.pos, "cache.pos", (self.B, self.slots), torch.int32, dev)
         _need_shape(self.tok, "cache.tok", (self.B, self.slots), torch.int32, dev)
         _need_shape(self.state, "cache.state", (self.B, STATE_WORDS), torch.int64, dev)
+        work, work_bytes = None, 0
+        if self.work is not None:
+            _need(self.work, "cache.work", torch.uint8, 1)
+            if self.work.device != dev:
+                raise ValueError("cache.work must be on the cache's device")
+            work, work_bytes = self.work.data_ptr(), self.work.numel()
         return _lib.SepCacheStruct(self.a, self.s, self.p, self.w, self.B, self.Hkv, self.D,
                                    _dtype_code(self.k), self.k.data_ptr(), self.v.data_ptr(),
                                    self.pos.data_ptr(), self.tok.data_ptr(), self.state.data_ptr(),
-                                   self.policy)
+                                   self.policy, work, work_bytes)
 
     def reset(self):
         sep_cache_reset(self)
@@ -325,6 +341,13 @@ def sep_cache_update(cache: SepCache, k_new, v_new, ids_new, sep_ids):
                                 _ptr(sep_ids) if sep_ids.numel() else None, sep_ids.numel(),
                                 _stream())
     _lib.check("sep_cache_update", code)
+
+
+def decode_work_bytes(cache: "SepCache", Hq: int) -> int:
+    """Work-buffer bytes the decode calls need to split their lists for Hq
+    query heads (0: they never split this cache)."""
+    st = cache.struct()
+    return int(_lib.load().sep_decode_work_bytes(ctypes.byref(st), Hq))
 
 
 def chunk_workspace_bytes(cache: "SepCache", C: int) -> int:

@@ -38,6 +38,7 @@ class SepCacheStruct(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("k", c_vp), ("v", c_vp), ("pos", c_vp), ("tok", c_vp), ("state", c_vp),
         ("policy", ctypes.c_int32),
+        ("work", c_vp), ("work_bytes", ctypes.c_size_t),
     ]
 
 
@@ -58,6 +59,7 @@ SIGNATURES = {
                                  c_int, c_vp]),
     "sep_mask_compact": (c_int, [c_vp, c_int, c_int, c_vp, c_int, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "sep_chunk_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(SepCacheStruct), c_int]),
+    "sep_decode_work_bytes": (ctypes.c_size_t, [ctypes.POINTER(SepCacheStruct), c_int]),
     "sep_attn_prefill_chunk": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, ctypes.POINTER(SepCacheStruct),
                                        c_int, c_int, c_float, c_vp, ctypes.c_size_t, c_vp, c_vp, c_vp]),
     "sep_rope_table": (c_int, [ctypes.c_double, c_int, c_int, c_vp, c_vp]),

@@ -39,6 +39,7 @@ int check_cache(const sep_cache* c) {
 int check_cache_kv(const sep_cache* c) {
   if (c->k == nullptr || c->v == nullptr) return SEP_ERR_NULL;
   if (!aligned16(c->k) || !aligned16(c->v)) return SEP_ERR_ALIGN;
+  if (c->work != nullptr && (reinterpret_cast<uintptr_t>(c->work) & 255) != 0) return SEP_ERR_WORKSPACE;
   return SEP_OK;
 }
 
@@ -197,6 +198,12 @@ int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const s
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return SEP_ERR_ALIGN;
   return hip_status(sep::launch_decode(q, k_new, v_new, *cache, Hq, scale, nullptr, out, lse, stream));
+}
+
+size_t sep_decode_work_bytes(const sep_cache* cache, int Hq) {
+  if (check_cache(cache) != SEP_OK || Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return 0;
+  if (!sep::decode_uses_wide(*cache)) return 0;
+  return sep::decode_split_bytes(*cache, Hq);
 }
 
 size_t sep_chunk_workspace_bytes(const sep_cache* cache, int C) {

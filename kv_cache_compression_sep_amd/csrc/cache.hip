@@ -637,10 +637,17 @@ __device__ __forceinline__ void update_body(const CacheArgs& A) {
         val[u] = ld_global_nt(reinterpret_cast<const u32x4*>(src + 16 * (col[u] % cpr)));
       }
     }
-    // R after the push holds t0 + 1 - cend0 entries
+    // R after the push holds t0 + 1 - cend0 entries. Without a separator
+    // ring (StreamingLLM: s = p = 0, ring of w slots) a compression drops
+    // R's oldest r_after - w entries and keeps nothing; the one it drops in
+    // a single-token step is the position t0 - w, whose slot the new token
+    // takes, so that compression is a slot write like the others.
     const int64_t r_after = t0 + 1 - (A.a + ncomp);
     const int64_t r_cap = DYN ? (A.s + A.p + A.w - cnt0) : (A.p + A.w);
-    if (t0 < A.a || r_after <= r_cap) {
+    if (t0 < A.a || r_after <= r_cap || A.s == 0) {
+      // R holds at most w entries before the push when s == 0, so at most one
+      // is dropped here
+      const int64_t dropped = (A.s == 0 && t0 >= A.a && r_after > A.w) ? r_after - A.w : 0;
       const int slot = t0 < A.a ? static_cast<int>(t0) : slot_r(t0, A.a, A.s, rw);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -664,6 +671,7 @@ __device__ __forceinline__ void update_body(const CacheArgs& A) {
         st_global(A.pos + static_cast<int64_t>(b) * A.c + slot, static_cast<int32_t>(t0));
         st_global(A.tok + static_cast<int64_t>(b) * A.c + slot, id);
         st_global(stw, t0 + 1);
+        if (dropped > 0) st_global(stw + 1, ncomp + dropped);
         st_global(stw + 4, ncomp);
       }
       return;
@@ -852,7 +860,7 @@ template <int D, bool ROPE, bool DYN>
 __global__ void __launch_bounds__(kUpdThreads) decode_update_kernel(DecodeArgs A, CacheArgs U) {
   static_assert(kUpdThreads == 8 * kWave, "the decode runs with 8 waves here");
   __shared__ int last;
-  decode_body<D, 8, ROPE>(A);
+  decode_body<D, 8, ROPE>(A, blockIdx.x, blockIdx.y, 0);
   __syncthreads();
   const int64_t sw = kStateWords * static_cast<int64_t>(blockIdx.y);
   if (threadIdx.x == 0) {
@@ -862,6 +870,19 @@ __global__ void __launch_bounds__(kUpdThreads) decode_update_kernel(DecodeArgs A
   __syncthreads();
   if (!last) return;
   if (threadIdx.x == 0) U.state[sw + kArriveWord] = 0;
+  update_body<UPD_FUSED, DYN>(U);
+}
+
+// Split decode's second launch, grid (Hkv + 1, B): workgroup g < Hkv merges
+// the partials of kv head g of sequence b (blockIdx.y); workgroup Hkv then
+// runs the single-token update of sequence b. The first launch (the ranges)
+// has finished reading the cache, so the update may rewrite it.
+template <int D, bool DYN>
+__global__ void __launch_bounds__(kUpdThreads) merge_update_kernel(DecodeArgs A, CacheArgs U) {
+  if (static_cast<int>(blockIdx.x) < U.Hkv) {
+    merge_body<D>(A, blockIdx.x, blockIdx.y, kUpdThreads);
+    return;
+  }
   update_body<UPD_FUSED, DYN>(U);
 }
 
@@ -880,9 +901,29 @@ hipError_t launch_decode_update(const void* q, const void* k_new, const void* v_
                                 const int32_t* sep_ids, int n_sep, const sep_cache& c, int Hq, float scale,
                                 const float* rope, void* out, float* lse, hipStream_t st) {
   const size_t dyn = update_dyn_bytes(c);
+  if (decode_uses_split(c, Hq) && dyn <= kFusedDynMax) {
+    // the ranges, then the merge with the update in the same launch
+    const DecodeArgs A = decode_args(q, k_new, v_new, c, Hq, scale, rope, out, lse);
+    hipError_t e = launch_split_ranges(A, c, st);
+    if (e != hipSuccess) return e;
+    CacheArgs U = cache_args(c, sep_ids, n_sep, 1);
+    U.T = 1;
+    U.k_new = static_cast<const char*>(k_new);
+    U.v_new = static_cast<const char*>(v_new);
+    U.ids_new = ids_new;
+    const dim3 grid(c.Hkv + 1, c.B);
+    if (c.D == 128) {
+      if (U.dynamic) hipLaunchKernelGGL((merge_update_kernel<128, true>), grid, dim3(kUpdThreads), dyn, st, A, U);
+      else hipLaunchKernelGGL((merge_update_kernel<128, false>), grid, dim3(kUpdThreads), dyn, st, A, U);
+    } else {
+      if (U.dynamic) hipLaunchKernelGGL((merge_update_kernel<64, true>), grid, dim3(kUpdThreads), dyn, st, A, U);
+      else hipLaunchKernelGGL((merge_update_kernel<64, false>), grid, dim3(kUpdThreads), dyn, st, A, U);
+    }
+    return hipGetLastError();
+  }
   // the fused launch covers the few-pairs case, where the decode runs with 8
   // waves; otherwise the two launches it stands for
-  if (!decode_uses_wide(c) || dyn > kFusedDynMax) {
+  if (!decode_uses_wide(c) || dyn > kFusedDynMax || decode_uses_split(c, Hq)) {
     hipError_t e = launch_decode(q, k_new, v_new, c, Hq, scale, rope, out, lse, st);
     if (e != hipSuccess) return e;
     return launch_cache_update(c, k_new, v_new, ids_new, 1, sep_ids, n_sep, st);

@@ -11,10 +11,15 @@
 //   u in [.., occ)                   -> recent-ring slots of positions [rec_lo, t)
 //   u == occ                         -> the new token (k_new / v_new)
 //
-// One workgroup per (kv head, sequence) reads that list once. No split of a
-// list over workgroups: merging splits would need a device-scope release and
-// acquire per workgroup, which on this GPU write back and invalidate the L2
-// of each XCD. Waves take 32-key slices, NW slices per iteration: S^T = K Q^T
+// One workgroup per (kv head, sequence) reads that list once; or, when the
+// cache carries a work buffer and there are few (sequence, kv head) pairs,
+// ns workgroups per pair each read one range of `span` consecutive entries
+// of the list and write their unnormalised partial (running max, sum of
+// weights, weighted sum of values, per query head) to the work buffer, and a
+// second kernel merges the ns partials with the log-sum-exp rule (the
+// kernel boundary orders the two; merging inside one kernel would need a
+// device-scope release and acquire per workgroup, which on this GPU write
+// back and invalidate the L2 of each XCD). Waves take 32-key slices, NW slices per iteration: S^T = K Q^T
 // with the 16x16x32 bf16 MFMA (K rows loaded straight into the A operand,
 // Q^T of the G query heads in registers), online softmax per head column,
 // then O^T += V^T P^T with V staged transposed in the wave's LDS slice. The
@@ -48,9 +53,16 @@ struct DecodeArgs {
   uint16_t* out;
   float* lse;
   const float* rope;                             // [n_pos][D/2] (cos, sin), ROPE only
+  float* part;                                   // split mode: partials [B][Hkv][ns][G][kPartStr]; else null
   int a, s, p, w, rw, c, Hq, Hkv, G;
+  int ns, span;                                  // split mode: ranges per list, entries per range
   float scale_log2;
 };
+
+// One partial: running max (log2 domain), sum of weights, two pad words, then
+// the weighted sum of values over d (16-byte aligned rows).
+template <int D>
+constexpr int part_stride() { return D + 4; }
 
 __device__ __forceinline__ float bf16lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -69,8 +81,10 @@ __device__ __forceinline__ void rotate_pairs(u32x4& lo, u32x4& hi, const f32x4 (
   }
 }
 
+// Decode of kv head g of sequence b: the whole list (A.part null) into out /
+// lse, or range `split` of it into its partial.
 template <int D, int NW, bool ROPE>
-__device__ __forceinline__ void decode_body(const DecodeArgs& A) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, int split) {
   constexpr int NT = NW * kWave;
   constexpr int VSTR = kSlice + 8;               // V^T row stride (bf16)
   constexpr int NDB = D / 16;                    // 16-row d-blocks of O^T
@@ -88,8 +102,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
   const int G = A.G;
   const int rw = A.rw;                          // recent-ring size
   uint16_t* vt = reinterpret_cast<uint16_t*>(arena) + wave * (D * VSTR);
@@ -108,6 +120,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
   const int u_r = n_init + cnt;                  // first recent-ring entry
   const int occ = u_r + n_rec;
   const int L = occ + 1;
+  // the entries [ub, ue) this workgroup reads (all of them without a split)
+  const int ub = A.part == nullptr ? 0 : split * A.span;
+  const int ue = A.part == nullptr ? L : min(L, ub + A.span);
   int s0 = 0;                                    // ring index of the oldest separator
   if (cnt > 0) {
     s0 = (head - cnt) % A.s;
@@ -166,7 +181,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
   auto load_slice = [&](int u0, Regs& R) {
 #pragma unroll
     for (int gq = 0; gq < 2; ++gq) {
-      const int u = min(u0 + 16 * gq + lane % 16, L - 1);
+      const int u = min(u0 + 16 * gq + lane % 16, ue - 1);
       const uint16_t* kr = row_ptr(u, kbase, knew);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
@@ -179,13 +194,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
       const int dc = pi / 8;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int u = min(u0 + 4 * kq + e, L - 1);
+        const int u = min(u0 + 4 * kq + e, ue - 1);
         R.v[j][e] = *reinterpret_cast<const u32x4*>(row_ptr(u, vbase, vnew) + 8 * dc);
       }
     }
   };
 
-  const int iters = (L + NW * kSlice - 1) / (NW * kSlice);
+  const int iters = ue > ub ? (ue - ub + NW * kSlice - 1) / (NW * kSlice) : 0;
   // ROPE: (cos, sin) of this lane's pairs at its first key of the current
   // slice, u = (it NW + wave) 32 + lane % 16; its second key (u + 16) takes
   // one complex product with the angles of 16 positions. Between slices u
@@ -197,7 +212,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
   // [16 | 32 NW][lane / 16][ks][m]
   auto rstep = reinterpret_cast<f32x4(*)[4][NKS / 2 > 0 ? NKS / 2 : 1][4]>(arena + ARENA);
   auto load_angles = [&](int it) {
-    const int u = min((it * NW + wave) * kSlice + lane % 16, L - 1);
+    const int u = min(ub + (it * NW + wave) * kSlice + lane % 16, L - 1);
     const float* trow = A.rope + static_cast<int64_t>(u) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS / 2; ++ks)
@@ -210,7 +225,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
                  a[3] * d[2] + a[2] * d[3]};
   };
   Regs cur;
-  load_slice(wave * kSlice, cur);               // the first slice's K/V in flight before the table reads
+  if (iters > 0) load_slice(ub + wave * kSlice, cur);   // the first slice's K/V in flight before the table reads
   if constexpr (ROPE) {
     {                                            // the query at position occ
       const float* trow = A.rope + static_cast<int64_t>(occ) * D;
@@ -242,7 +257,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
     __syncthreads();
   }
   for (int it = 0; it < iters; ++it) {
-    const int u0 = (it * NW + wave) * kSlice;   // this wave's slice
+    const int u0 = ub + (it * NW + wave) * kSlice;   // this wave's slice
     // ---- V rows -> transposed LDS slice. Quads q (keys 4q..4q+3) go to
     //      column 8*(q%4) + 4*(q/4), so the eight keys a PV lane group needs
     //      ({4h..4h+3} and {16+4h..16+4h+3}) are contiguous.
@@ -294,7 +309,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
       s[gq] = acc;
     }
     // ---- start the next slice's loads while this one is finished
-    if (it + 1 < iters) load_slice(((it + 1) * NW + wave) * kSlice, cur);
+    if (it + 1 < iters) load_slice(ub + ((it + 1) * NW + wave) * kSlice, cur);
 
     float mx = -INFINITY;
 #pragma unroll
@@ -302,7 +317,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int u = u0 + 16 * gq + 4 * hh + r;
-        if (u >= L) s[gq][r] = -INFINITY;
+        if (u >= ue) s[gq][r] = -INFINITY;
         mx = fmaxf(mx, s[gq][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -365,6 +380,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
       o += f * red_o[(wv * 16 + hq) * (D + 1) + d];
       l += f * red_l[wv][hq];
     }
+    if (A.part != nullptr) {                    // this range's partial, unnormalised
+      float* pp = A.part + ((bg * A.ns + split) * G + hq) * part_stride<D>();
+      pp[4 + d] = o;
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = l;
+      }
+      continue;
+    }
     const int64_t orow = static_cast<int64_t>(b) * A.Hq + g * G + hq;
     const uint32_t bits = pack_bf16x2(o / l, 0.f);
     A.out[orow * D + d] = static_cast<uint16_t>(bits & 0xffffu);
@@ -372,9 +396,41 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A) {
   }
 }
 
-// Few (sequence, kv head) pairs: wider workgroups (8 waves) so that each
-// pair's list is read by more waves at once.
-inline bool decode_uses_wide(const sep_cache& c) { return c.B * c.Hkv < 256; }
+// Merge of the ns partials of kv head g of sequence b into out / lse: with
+// M the largest partial max, o = sum_i 2^(m_i - M) o_i and l = sum_i
+// 2^(m_i - M) l_i, out = o / l and lse = (M + log2 l) ln 2; a range past the
+// end of the list has m_i = -inf and weighs nothing.
+template <int D>
+__device__ __forceinline__ void merge_body(const DecodeArgs& A, int g, int b, int nthreads) {
+  constexpr int PS = part_stride<D>();
+  const int G = A.G;
+  const int64_t bg = static_cast<int64_t>(b) * A.Hkv + g;
+  for (int e = threadIdx.x; e < G * D; e += nthreads) {
+    const int hq = e / D;
+    const int d = e % D;
+    const float* pp = A.part + bg * A.ns * G * PS + hq * PS;
+    float M = -INFINITY;
+    for (int i = 0; i < A.ns; ++i) M = fmaxf(M, pp[i * G * PS]);
+    float o = 0.f, l = 0.f;
+    for (int i = 0; i < A.ns; ++i) {
+      const float m = pp[i * G * PS];
+      const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+      o += f * pp[i * G * PS + 4 + d];
+      l += f * pp[i * G * PS + 1];
+    }
+    const int64_t orow = static_cast<int64_t>(b) * A.Hq + g * G + hq;
+    const uint32_t bits = pack_bf16x2(o / l, 0.f);
+    A.out[orow * D + d] = static_cast<uint16_t>(bits & 0xffffu);
+    if (d == 0 && A.lse != nullptr) A.lse[orow] = (M + fast_log2(l)) * kLn2;
+  }
+}
+
+// waves of a split-decode workgroup: one 32-entry slice each per range unit
+constexpr int kSplitWaves = kSplitChunk / kSlice;
+static_assert(kSplitWaves * kSlice == kSplitChunk, "split ranges are whole slices");
+
+// the ranges of a split decode (decode.hip); their merge is a second launch
+hipError_t launch_split_ranges(const DecodeArgs& A, const sep_cache& c, hipStream_t st);
 
 inline DecodeArgs decode_args(const void* q, const void* k_new, const void* v_new, const sep_cache& c, int Hq,
                               float scale, const float* rope, void* out, float* lse) {
@@ -388,6 +444,13 @@ inline DecodeArgs decode_args(const void* q, const void* k_new, const void* v_ne
   A.out = static_cast<uint16_t*>(out);
   A.lse = lse;
   A.rope = rope;
+  A.part = nullptr;
+  A.ns = 1;
+  A.span = 0;
+  if (decode_uses_split(c, Hq)) {
+    A.part = static_cast<float*>(c.work);
+    decode_split_shape(c, &A.ns, &A.span);
+  }
   A.a = c.a;
   A.s = c.s;  // the separator-ring branch is only reached when cnt > 0, i.e. s >= 1
   A.p = c.p;

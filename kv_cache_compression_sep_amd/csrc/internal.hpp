@@ -19,6 +19,30 @@ inline int cache_ring(const sep_cache& c) {
 }
 inline int cache_slots(const sep_cache& c) { return c.a + c.s + cache_ring(c); }
 
+// Decode geometry. Few (sequence, kv head) pairs: wider workgroups (8
+// waves), so that each pair's list is read by more waves at once; and, when
+// the cache carries a large enough work buffer, each list split over several
+// workgroups: ranges of whole 128-entry units (one 32-entry slice for each of
+// 4 waves), at most kMaxSplits ranges per list (longer lists take longer
+// ranges). A list holds at most slots + 1 entries.
+inline bool decode_uses_wide(const sep_cache& c) { return c.B * c.Hkv < 256; }
+constexpr int kSplitChunk = 128;
+constexpr int kMaxSplits = 32;
+inline void decode_split_shape(const sep_cache& c, int* ns, int* span) {
+  const int nch = (cache_slots(c) + 1 + kSplitChunk - 1) / kSplitChunk;
+  *ns = nch < kMaxSplits ? nch : kMaxSplits;
+  *span = kSplitChunk * ((nch + *ns - 1) / *ns);
+}
+// partials: [B][Hq][ns] rows of D + 4 floats
+inline size_t decode_split_bytes(const sep_cache& c, int Hq) {
+  int ns, span;
+  decode_split_shape(c, &ns, &span);
+  return static_cast<size_t>(c.B) * Hq * ns * static_cast<size_t>(c.D + 4) * sizeof(float);
+}
+inline bool decode_uses_split(const sep_cache& c, int Hq) {
+  return decode_uses_wide(c) && c.work != nullptr && c.work_bytes >= decode_split_bytes(c, Hq);
+}
+
 hipError_t launch_is_sep(const int32_t* ids, int64_t N, const int32_t* sep_ids, int n_sep,
                          uint8_t* is_sep, hipStream_t st);
 hipError_t launch_tile_class(const uint8_t* is_sep, int B, int S, int a, int n, int tq, int tk,

@@ -66,6 +66,8 @@ def guarded_cache(*args, **kw):
     c = SepCache(*args, **kw)
     c.k, c.v = guarded_like(c.k), guarded_like(c.v)
     c.pos, c.tok, c.state = guarded_like(c.pos), guarded_like(c.tok), guarded_like(c.state)
+    if c.work is not None:
+        c.work = guarded_like(c.work)
     return c
 
 

@@ -55,10 +55,13 @@ def test_version_and_status_strings(lib):
 
 
 def test_struct_layout_matches_header():
-    # 8 int32, 5 pointers, the int32 policy (padded to 8 bytes)
-    assert ctypes.sizeof(_lib.SepCacheStruct) == 8 * 4 + 5 * 8 + 8
+    # 8 int32, 5 pointers, the int32 policy (padded to 8 bytes), the work
+    # pointer and its size
+    assert ctypes.sizeof(_lib.SepCacheStruct) == 8 * 4 + 5 * 8 + 8 + 2 * 8
     assert _lib.SepCacheStruct.k.offset == 32
     assert _lib.SepCacheStruct.policy.offset == 72
+    assert _lib.SepCacheStruct.work.offset == 80
+    assert _lib.SepCacheStruct.work_bytes.offset == 88
 
 
 def test_mask_build_argument_checks(lib):

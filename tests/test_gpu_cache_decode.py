@@ -186,13 +186,14 @@ DECODE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
-def test_decode_matches_oracle(case):
+def test_decode_matches_oracle(case, split):
     B, Hq, Hkv, D, a, s, p, w, T = case[:9]
     policy = case[9] if len(case) > 9 else 0
     st = Stream(zlib.crc32(repr(case).encode()), B, Hq, Hkv, D, T + 40, 0.2)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    cache = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy)
+    cache = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy, split=split)
     sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     st.push_gpu(cache, 0, T, d_sep)
     for b in range(B):

@@ -20,7 +20,7 @@ import oracle
 from kv_cache_compression_sep_amd import (SEP_POLICY_DYNAMIC, SEP_POLICY_NO_ACCUM, SepCache, SepError,
                                           sep_attn_decode_rope, sep_rope_table)
 
-from .gpu_util import check_close, from_dev, to_dev
+from .gpu_util import check_close, from_dev, guarded_cache, to_dev
 from .test_gpu_cache_decode import SEP_IDS, Stream, sim_for
 from inputs import gen
 
@@ -55,13 +55,14 @@ ROPE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
 @pytest.mark.parametrize("case", ROPE_CASES, ids=[str(c) for c in ROPE_CASES])
-def test_decode_rope_matches_oracle(case):
+def test_decode_rope_matches_oracle(case, split):
     B, Hq, Hkv, D, a, s, p, w, T, policy = case
-    print(f"rope decode case {case}", flush=True)
+    print(f"rope decode case {case} split={split}", flush=True)
     st = Stream(zlib.crc32(repr(("rope", case)).encode()), B, Hq, Hkv, D, T + 24, 0.1)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    cache = SepCache(B, Hkv, D, a, s, p, w, policy=policy)
+    cache = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy, split=split)
     table = sep_rope_table(LLAMA3_ROPE_BASE, D, cache.slots + 1)
     sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     st.push_gpu(cache, 0, T, d_sep)

@@ -43,14 +43,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
-def test_fused_step_equals_two_calls_and_oracle(case):
+def test_fused_step_equals_two_calls_and_oracle(case, split):
     B, Hq, Hkv, D, a, s, p, w, T0, steps, policy, rope = case
-    print(f"decode+update case {case}", flush=True)
+    print(f"decode+update case {case} split={split}", flush=True)
     st = Stream(zlib.crc32(repr(("fused", case)).encode()), B, Hq, Hkv, D, T0 + steps, 0.25)
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
-    fused = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy)
-    plain = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy)
+    fused = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy, split=split)
+    plain = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy, split=split)
+    assert (fused.work is not None) == (split and B * Hkv < 256)
     sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     if T0 > 0:
         st.push_gpu(fused, 0, T0, d_sep)
