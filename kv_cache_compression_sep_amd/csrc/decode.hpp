@@ -14,9 +14,10 @@
 // One workgroup per (kv head, sequence) reads that list once; or, when the
 // cache carries a work buffer and there are few (sequence, kv head) pairs,
 // ns workgroups per pair each read one range of `span` consecutive entries
-// of the list and write their unnormalised partial (running max, sum of
-// weights, weighted sum of values, per query head) to the work buffer, and a
-// second kernel merges the ns partials with the log-sum-exp rule (the
+// of the list, every wave writing its unnormalised partial (running max, sum
+// of weights, weighted sum of values, per query head) straight from its
+// registers to the work buffer, and a second kernel merges the partials
+// with the log-sum-exp rule (the
 // kernel boundary orders the two; merging inside one kernel would need a
 // device-scope release and acquire per workgroup, which on this GPU write
 // back and invalidate the L2 of each XCD). Waves take 32-key slices, NW slices per iteration: S^T = K Q^T
@@ -53,9 +54,9 @@ struct DecodeArgs {
   uint16_t* out;
   float* lse;
   const float* rope;                             // [n_pos][D/2] (cos, sin), ROPE only
-  float* part;                                   // split mode: partials [B][Hkv][ns][G][kPartStr]; else null
+  float* part;                                   // split mode: partials [B][Hkv][np][G][part_stride]; else null
   int a, s, p, w, rw, c, Hq, Hkv, G;
-  int ns, span;                                  // split mode: ranges per list, entries per range
+  int ns, span, np;                              // split mode: ranges per list, entries per range, partials per list
   float scale_log2;
 };
 
@@ -356,6 +357,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, i
   float lw = l_run;
   lw += __shfl_xor(lw, 16, kWave);
   lw += __shfl_xor(lw, 32, kWave);
+  if (A.part != nullptr) {                      // split: this wave's partial, unnormalised
+    if (lane % 16 < G) {
+      float* pp = A.part + ((bg * A.np + split * NW + wave) * G + lane % 16) * part_stride<D>();
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(pp + 4 + 16 * db + 4 * hh) = oacc[db];
+      if (hh == 0) *reinterpret_cast<f32x2*>(pp) = f32x2{m_run, lw};
+    }
+    return;
+  }
   float* red_o = reinterpret_cast<float*>(arena);   // [NW][16][D + 1], reuses the V^T slices
   if (lane < 16) {
     red_m[wave][lane] = m_run;
@@ -380,15 +390,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, i
       o += f * red_o[(wv * 16 + hq) * (D + 1) + d];
       l += f * red_l[wv][hq];
     }
-    if (A.part != nullptr) {                    // this range's partial, unnormalised
-      float* pp = A.part + ((bg * A.ns + split) * G + hq) * part_stride<D>();
-      pp[4 + d] = o;
-      if (d == 0) {
-        pp[0] = M;
-        pp[1] = l;
-      }
-      continue;
-    }
     const int64_t orow = static_cast<int64_t>(b) * A.Hq + g * G + hq;
     const uint32_t bits = pack_bf16x2(o / l, 0.f);
     A.out[orow * D + d] = static_cast<uint16_t>(bits & 0xffffu);
@@ -396,27 +397,49 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, i
   }
 }
 
-// Merge of the ns partials of kv head g of sequence b into out / lse: with
+// Merge of the np partials of kv head g of sequence b into out / lse: with
 // M the largest partial max, o = sum_i 2^(m_i - M) o_i and l = sum_i
-// 2^(m_i - M) l_i, out = o / l and lse = (M + log2 l) ln 2; a range past the
-// end of the list has m_i = -inf and weighs nothing.
+// 2^(m_i - M) l_i, out = o / l and lse = (M + log2 l) ln 2; a wave that saw
+// no entry has m_i = -inf and weighs nothing. The partials are read kMB at a
+// time, all loads issued before any is used, and blocks after the first are
+// folded in with an online rescale.
 template <int D>
 __device__ __forceinline__ void merge_body(const DecodeArgs& A, int g, int b, int nthreads) {
   constexpr int PS = part_stride<D>();
+  constexpr int kMB = 16;
   const int G = A.G;
   const int64_t bg = static_cast<int64_t>(b) * A.Hkv + g;
   for (int e = threadIdx.x; e < G * D; e += nthreads) {
     const int hq = e / D;
     const int d = e % D;
-    const float* pp = A.part + bg * A.ns * G * PS + hq * PS;
-    float M = -INFINITY;
-    for (int i = 0; i < A.ns; ++i) M = fmaxf(M, pp[i * G * PS]);
-    float o = 0.f, l = 0.f;
-    for (int i = 0; i < A.ns; ++i) {
-      const float m = pp[i * G * PS];
-      const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-      o += f * pp[i * G * PS + 4 + d];
-      l += f * pp[i * G * PS + 1];
+    const float* pp = A.part + bg * A.np * G * PS + hq * PS;
+    float M = -INFINITY, o = 0.f, l = 0.f;
+    for (int i0 = 0; i0 < A.np; i0 += kMB) {
+      float mv[kMB], lv[kMB], ov[kMB];
+#pragma unroll
+      for (int k = 0; k < kMB; ++k) {
+        const bool ok = i0 + k < A.np;
+        const float* q = pp + static_cast<int64_t>(ok ? i0 + k : 0) * G * PS;
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(q);
+        mv[k] = ok ? ml[0] : -INFINITY;
+        lv[k] = ml[1];
+        ov[k] = q[4 + d];
+      }
+      float Mb = M;
+#pragma unroll
+      for (int k = 0; k < kMB; ++k) Mb = fmaxf(Mb, mv[k]);
+      if (M != -INFINITY && Mb != M) {
+        const float f = fast_exp2(M - Mb);
+        o *= f;
+        l *= f;
+      }
+#pragma unroll
+      for (int k = 0; k < kMB; ++k) {
+        const float f = (mv[k] == -INFINITY) ? 0.f : fast_exp2(mv[k] - Mb);
+        o += f * ov[k];
+        l += f * lv[k];
+      }
+      M = Mb;
     }
     const int64_t orow = static_cast<int64_t>(b) * A.Hq + g * G + hq;
     const uint32_t bits = pack_bf16x2(o / l, 0.f);
@@ -425,8 +448,7 @@ __device__ __forceinline__ void merge_body(const DecodeArgs& A, int g, int b, in
   }
 }
 
-// waves of a split-decode workgroup: one 32-entry slice each per range unit
-constexpr int kSplitWaves = kSplitChunk / kSlice;
+// a split-decode workgroup: one 32-entry slice per wave and range unit
 static_assert(kSplitWaves * kSlice == kSplitChunk, "split ranges are whole slices");
 
 // the ranges of a split decode (decode.hip); their merge is a second launch
@@ -447,9 +469,11 @@ inline DecodeArgs decode_args(const void* q, const void* k_new, const void* v_ne
   A.part = nullptr;
   A.ns = 1;
   A.span = 0;
+  A.np = 0;
   if (decode_uses_split(c, Hq)) {
     A.part = static_cast<float*>(c.work);
     decode_split_shape(c, &A.ns, &A.span);
+    A.np = A.ns * kSplitWaves;
   }
   A.a = c.a;
   A.s = c.s;  // the separator-ring branch is only reached when cnt > 0, i.e. s >= 1

@@ -33,11 +33,12 @@ inline void decode_split_shape(const sep_cache& c, int* ns, int* span) {
   *ns = nch < kMaxSplits ? nch : kMaxSplits;
   *span = kSplitChunk * ((nch + *ns - 1) / *ns);
 }
-// partials: [B][Hq][ns] rows of D + 4 floats
+// one partial per wave of a range: [B][Hkv][ns * kSplitWaves][G] rows of D + 4 floats
+constexpr int kSplitWaves = kSplitChunk / 32;
 inline size_t decode_split_bytes(const sep_cache& c, int Hq) {
   int ns, span;
   decode_split_shape(c, &ns, &span);
-  return static_cast<size_t>(c.B) * Hq * ns * static_cast<size_t>(c.D + 4) * sizeof(float);
+  return static_cast<size_t>(c.B) * Hq * ns * kSplitWaves * static_cast<size_t>(c.D + 4) * sizeof(float);
 }
 inline bool decode_uses_split(const sep_cache& c, int Hq) {
   return decode_uses_wide(c) && c.work != nullptr && c.work_bytes >= decode_split_bytes(c, Hq);
