@@ -23,9 +23,10 @@
 // back and invalidate the L2 of each XCD). Waves take 32-key slices, NW slices per iteration: S^T = K Q^T
 // with the 16x16x32 bf16 MFMA (K rows loaded straight into the A operand,
 // Q^T of the G query heads in registers), online softmax per head column,
-// then O^T += V^T P^T with V staged transposed in the wave's LDS slice. The
-// next slice's K and V rows are loaded while the current one is computed.
-// Waves merge through LDS at the end.
+// then O^T += V^T P^T with V staged transposed in the wave's own LDS slice
+// (so the waves need no barrier until they merge). The next slice's K and V
+// rows are loaded while the current one is computed. Waves merge through LDS
+// at the end.
 //
 // With ROPE (sep_attn_decode_rope; P1 "Streaming-SepLLM": streaming needs
 // positional-encoding shifting; RoFormer §3.4 for the rotation), virtual
@@ -341,7 +342,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, i
     }
     l_run = l_run * corr + lsum;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-    __syncthreads();  // V^T slices written
+    // The V^T slice is this wave's own LDS region: its writes above complete
+    // before the reads below (a wave's LDS operations run in order; the wait
+    // also keeps the compiler from moving memory operations across), and the
+    // next slice's writes come after these reads were consumed. No other wave
+    // touches it until the merge, which starts with a barrier.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const uint16_t* vrow = vt + (16 * db + lane % 16) * VSTR + 8 * hh;
@@ -349,7 +355,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, i
       oacc[db] = oacc[db] * corr;
       oacc[db] = mfma16x16x32(av, pb, oacc[db]);
     }
-    __syncthreads();  // V^T slices consumed
+    asm volatile("" ::: "memory");
   }
 
   // ---- merge the waves: lane l holds head l%16, d = 16*db + 4*(l/16) + r;
@@ -366,6 +372,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& A, int g, int b, i
     }
     return;
   }
+  __syncthreads();                              // every wave is done with its V^T slice
   float* red_o = reinterpret_cast<float*>(arena);   // [NW][16][D + 1], reuses the V^T slices
   if (lane < 16) {
     red_m[wave][lane] = m_run;
