@@ -52,19 +52,22 @@ __device__ __forceinline__ v4i16b read_tr16b(const char* p) {
 }
 
 // Byte offsets of this lane's transpose reads in rows R and R + 8 of a
-// 16-row group (the swizzle repeats every 16 rows), per d block.
+// 16-row group (the swizzle repeats every 16 rows), d block db.
 template <int D>
-__device__ __forceinline__ void tr_offsets(int lane, int (&off)[D / 32][2]) {
+__device__ __forceinline__ void tr_offsets_block(int lane, int db, int (&off)[2]) {
   using G = BGeo<D>;
   const int tg = lane / 16, tj = lane % 16;
   const int th = tg / 2, tdh = tg % 2;
   const int R = 4 * th + tj / 4;
+  const int dcol = 32 * db + 16 * tdh + 4 * (tj % 4);
 #pragma unroll
-  for (int db = 0; db < G::DB; ++db) {
-    const int dcol = 32 * db + 16 * tdh + 4 * (tj % 4);
+  for (int e = 0; e < 2; ++e) off[e] = 16 * G::slot(R + 8 * e, dcol / 8) + 2 * (dcol % 8);
+}
+
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[D / 32][2]) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) off[db][e] = 16 * G::slot(R + 8 * e, dcol / 8) + 2 * (dcol % 8);
-  }
+  for (int db = 0; db < D / 32; ++db) tr_offsets_block<D>(lane, db, off[db]);
 }
 
 // A operand over rows 16 kc .. 16 kc + 15 of a tile, d block db.
@@ -244,63 +247,108 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
 }
 
 // ---------------------------------------------------------------- dK, dV (bf16)
-// A workgroup holds 128 keys in 4 groups of 32 and splits d into D / 64
-// halves: wave w takes key group w % 4 and d columns [64 (w / 4), +64), so
-// that its dK and dV accumulators (32 keys x 64 d each) leave room for two
-// waves per SIMD. The scores need all of d, so the waves of one key group
-// compute S and dP alike.
+// A workgroup holds 128 keys in 4 groups of 32 and gives each group two
+// waves. The P wave (waves 0-3) computes S = Q K^T and P, accumulates
+// dV^T += dO^T P over the whole of d, and leaves P (fp32) in LDS. The dS wave
+// (waves 4-7) computes dP = dO V^T and, one query tile later, dS = P (dP -
+// delta) from that P, and accumulates dK^T += Q^T dS over the whole of d. So
+// every product and every element of P and dS is computed once per (key,
+// query row), and each wave holds one of K^T, V^T in registers.
 template <int D>
 struct KVGeo {
-  static constexpr int DSPLIT = D / 64;           // d halves
-  static constexpr int NWAVE = 4 * DSPLIT;
+  static constexpr int KS = D / 16;               // 16-wide k-steps over d
+  static constexpr int DB = D / 32;               // 32-row d blocks
+  static constexpr int NWAVE = 8;
   static constexpr int NTH = NWAVE * kWave;
 };
 
-// One query tile (32 rows of Q and dO, staged in LDS) against this wave's 32
-// keys (K^T and V^T fragments in registers): S = Q K^T and dP = dO V^T put
-// one key per lane; then dV^T += dO^T P and dK^T += Q^T dS over the 32 rows,
-// for the wave's two 32-column d blocks (transpose offsets toff).
-template <int D, class Vis>
-__device__ __forceinline__ void kv_tile_bf16(const char* Qs, const char* Os, const float* lse, const float* dlt,
-                                             const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
-                                             const int (&toff)[2][2], float scale_log2, int lane, Vis visible,
-                                             f32x16 (&dk)[2], f32x16 (&dv)[2]) {
+// The KS products over d of tile rows lane % 32 with the register fragments
+// b (one key per lane): all A operands are read before the first MFMA, so
+// that the LDS latency is paid once per tile.
+template <int D>
+__device__ __forceinline__ f32x16 tile_scores(const char* tile, const bf16x8 (&b)[D / 16], int lane) {
   constexpr int KS = D / 16;
-  const int hsel = lane / 32;
-  f32x16 sc = {}, dp = {};
+  bf16x8 a[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    sc = mfma32x32x16(row_operand<D>(Qs, lane % 32, ks, lane), kf[ks], sc);
-    dp = mfma32x32x16(row_operand<D>(Os, lane % 32, ks, lane), vf[ks], dp);
-  }
-  // P and dS straight into bf16 pairs (the B operands), element r of the
-  // accumulator in word r / 2
-  u32x4 wp[2], wds[2];
+  for (int ks = 0; ks < KS; ++ks) a[ks] = row_operand<D>(tile, lane % 32, ks, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 acc = {};
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    float pv[2], dv2[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int il = 8 * ((r + e) / 4) + 4 * hsel + ((r + e) % 4);   // query row of element r + e
-      pv[e] = visible(il) ? fast_exp2(__builtin_fmaf(sc[r + e], scale_log2, -lse[il] * kLog2e)) : 0.0f;
-      dv2[e] = pv[e] * (dp[r + e] - dlt[il]);
-    }
-    wp[r / 8][(r % 8) / 2] = pack_bf16x2(pv[0], pv[1]);
-    wds[r / 8][(r % 8) / 2] = pack_bf16x2(dv2[0], dv2[1]);
-  }
-#pragma unroll
-  for (int kcl = 0; kcl < 2; ++kcl) {
-    const bf16x8 bp = __builtin_bit_cast(bf16x8, wp[kcl]), bds = __builtin_bit_cast(bf16x8, wds[kcl]);
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      dv[db] = mfma32x32x16(tr_operand<D>(Os, toff[db], kcl), bp, dv[db]);
-      dk[db] = mfma32x32x16(tr_operand<D>(Qs, toff[db], kcl), bds, dk[db]);
-    }
-  }
+  for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[ks], b[ks], acc);
+  return acc;
 }
 
-// Query tiles of 32 rows (Q, dO, lse, delta) stream into a ring of four LDS
-// stages by LDS-DMA (global_load_lds: no register results), three tiles
+// acc[db] += tile^T w over the 32 tile rows, per d block: the A operands
+// come from the transpose reads, the B operands w[kc] hold the weights of
+// accumulator elements 8 kc .. 8 kc + 7 (rows 16 kc .. 16 kc + 15).
+template <int D>
+__device__ __forceinline__ void tile_accumulate(const char* tile, const int (&toff)[D / 32][2],
+                                                const bf16x8 (&w)[2], f32x16 (&acc)[D / 32]) {
+  constexpr int DB = D / 32;
+  bf16x8 a[2][DB];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) a[kc][db] = tr_operand<D>(tile, toff[db], kc);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16(a[kc][db], w[kc], acc[db]);
+}
+
+// P wave, one query tile: bit il of vm says that tile row il is visible to
+// this lane's key. P goes to pw[i * 64] (i < 4, elements 4 i .. 4 i + 3),
+// hidden pairs as +0 (an AND with the pair's sign-extended bit).
+template <int D>
+__device__ __forceinline__ void p_tile(const char* Qs, const char* Os, const float* lse,
+                                       const bf16x8 (&kf)[D / 16], const int (&toff)[D / 32][2],
+                                       float scale_log2, int lane, uint32_t vm, f32x4* pw,
+                                       f32x16 (&dv)[D / 32]) {
+  const int hsel = lane / 32;
+  const uint32_t vh = vm >> (4 * hsel);           // bit 8 (r / 4) + r % 4: accumulator element r
+  const f32x16 sc = tile_scores<D>(Qs, kf, lane);
+  float p[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int il = 8 * (r / 4) + 4 * hsel + (r % 4);                  // query row of element r
+    const float e = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -lse[il] * kLog2e));
+    const uint32_t keep = __builtin_amdgcn_sbfe(vh, 8 * (r / 4) + (r % 4), 1);
+    uint32_t pb;                                  // (the compiler would make the AND a compare and select)
+    asm("v_and_b32 %0, %1, %2" : "=v"(pb) : "v"(__builtin_bit_cast(uint32_t, e)), "v"(keep));
+    p[r] = __builtin_bit_cast(float, pb);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i * kWave] = f32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
+  const bf16x8 w[2] = {pack8(p), pack8(p + 8)};
+  tile_accumulate<D>(Os, toff, w, dv);
+}
+
+// dS wave, the tile whose P the P wave left at pr and whose dP is dp.
+template <int D>
+__device__ __forceinline__ void ds_tile(const char* Qs, const float* dlt, const f32x4* pr, const f32x16& dp,
+                                        const int (&toff)[D / 32][2], int lane, f32x16 (&dk)[D / 32]) {
+  const int hsel = lane / 32;
+  float ds[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 pq = pr[i * kWave];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ds[4 * i + e] = pq[e] * (dp[4 * i + e] - dlt[8 * i + 4 * hsel + e]);
+  }
+  const bf16x8 w[2] = {pack8(ds), pack8(ds + 8)};
+  tile_accumulate<D>(Qs, toff, w, dk);
+}
+
+// Bits [lo, hi) of a 32-row tile, the bounds clamped to the tile.
+__device__ __forceinline__ uint32_t row_range(int lo, int hi) {
+  lo = min(max(lo, 0), 32);
+  hi = min(max(hi, lo), 32);
+  return static_cast<uint32_t>((1ull << hi) - (1ull << lo));
+}
+
+// Query tiles of 32 rows (Q, dO, lse, delta) stream into a ring of NST LDS
+// stages by LDS-DMA (global_load_lds: no register results), AHEAD tiles
 // ahead of the one being computed. Every wave issues exactly OPS DMA ops per
 // tile (dummies into its junk row past the last tile, or for the lse/delta
 // rows that only wave 0 loads), so one exact vmcnt count per tile says that
@@ -331,17 +379,19 @@ __device__ __forceinline__ void bw_dma4(const void* base, uint32_t off, uint32_t
                :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
 
+// The dS wave reads tile t - 1 while tile t + AHEAD lands: NST = AHEAD + 2.
 template <int D, int NW>
 struct QRing {
   static constexpr int CPR = BGeo<D>::CPR;
   static constexpr int TB = QB * D * 2;           // bytes of a 32-row Q (or dO) tile
-  static constexpr int PERW = TB / 1024 / NW;     // 1 KB DMA instructions per wave per tensor
+  static constexpr int NINS = TB / 1024;          // 1 KB DMA instructions per tensor
+  static constexpr int PERW = NINS >= NW ? NINS / NW : 1;   // per wave (dummies past NINS)
   static constexpr int OPS = 2 * PERW + 2;        // + one dword op each for lse and delta
-  static constexpr int NST = 4;
-  static constexpr int AHEAD = NST - 1;
+  static constexpr int AHEAD = 3;
+  static constexpr int NST = AHEAD + 2;
   static constexpr int STAGE = 2 * TB + 2 * 64 * 4;
   static constexpr int BYTES = NST * STAGE;
-  static_assert(PERW >= 1, "tile too small for the wave count");
+  static_assert(NINS % NW == 0 || NINS < NW, "whole instructions per wave");
   char* ring;                                     // NST x [Q | dO | lse (64) | delta (64)]
   char* junk;                                     // NW x 1 KB, targets of dummy ops
   __device__ char* q(int t) const { return ring + (t % NST) * STAGE; }
@@ -351,19 +401,20 @@ struct QRing {
   // the DMA ops of tile t (rows qt0.. of query row block hrow), or dummies
   __device__ void issue(const BwdArgs& P, bool real, int64_t hrow, int qt0, int t) const {
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(P.q) + hrow * D;
     const uint16_t* ob = reinterpret_cast<const uint16_t*>(P.dout) + hrow * D;
     char* jw = junk + wave * 1024;
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
       const int ins = wave * PERW + i;
+      const bool rw = real && ins < NINS;
       const int sl = ins * kWave + lane;
       const int r = sl / CPR;
       const int c = (sl % CPR) ^ BGeo<D>::swz(r);
-      const uint32_t off = real ? static_cast<uint32_t>(min(qt0 + r, P.S - 1) * (D * 2) + 16 * c) : 0u;
-      bw_dma16(qb, off, __builtin_amdgcn_readfirstlane(bw_lds(real ? q(t) + ins * 1024 : jw)));
-      bw_dma16(ob, off, __builtin_amdgcn_readfirstlane(bw_lds(real ? o(t) + ins * 1024 : jw)));
+      const uint32_t off = rw ? static_cast<uint32_t>(min(qt0 + r, P.S - 1) * (D * 2) + 16 * c) : 0u;
+      bw_dma16(qb, off, __builtin_amdgcn_readfirstlane(bw_lds(rw ? q(t) + ins * 1024 : jw)));
+      bw_dma16(ob, off, __builtin_amdgcn_readfirstlane(bw_lds(rw ? o(t) + ins * 1024 : jw)));
     }
     const bool rl = real && wave == 0;
     const uint32_t offl = rl ? 4u * static_cast<uint32_t>(min(qt0 + lane % 32, P.S - 1)) : 0u;
@@ -372,10 +423,18 @@ struct QRing {
   }
 };
 
-// Run compute(t, stage) over nt query tiles; tile(t) gives (hrow, qt0).
-// Every global load and store of the workgroup issued before the call must
-// be complete or unrelated to vmcnt ordering: the call starts with a full
-// wait.
+// P of the last two query tiles, per key group and lane: [2][4][4][64] f32x4.
+constexpr int kPBytes = 2 * 4 * 4 * kWave * 16;
+__device__ __forceinline__ f32x4* p_slot(char* pbuf, int t, int kg, int lane) {
+  return reinterpret_cast<f32x4*>(pbuf) + ((t % 2) * 4 + kg) * 4 * kWave + lane;
+}
+
+// Run compute(t) for t = 0 .. nt (t = nt: no tile, the dS waves' last step);
+// tile(t) gives (hrow, qt0) of tile t < nt. Every global load and store of
+// the workgroup issued before the call must be complete or unrelated to
+// vmcnt ordering: the call starts with a full wait. LDS stores of compute(t)
+// are complete before compute(t + 1) starts on any wave (the wait of the
+// tile count includes lgkmcnt(0) and precedes the publishing barrier).
 template <class RG, class TileOf, class Compute>
 __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R, int nt, TileOf tile,
                                                    Compute compute) {
@@ -389,9 +448,9 @@ __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R
     tile(t < nt ? t : 0, &hrow, &qt0);
     R.issue(P, t < nt, hrow, qt0, t);
   }
-  for (int t = 0; t < nt; ++t) {
+  for (int t = 0; t <= nt; ++t) {
     bw_fence();
-    __builtin_amdgcn_s_barrier();                 // stage (t - 1) % 4 consumed by every wave
+    __builtin_amdgcn_s_barrier();                 // compute(t - 1) done by every wave
     bw_fence();
     {
       const int tn = t + RG::AHEAD;
@@ -410,27 +469,39 @@ __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R
   __syncthreads();
 }
 
-// K^T and V^T fragments of key j: d = 16 ks + 8 (lane / 32) + i
+// K^T (or V^T) fragments of key j: d = 16 ks + 8 (lane / 32) + i
 template <int D>
-__device__ __forceinline__ void load_key_bf16(const uint16_t* kb, const uint16_t* vb, int j, int lane,
-                                              bf16x8 (&kf)[D / 16], bf16x8 (&vf)[D / 16]) {
+__device__ __forceinline__ void load_key_bf16(const uint16_t* base, int j, int lane, bf16x8 (&f)[D / 16]) {
   const int hsel = lane / 32;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + static_cast<int64_t>(j) * D + 16 * ks + 8 * hsel));
-    vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(j) * D + 16 * ks + 8 * hsel));
-  }
+  for (int ks = 0; ks < D / 16; ++ks)
+    f[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(j) * D + 16 * ks + 8 * hsel));
 }
 
-// This lane's transpose offsets for the two d blocks of d half dh.
-template <int D>
-__device__ __forceinline__ void half_offsets(int lane, int dh, int (&toff)[2][2]) {
-  int all[D / 32][2];
-  tr_offsets<D>(lane, all);
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) toff[db][e] = all[2 * dh + db][e];
+// The query tile loop of one wave of a key group's pair: the P wave on tile
+// t, the dS wave on tile t - 1 (dS, dK) and tile t (dP). vis(t) gives the
+// visibility mask of tile t for this lane's key; a tile that no lane of the
+// group sees is skipped by both waves alike. The two roles run separate
+// loops (with the same barriers), so that each is register-allocated alone.
+template <int D, class Ring, class TileOf, class Vis>
+__device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char* pbuf, int nt, TileOf tile,
+                                          bool pwave, int kg, int lane, const bf16x8 (&kv)[D / 16],
+                                          const int (&toff)[D / 32][2], Vis vis, f32x16 (&acc)[D / 32]) {
+  if (pwave) {
+    stream_query_tiles(P, R, nt, tile, [&](int t) {
+      if (t == nt) return;
+      const uint32_t vm = vis(t);
+      if (ballot(vm != 0u) == 0) return;
+      p_tile<D>(R.q(t), R.o(t), R.l(t), kv, toff, P.scale_log2, lane, vm, p_slot(pbuf, t, kg, lane), acc);
+    });
+  } else {
+    f32x16 dp = {};
+    stream_query_tiles(P, R, nt, tile, [&](int t) {
+      if (t > 0 && ballot(vis(t - 1) != 0u) != 0)
+        ds_tile<D>(R.q(t - 1), R.d(t - 1), p_slot(pbuf, t - 1, kg, lane), dp, toff, lane, acc);
+      if (t < nt && ballot(vis(t) != 0u) != 0) dp = tile_scores<D>(R.o(t), kv, lane);
+    });
+  }
 }
 
 template <int D>
@@ -439,11 +510,12 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
   using Ring = QRing<D, KG::NWAVE>;
   __shared__ __attribute__((aligned(1024))) char ringmem[Ring::BYTES];
   __shared__ __attribute__((aligned(1024))) char junkmem[KG::NWAVE * 1024];
+  __shared__ __attribute__((aligned(16))) char pbuf[kPBytes];
   const Ring R{ringmem, junkmem};
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int kg = wave % 4;                        // key group
-  const int dh = wave / 4;                        // d half
+  const bool pwave = wave < 4;
   const int hsel = lane / 32;
   const int kt = blockIdx.x % n_kt;
   const int bgi = blockIdx.x / n_kt;
@@ -455,51 +527,40 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
   const int jc = min(j, S - 1);
   const uint8_t* fl = P.is_sep + static_cast<int64_t>(b) * S;
   const bool own = j < S && j >= P.a && fl[jc] == 0;    // initial and separator keys: dkdv_glob
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  bf16x8 kf[D / 16], vf[D / 16];
-  load_key_bf16<D>(kb, vb, jc, lane, kf, vf);
-  int toff[2][2];
-  half_offsets<D>(lane, dh, toff);
-  f32x16 dk[2], dv[2];
+  const int64_t kvrow = static_cast<int64_t>(b * P.Hkv + g) * S;
+  bf16x8 kv[KG::KS];
+  load_key_bf16<D>((pwave ? reinterpret_cast<const uint16_t*>(P.k) : reinterpret_cast<const uint16_t*>(P.v)) +
+                       kvrow * D,
+                   jc, lane, kv);
+  int toff[KG::DB][2];
+  tr_offsets<D>(lane, toff);
+  f32x16 acc[KG::DB];
 #pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
+  for (int db = 0; db < KG::DB; ++db) acc[db] = f32x16{};
   // query tiles of the keys' windows, [j0, j0 + KB - 1 + n) capped at S, per head
   const int64_t qend64 = static_cast<int64_t>(j0) + KB - 1 + P.n;
   const int qend = static_cast<int>(qend64 < S ? qend64 : S);
   const int ntq = (qend - j0 + QB - 1) / QB;
   const int nt = P.G * ntq;
-  const int wj0 = j0 + 32 * kg;
+  const int hi_j = own ? j + min(S - j, P.n) : 0;  // rows i with j <= i < j + n, i < S
   auto tile = [&](int t, int64_t* hrow, int* qt0) {
     *hrow = static_cast<int64_t>(b * P.Hq + g * P.G + t / ntq) * S;
     *qt0 = j0 + (t % ntq) * QB;
   };
-  stream_query_tiles(P, R, nt, tile, [&](int t) {
+  auto vis = [&](int t) {
     const int qt0 = j0 + (t % ntq) * QB;
-    if (qt0 + QB - 1 < wj0 || static_cast<int64_t>(qt0) > static_cast<int64_t>(wj0) + 31 + P.n - 1) return;
-    kv_tile_bf16<D>(R.q(t), R.o(t), R.l(t), R.d(t), kf, vf, toff, P.scale_log2, lane,
-                    [&](int il) {
-                      const int i = qt0 + il;
-                      return own && i < S && i >= j && i - j < P.n;
-                    },
-                    dk, dv);
-  });
+    return own ? row_range(j - qt0, hi_j - qt0) : 0u;
+  };
+  pair_loop<D>(P, R, pbuf, nt, tile, pwave, kg, lane, kv, toff, vis, acc);
   if (j < S) {
-    float* dkr = P.dk + (static_cast<int64_t>(b * P.Hkv + g) * S + j) * D;
-    float* dvr = P.dv + (static_cast<int64_t>(b * P.Hkv + g) * S + j) * D;
+    float* dst = (pwave ? P.dv : P.dk) + (kvrow + j) * D;
+    const float f = pwave ? 1.0f : P.scale;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < KG::DB; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int d = 64 * dh + 32 * db + 8 * q + 4 * hsel;
-        *reinterpret_cast<f32x4*>(dkr + d) = f32x4{dk[db][4 * q] * P.scale, dk[db][4 * q + 1] * P.scale,
-                                                   dk[db][4 * q + 2] * P.scale, dk[db][4 * q + 3] * P.scale};
-        *reinterpret_cast<f32x4*>(dvr + d) = f32x4{dv[db][4 * q], dv[db][4 * q + 1], dv[db][4 * q + 2],
-                                                   dv[db][4 * q + 3]};
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q + 4 * hsel) =
+            f32x4{acc[db][4 * q] * f, acc[db][4 * q + 1] * f, acc[db][4 * q + 2] * f, acc[db][4 * q + 3] * f};
   }
 }
 
@@ -507,20 +568,23 @@ template <int D>
 __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_qc, int nslots) {
   using KG = KVGeo<D>;
   using Ring = QRing<D, KG::NWAVE>;
-  static_assert(KG::NWAVE * 32 * 64 * 4 <= Ring::BYTES, "the flush buffer aliases the ring");
-  __shared__ __attribute__((aligned(1024))) char ringmem[Ring::BYTES];
+  constexpr int RED = KG::NWAVE * 32 * 64 * 4;    // one 64-column pass of every wave's partial
+  constexpr int SM = Ring::BYTES + kPBytes;
+  static_assert(RED <= SM, "the flush buffer aliases the ring and the P buffers");
+  __shared__ __attribute__((aligned(1024))) char smem[SM];
   __shared__ __attribute__((aligned(1024))) char junkmem[KG::NWAVE * 1024];
   __shared__ int32_t kpos[KB];
   __shared__ int32_t tstart[kMaxChunks + 1];
   __shared__ int32_t wsum[KG::NWAVE];
-  const Ring R{ringmem, junkmem};
-  // one wave's partial dK or dV, key-major, column (d - 64 dh) ^ row: [NWAVE][32][64]
-  float* red = reinterpret_cast<float*>(ringmem);
+  const Ring R{smem, junkmem};
+  char* pbuf = smem + Ring::BYTES;
+  // one wave's partial over 64 columns, key-major, column ^ key: [NWAVE][32][64]
+  float* red = reinterpret_cast<float*>(smem);
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int kg = wave % 4;
-  const int dh = wave / 4;
+  const bool pwave = wave < 4;
   const int hsel = lane / 32;
   const int BH = P.B * P.Hkv;
   const int bgi = blockIdx.x % BH;
@@ -535,12 +599,13 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
   auto n_global = [&](int c1) { return min(ninit, c1) + (c1 > ninit ? rk[c1] - rank_a : 0); };
   const int total = chunk_tile_prefix<KG::NTH>(n_global, S, n_qc, tstart, wsum);
 
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  const uint16_t* vb = reinterpret_cast<const uint16_t*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  float* dkb = P.dk + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  float* dvb = P.dv + static_cast<int64_t>(b * P.Hkv + g) * S * D;
-  int toff[2][2];
-  half_offsets<D>(lane, dh, toff);
+  const int64_t kvrow = static_cast<int64_t>(b * P.Hkv + g) * S;
+  const uint16_t* kvb =
+      (pwave ? reinterpret_cast<const uint16_t*>(P.k) : reinterpret_cast<const uint16_t*>(P.v)) + kvrow * D;
+  float* dst = (pwave ? P.dv : P.dk) + kvrow * D;
+  const float f = pwave ? 1.0f : P.scale;
+  int toff[KG::DB][2];
+  tr_offsets<D>(lane, toff);
 
   for (int w = slot; w < total; w += nslots) {
     const int qc = chunk_of(tstart, n_qc, w);
@@ -556,47 +621,38 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
     }
     __syncthreads();
     const int j = kpos[32 * kg + lane % 32];      // this lane's key, -1 past the list
-    bf16x8 kf[D / 16], vf[D / 16];
-    load_key_bf16<D>(kb, vb, j < 0 ? 0 : j, lane, kf, vf);
-    f32x16 dk[2], dv[2];
+    bf16x8 kv[KG::KS];
+    load_key_bf16<D>(kvb, j < 0 ? 0 : j, lane, kv);
+    f32x16 acc[KG::DB];
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      dk[db] = f32x16{};
-      dv[db] = f32x16{};
-    }
+    for (int db = 0; db < KG::DB; ++db) acc[db] = f32x16{};
     const int jlo = kpos[0];
-    const int wlo = kpos[32 * kg];
     const int qs0 = max(c0, jlo) / QB * QB;
     const int ntq = (c1 - qs0 + QB - 1) / QB;
     const int nt = P.G * ntq;
+    const int lo_j = max(c0, j);                  // rows i of the chunk [c0, c1) with i >= j
     auto tile = [&](int t, int64_t* hrow, int* qt0) {
       *hrow = static_cast<int64_t>(b * P.Hq + g * P.G + t / ntq) * S;
       *qt0 = qs0 + (t % ntq) * QB;
     };
-    stream_query_tiles(P, R, nt, tile, [&](int t) {
+    auto vis = [&](int t) {
       const int qt0 = qs0 + (t % ntq) * QB;
-      if (wlo < 0 || qt0 + QB - 1 < wlo) return;
-      kv_tile_bf16<D>(R.q(t), R.o(t), R.l(t), R.d(t), kf, vf, toff, P.scale_log2, lane,
-                      [&](int il) {
-                        const int i = qt0 + il;
-                        return j >= 0 && i >= c0 && i < c1 && i >= j;
-                      },
-                      dk, dv);
-    });
+      return j >= 0 ? row_range(lo_j - qt0, c1 - qt0) : 0u;
+    };
+    pair_loop<D>(P, R, pbuf, nt, tile, pwave, kg, lane, kv, toff, vis, acc);
     // Add the partials with fp32 atomics, key row by key row through LDS, so
     // that each atomic instruction covers 2 x 32 consecutive floats of two
-    // rows (2 cache lines) instead of one float of 32 rows.
+    // rows (2 cache lines) instead of one float of 32 rows; 64 columns a pass.
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
+    for (int h = 0; h < D / 64; ++h) {
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int dl = 32 * db + 8 * (r / 4) + 4 * hsel + (r % 4);       // column within the half
-          red[(wave * 32 + lane % 32) * 64 + (dl ^ (lane % 32))] = which == 0 ? dk[db][r] * P.scale : dv[db][r];
+          const int dl = 32 * db + 8 * (r / 4) + 4 * hsel + (r % 4);       // column within the pass
+          red[(wave * 32 + lane % 32) * 64 + (dl ^ (lane % 32))] = acc[2 * h + db][r] * f;
         }
       __syncthreads();
-      float* dst = which == 0 ? dkb : dvb;
 #pragma unroll 4
       for (int pass = 0; pass < 16; ++pass) {
         const int row = 2 * pass + lane / 32;
@@ -604,7 +660,7 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
         if (jr >= 0) {
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            atomicAdd(dst + static_cast<int64_t>(jr) * D + 64 * dh + 32 * e + lane % 32,
+            atomicAdd(dst + static_cast<int64_t>(jr) * D + 64 * h + 32 * e + lane % 32,
                       red[(wave * 32 + row) * 64 + ((32 * e + lane % 32) ^ row)]);
         }
       }
