@@ -262,15 +262,45 @@ struct KVGeo {
   static constexpr int NTH = NWAVE * kWave;
 };
 
+// This lane's LDS byte offsets within a 32-row tile: the row reads of
+// tile_scores (chunk 2 ks + lane / 32 of row lane % 32) and the transpose
+// reads of tile_accumulate. Kept in registers, so that each operand address
+// of a tile is one add to the tile's base.
+template <int D>
+struct LaneOff {
+  uint32_t row[D / 16];
+  int tr[D / 32][2];
+  __device__ explicit LaneOff(int lane) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = 16 * BGeo<D>::slot(lane % 32, 2 * ks + lane / 32);
+    tr_offsets<D>(lane, tr);
+  }
+};
+
+// The LDS byte address of a tile, hidden from the compiler's address
+// arithmetic (which otherwise rebuilds every operand address of a tile from
+// the ring's loop-carried pieces): each address below is then one add.
+typedef __attribute__((address_space(3))) const char* lds_cptr;
+__device__ __forceinline__ uint32_t tile_base(const char* p) {
+  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)p));
+  asm volatile("" : "+s"(a));
+  return a;
+}
+__device__ __forceinline__ lds_cptr lds_at(uint32_t a) { return (lds_cptr)static_cast<uintptr_t>(a); }
+
 // The KS products over d of tile rows lane % 32 with the register fragments
 // b (one key per lane): all A operands are read before the first MFMA, so
 // that the LDS latency is paid once per tile.
 template <int D>
-__device__ __forceinline__ f32x16 tile_scores(const char* tile, const bf16x8 (&b)[D / 16], int lane) {
+__device__ __forceinline__ f32x16 tile_scores(const char* tile, const LaneOff<D>& lo, const bf16x8 (&b)[D / 16]) {
   constexpr int KS = D / 16;
   bf16x8 a[KS];
+  const uint32_t base = tile_base(tile);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) a[ks] = row_operand<D>(tile, lane % 32, ks, lane);
+  for (int ks = 0; ks < KS; ++ks) {
+    a[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(
+                                           lds_at(base + lo.row[ks])));
+  }
   __builtin_amdgcn_sched_barrier(0);
   f32x16 acc = {};
 #pragma unroll
@@ -282,14 +312,23 @@ __device__ __forceinline__ f32x16 tile_scores(const char* tile, const bf16x8 (&b
 // come from the transpose reads, the B operands w[kc] hold the weights of
 // accumulator elements 8 kc .. 8 kc + 7 (rows 16 kc .. 16 kc + 15).
 template <int D>
-__device__ __forceinline__ void tile_accumulate(const char* tile, const int (&toff)[D / 32][2],
-                                                const bf16x8 (&w)[2], f32x16 (&acc)[D / 32]) {
+__device__ __forceinline__ void tile_accumulate(const char* tile, const LaneOff<D>& lo, const bf16x8 (&w)[2],
+                                                f32x16 (&acc)[D / 32]) {
   constexpr int DB = D / 32;
   bf16x8 a[2][DB];
+  const uint32_t base = tile_base(tile);
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) a[kc][db] = tr_operand<D>(tile, toff[db], kc);
+    for (int db = 0; db < DB; ++db) {
+      constexpr int RB = BGeo<D>::CPR * 16;       // bytes per row
+      const v4i16b x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16b*)(lds_at(base + lo.tr[db][0]) + 16 * kc * RB));
+      const v4i16b x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16b*)(lds_at(base + lo.tr[db][1]) + 16 * kc * RB));
+      const v8i16b cat = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      a[kc][db] = __builtin_bit_cast(bf16x8, cat);
+    }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
@@ -298,46 +337,53 @@ __device__ __forceinline__ void tile_accumulate(const char* tile, const int (&to
 }
 
 // P wave, one query tile: bit il of vm says that tile row il is visible to
-// this lane's key. P goes to pw[i * 64] (i < 4, elements 4 i .. 4 i + 3),
-// hidden pairs as +0 (an AND with the pair's sign-extended bit).
+// this lane's key; masked false promises that every bit of every lane is
+// set (a uniform branch skips the masking). P goes to pw[i * 64] (i < 4,
+// elements 4 i .. 4 i + 3), hidden pairs as +0 (an AND with the pair's
+// sign-extended bit).
 template <int D>
-__device__ __forceinline__ void p_tile(const char* Qs, const char* Os, const float* lse,
-                                       const bf16x8 (&kf)[D / 16], const int (&toff)[D / 32][2],
-                                       float scale_log2, int lane, uint32_t vm, f32x4* pw,
-                                       f32x16 (&dv)[D / 32]) {
+__device__ __forceinline__ void p_tile(const char* Qs, const char* Os, const float* lse, const bf16x8 (&kf)[D / 16],
+                                       const LaneOff<D>& lo, float scale_log2, int lane, uint32_t vm, bool masked,
+                                       f32x4* pw, f32x16 (&dv)[D / 32]) {
   const int hsel = lane / 32;
-  const uint32_t vh = vm >> (4 * hsel);           // bit 8 (r / 4) + r % 4: accumulator element r
-  const f32x16 sc = tile_scores<D>(Qs, kf, lane);
+  f32x4 l4[4];                                    // lse of rows 8 i + 4 (lane / 32) + e
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l4[i] = *reinterpret_cast<const f32x4*>(lse + 8 * i + 4 * hsel);
+  const f32x16 sc = tile_scores<D>(Qs, lo, kf);
   float p[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int il = 8 * (r / 4) + 4 * hsel + (r % 4);                  // query row of element r
-    const float e = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -lse[il] * kLog2e));
-    const uint32_t keep = __builtin_amdgcn_sbfe(vh, 8 * (r / 4) + (r % 4), 1);
-    uint32_t pb;                                  // (the compiler would make the AND a compare and select)
-    asm("v_and_b32 %0, %1, %2" : "=v"(pb) : "v"(__builtin_bit_cast(uint32_t, e)), "v"(keep));
-    p[r] = __builtin_bit_cast(float, pb);
+  for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -l4[r / 4][r % 4] * kLog2e));
+  if (masked) {
+    const uint32_t vh = vm >> (4 * hsel);         // bit 8 (r / 4) + r % 4: accumulator element r
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t keep = __builtin_amdgcn_sbfe(vh, 8 * (r / 4) + (r % 4), 1);
+      uint32_t pb;                                // (the compiler would make the AND a compare and select)
+      asm("v_and_b32 %0, %1, %2" : "=v"(pb) : "v"(__builtin_bit_cast(uint32_t, p[r])), "v"(keep));
+      p[r] = __builtin_bit_cast(float, pb);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) pw[i * kWave] = f32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
   const bf16x8 w[2] = {pack8(p), pack8(p + 8)};
-  tile_accumulate<D>(Os, toff, w, dv);
+  tile_accumulate<D>(Os, lo, w, dv);
 }
 
 // dS wave, the tile whose P the P wave left at pr and whose dP is dp.
 template <int D>
 __device__ __forceinline__ void ds_tile(const char* Qs, const float* dlt, const f32x4* pr, const f32x16& dp,
-                                        const int (&toff)[D / 32][2], int lane, f32x16 (&dk)[D / 32]) {
+                                        const LaneOff<D>& lo, int lane, f32x16 (&dk)[D / 32]) {
   const int hsel = lane / 32;
   float ds[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const f32x4 pq = pr[i * kWave];
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + 8 * i + 4 * hsel);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ds[4 * i + e] = pq[e] * (dp[4 * i + e] - dlt[8 * i + 4 * hsel + e]);
+    for (int e = 0; e < 4; ++e) ds[4 * i + e] = pq[e] * (dp[4 * i + e] - d4[e]);
   }
   const bf16x8 w[2] = {pack8(ds), pack8(ds + 8)};
-  tile_accumulate<D>(Qs, toff, w, dk);
+  tile_accumulate<D>(Qs, lo, w, dk);
 }
 
 // Bits [lo, hi) of a 32-row tile, the bounds clamped to the tile.
@@ -379,7 +425,24 @@ __device__ __forceinline__ void bw_dma4(const void* base, uint32_t off, uint32_t
                :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
 
+// Position of a query tile in a key block's sequence: query tile q of head h
+// of the group, advanced one tile at a time (no divisions in the loop).
+struct TileSeq {
+  int h, q;
+  __device__ void next(int ntq) {
+    if (++q == ntq) {
+      q = 0;
+      ++h;
+    }
+  }
+};
+
+// The LDS byte address of p, computed once (wave-uniform).
+__device__ __forceinline__ uint32_t lds_u32(const char* p) { return tile_base(p); }
+
 // The dS wave reads tile t - 1 while tile t + AHEAD lands: NST = AHEAD + 2.
+// Stages are named by index (0 .. NST - 1); the DMA geometry of this lane is
+// computed once.
 template <int D, int NW>
 struct QRing {
   static constexpr int CPR = BGeo<D>::CPR;
@@ -393,76 +456,93 @@ struct QRing {
   static constexpr int BYTES = NST * STAGE;
   static_assert(NINS % NW == 0 || NINS < NW, "whole instructions per wave");
   char* ring;                                     // NST x [Q | dO | lse (64) | delta (64)]
-  char* junk;                                     // NW x 1 KB, targets of dummy ops
-  __device__ char* q(int t) const { return ring + (t % NST) * STAGE; }
-  __device__ char* o(int t) const { return q(t) + TB; }
-  __device__ float* l(int t) const { return reinterpret_cast<float*>(q(t) + 2 * TB); }
-  __device__ float* d(int t) const { return l(t) + 64; }
-  // the DMA ops of tile t (rows qt0.. of query row block hrow), or dummies
-  __device__ void issue(const BwdArgs& P, bool real, int64_t hrow, int qt0, int t) const {
+  uint32_t ring_lds;                              // LDS address of the ring
+  uint32_t junk_lds;                              // this wave's 1 KB junk row, target of dummy ops
+  int wave;
+  int row[PERW];                                  // this lane's tile row and byte column, per op
+  uint32_t col[PERW];
+  __device__ QRing(char* ring_, char* junk) : ring(ring_) {
     const int lane = threadIdx.x % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    ring_lds = lds_u32(ring_);
+    junk_lds = lds_u32(junk) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) {
+      const int sl = (wave * PERW + i) * kWave + lane;
+      row[i] = sl / CPR;
+      col[i] = 16 * ((sl % CPR) ^ BGeo<D>::swz(row[i]));
+    }
+  }
+  __device__ char* q(int st) const { return ring + st * STAGE; }
+  __device__ char* o(int st) const { return q(st) + TB; }
+  __device__ float* l(int st) const { return reinterpret_cast<float*>(q(st) + 2 * TB); }
+  __device__ float* d(int st) const { return l(st) + 64; }
+  // the DMA ops of one tile (rows qt0.. of query row block hrow) into stage
+  // st, or dummies into the junk row (hrow must still be a valid row block)
+  __device__ void issue(const BwdArgs& P, bool real, int64_t hrow, int qt0, int st) const {
+    const int lane = threadIdx.x % kWave;
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(P.q) + hrow * D;
     const uint16_t* ob = reinterpret_cast<const uint16_t*>(P.dout) + hrow * D;
-    char* jw = junk + wave * 1024;
+    const uint32_t sb = ring_lds + st * STAGE;
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
       const int ins = wave * PERW + i;
       const bool rw = real && ins < NINS;
-      const int sl = ins * kWave + lane;
-      const int r = sl / CPR;
-      const int c = (sl % CPR) ^ BGeo<D>::swz(r);
-      const uint32_t off = rw ? static_cast<uint32_t>(min(qt0 + r, P.S - 1) * (D * 2) + 16 * c) : 0u;
-      bw_dma16(qb, off, __builtin_amdgcn_readfirstlane(bw_lds(rw ? q(t) + ins * 1024 : jw)));
-      bw_dma16(ob, off, __builtin_amdgcn_readfirstlane(bw_lds(rw ? o(t) + ins * 1024 : jw)));
+      const uint32_t off = rw ? static_cast<uint32_t>(min(qt0 + row[i], P.S - 1) * (D * 2)) + col[i] : 0u;
+      bw_dma16(qb, off, rw ? sb + ins * 1024 : junk_lds);
+      bw_dma16(ob, off, rw ? sb + TB + ins * 1024 : junk_lds);
     }
     const bool rl = real && wave == 0;
     const uint32_t offl = rl ? 4u * static_cast<uint32_t>(min(qt0 + lane % 32, P.S - 1)) : 0u;
-    bw_dma4(P.lse + hrow, offl, __builtin_amdgcn_readfirstlane(bw_lds(rl ? reinterpret_cast<char*>(l(t)) : jw)));
-    bw_dma4(P.delta + hrow, offl, __builtin_amdgcn_readfirstlane(bw_lds(rl ? reinterpret_cast<char*>(d(t)) : jw)));
+    bw_dma4(P.lse + hrow, offl, rl ? sb + 2 * TB : junk_lds);
+    bw_dma4(P.delta + hrow, offl, rl ? sb + 2 * TB + 256 : junk_lds);
   }
 };
 
 // P of the last two query tiles, per key group and lane: [2][4][4][64] f32x4.
 constexpr int kPBytes = 2 * 4 * 4 * kWave * 16;
 __device__ __forceinline__ f32x4* p_slot(char* pbuf, int t, int kg, int lane) {
-  return reinterpret_cast<f32x4*>(pbuf) + ((t % 2) * 4 + kg) * 4 * kWave + lane;
+  return reinterpret_cast<f32x4*>(pbuf) + ((t & 1) * 4 + kg) * 4 * kWave + lane;
 }
 
-// Run compute(t) for t = 0 .. nt (t = nt: no tile, the dS waves' last step);
-// tile(t) gives (hrow, qt0) of tile t < nt. Every global load and store of
-// the workgroup issued before the call must be complete or unrelated to
-// vmcnt ordering: the call starts with a full wait. LDS stores of compute(t)
-// are complete before compute(t + 1) starts on any wave (the wait of the
-// tile count includes lgkmcnt(0) and precedes the publishing barrier).
-template <class RG, class TileOf, class Compute>
-__device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R, int nt, TileOf tile,
-                                                   Compute compute) {
+// Run compute(t, st) for t = 0 .. nt, st the ring stage of tile t (t = nt:
+// no tile, the dS waves' last step). The tiles are those of the sequence
+// from s0 (ntq query tiles per head, the first at row qs0; hrow_of(h) the
+// query row block of head h). Every global load and store of the workgroup
+// issued before the call must be complete or unrelated to vmcnt ordering:
+// the call starts with a full wait. LDS stores of compute(t) are complete
+// before compute(t + 1) starts on any wave (the wait of the tile count
+// includes lgkmcnt(0) and precedes the publishing barrier).
+template <class RG, class HRow, class Compute>
+__device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R, int nt, TileSeq s0, int ntq,
+                                                   int qs0, HRow hrow_of, Compute compute) {
   bw_fence();
   __builtin_amdgcn_s_waitcnt(0);
   bw_fence();
+  const int64_t hrow0 = hrow_of(s0.h);
+  TileSeq is = s0;                                // next tile to issue
+  int ist = 0;                                    // its stage
+  int left = nt;                                  // tiles not yet issued
+  auto issue_next = [&]() {
+    const bool real = left > 0;
+    R.issue(P, real, real ? hrow_of(is.h) : hrow0, qs0 + is.q * QB, ist);
+    if (real) is.next(ntq);
+    --left;
+    ist = ist + 1 == RG::NST ? 0 : ist + 1;
+  };
 #pragma unroll
-  for (int t = 0; t < RG::AHEAD; ++t) {
-    int64_t hrow;
-    int qt0;
-    tile(t < nt ? t : 0, &hrow, &qt0);
-    R.issue(P, t < nt, hrow, qt0, t);
-  }
+  for (int t = 0; t < RG::AHEAD; ++t) issue_next();
+  int st = 0;
   for (int t = 0; t <= nt; ++t) {
     bw_fence();
     __builtin_amdgcn_s_barrier();                 // compute(t - 1) done by every wave
     bw_fence();
-    {
-      const int tn = t + RG::AHEAD;
-      int64_t hrow;
-      int qt0;
-      tile(tn < nt ? tn : 0, &hrow, &qt0);
-      R.issue(P, tn < nt, hrow, qt0, tn);
-    }
+    issue_next();
     bw_wait_vm<RG::AHEAD * RG::OPS>();            // this wave's parts of tile t landed
     __builtin_amdgcn_s_barrier();
     bw_fence();
-    compute(t);
+    compute(t, st);
+    st = st + 1 == RG::NST ? 0 : st + 1;
   }
   bw_fence();
   __builtin_amdgcn_s_waitcnt(0);                  // no DMA still landing (dummies included)
@@ -479,27 +559,40 @@ __device__ __forceinline__ void load_key_bf16(const uint16_t* base, int j, int l
 }
 
 // The query tile loop of one wave of a key group's pair: the P wave on tile
-// t, the dS wave on tile t - 1 (dS, dK) and tile t (dP). vis(t) gives the
-// visibility mask of tile t for this lane's key; a tile that no lane of the
-// group sees is skipped by both waves alike. The two roles run separate
-// loops (with the same barriers), so that each is register-allocated alone.
-template <int D, class Ring, class TileOf, class Vis>
-__device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char* pbuf, int nt, TileOf tile,
-                                          bool pwave, int kg, int lane, const bf16x8 (&kv)[D / 16],
-                                          const int (&toff)[D / 32][2], Vis vis, f32x16 (&acc)[D / 32]) {
+// t, the dS wave on tile t - 1 (dS, dK) and tile t (dP). vis(qt0) gives the
+// visibility mask of the tile at row qt0 for this lane's key; a tile that
+// no lane of the group sees is skipped by both waves alike. The two roles
+// run separate loops (with the same barriers), so that each is
+// register-allocated alone.
+template <int D, class Ring, class HRow, class Vis>
+__device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char* pbuf, int nt, TileSeq s0, int ntq,
+                                          int qs0, HRow hrow_of, bool pwave, int kg, int lane,
+                                          const bf16x8 (&kv)[D / 16], const LaneOff<D>& lo, Vis vis,
+                                          f32x16 (&acc)[D / 32]) {
+  TileSeq cs = s0;                                // tile t
   if (pwave) {
-    stream_query_tiles(P, R, nt, tile, [&](int t) {
+    stream_query_tiles(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
       if (t == nt) return;
-      const uint32_t vm = vis(t);
+      const uint32_t vm = vis(qs0 + cs.q * QB);
+      cs.next(ntq);
       if (ballot(vm != 0u) == 0) return;
-      p_tile<D>(R.q(t), R.o(t), R.l(t), kv, toff, P.scale_log2, lane, vm, p_slot(pbuf, t, kg, lane), acc);
+      p_tile<D>(R.q(st), R.o(st), R.l(st), kv, lo, P.scale_log2, lane, vm, ballot(vm != ~0u) != 0,
+                p_slot(pbuf, t, kg, lane), acc);
     });
   } else {
     f32x16 dp = {};
-    stream_query_tiles(P, R, nt, tile, [&](int t) {
-      if (t > 0 && ballot(vis(t - 1) != 0u) != 0)
-        ds_tile<D>(R.q(t - 1), R.d(t - 1), p_slot(pbuf, t - 1, kg, lane), dp, toff, lane, acc);
-      if (t < nt && ballot(vis(t) != 0u) != 0) dp = tile_scores<D>(R.o(t), kv, lane);
+    bool prev = false;                            // tile t - 1 seen by the group
+    stream_query_tiles(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
+      if (prev) {
+        const int sp = st == 0 ? Ring::NST - 1 : st - 1;
+        ds_tile<D>(R.q(sp), R.d(sp), p_slot(pbuf, t - 1, kg, lane), dp, lo, lane, acc);
+      }
+      prev = false;
+      if (t < nt) {
+        prev = ballot(vis(qs0 + cs.q * QB) != 0u) != 0;
+        cs.next(ntq);
+        if (prev) dp = tile_scores<D>(R.o(st), lo, kv);
+      }
     });
   }
 }
@@ -517,8 +610,14 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
   const int kg = wave % 4;                        // key group
   const bool pwave = wave < 4;
   const int hsel = lane / 32;
-  const int kt = blockIdx.x % n_kt;
-  const int bgi = blockIdx.x / n_kt;
+  // workgroups are dealt to the 8 XCDs in turn: give each XCD a run of
+  // consecutive key blocks, whose query windows overlap, to share its L2
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % 8, xk = blockIdx.x / 8;
+  const int xq = nwg / 8, xr = nwg % 8;
+  const int idx = xcd < xr ? xcd * (xq + 1) + xk : xr * (xq + 1) + (xcd - xr) * xq + xk;
+  const int kt = idx % n_kt;
+  const int bgi = idx / n_kt;
   const int g = bgi % P.Hkv;
   const int b = bgi / P.Hkv;
   const int S = P.S;
@@ -532,8 +631,7 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
   load_key_bf16<D>((pwave ? reinterpret_cast<const uint16_t*>(P.k) : reinterpret_cast<const uint16_t*>(P.v)) +
                        kvrow * D,
                    jc, lane, kv);
-  int toff[KG::DB][2];
-  tr_offsets<D>(lane, toff);
+  const LaneOff<D> lo(lane);
   f32x16 acc[KG::DB];
 #pragma unroll
   for (int db = 0; db < KG::DB; ++db) acc[db] = f32x16{};
@@ -543,15 +641,9 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
   const int ntq = (qend - j0 + QB - 1) / QB;
   const int nt = P.G * ntq;
   const int hi_j = own ? j + min(S - j, P.n) : 0;  // rows i with j <= i < j + n, i < S
-  auto tile = [&](int t, int64_t* hrow, int* qt0) {
-    *hrow = static_cast<int64_t>(b * P.Hq + g * P.G + t / ntq) * S;
-    *qt0 = j0 + (t % ntq) * QB;
-  };
-  auto vis = [&](int t) {
-    const int qt0 = j0 + (t % ntq) * QB;
-    return own ? row_range(j - qt0, hi_j - qt0) : 0u;
-  };
-  pair_loop<D>(P, R, pbuf, nt, tile, pwave, kg, lane, kv, toff, vis, acc);
+  auto hrow_of = [&](int h) { return static_cast<int64_t>(b * P.Hq + g * P.G + h) * S; };
+  auto vis = [&](int qt0) { return own ? row_range(j - qt0, hi_j - qt0) : 0u; };
+  pair_loop<D>(P, R, pbuf, nt, TileSeq{0, 0}, ntq, j0, hrow_of, pwave, kg, lane, kv, lo, vis, acc);
   if (j < S) {
     float* dst = (pwave ? P.dv : P.dk) + (kvrow + j) * D;
     const float f = pwave ? 1.0f : P.scale;
@@ -564,18 +656,27 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
   }
 }
 
+// dK, dV of the initial and separator keys ("global" keys: the list of
+// initial positions, then sep_pos). Key tile u holds list entries
+// [128 u, 128 u + 128); it meets every query row from its first key's
+// position on, per head of the group: G * ntq(u) steps of one 32-row query
+// tile. The steps of a kv head, key tile by key tile, are cut into nslots
+// equal ranges, one per workgroup; a workgroup adds its partial dK, dV to
+// memory (fp32 atomics) once per key tile its range touches, so the
+// accumulation over query rows stays in registers for whole ranges.
 template <int D>
-__global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArgs P, int n_qc, int nslots) {
+__global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArgs P, int nslots) {
   using KG = KVGeo<D>;
   using Ring = QRing<D, KG::NWAVE>;
+  constexpr int NTH = KG::NTH;
   constexpr int RED = KG::NWAVE * 32 * 64 * 4;    // one 64-column pass of every wave's partial
   constexpr int SM = Ring::BYTES + kPBytes;
   static_assert(RED <= SM, "the flush buffer aliases the ring and the P buffers");
   __shared__ __attribute__((aligned(1024))) char smem[SM];
   __shared__ __attribute__((aligned(1024))) char junkmem[KG::NWAVE * 1024];
   __shared__ int32_t kpos[KB];
-  __shared__ int32_t tstart[kMaxChunks + 1];
   __shared__ int32_t wsum[KG::NWAVE];
+  __shared__ int32_t start[2];                    // first key tile of the range, first step in it
   const Ring R{smem, junkmem};
   char* pbuf = smem + Ring::BYTES;
   // one wave's partial over 64 columns, key-major, column ^ key: [NWAVE][32][64]
@@ -592,32 +693,75 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
   const int g = bgi % P.Hkv;
   const int b = bgi / P.Hkv;
   const int S = P.S;
+  const int G = P.G;
   const int32_t* rk = P.rank + static_cast<int64_t>(b) * (S + 1);
   const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * S;
   const int ninit = min(P.a, S);
   const int rank_a = rk[ninit];
-  auto n_global = [&](int c1) { return min(ninit, c1) + (c1 > ninit ? rk[c1] - rank_a : 0); };
-  const int total = chunk_tile_prefix<KG::NTH>(n_global, S, n_qc, tstart, wsum);
+  const int n_gl = ninit + rk[S] - rank_a;        // global keys of the sequence
+  auto entry_pos = [&](int e) { return e < ninit ? e : sp[rank_a + (e - ninit)]; };
+  const int nqt = (S + QB - 1) / QB;
+  const int nkt = (n_gl + KB - 1) / KB;
+  auto ntq_of = [&](int u) { return nqt - entry_pos(KB * u) / QB; };
+
+  // Query tiles per key tile, summed: each thread a segment of key tiles,
+  // an exclusive scan over the threads.
+  const int seg = (nkt + NTH - 1) / NTH;
+  const int ub = min(tid * seg, nkt);
+  const int ue = min(ub + seg, nkt);
+  int local = 0;
+  for (int u = ub; u < ue; ++u) local += ntq_of(u);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  if (tid == 0) start[0] = -1;
+  __syncthreads();
+  int excl = incl - local;
+  int tot_q = 0;
+  for (int w = 0; w < KG::NWAVE; ++w) {
+    if (w < wave) excl += wsum[w];
+    tot_q += wsum[w];
+  }
+  const int64_t total = static_cast<int64_t>(G) * tot_q;
+  const int64_t s0 = total * slot / nslots;
+  const int64_t s1 = total * (slot + 1) / nslots;
+  // the thread whose key tiles hold step s0 records where the range starts
+  if (s0 < s1 && static_cast<int64_t>(G) * excl <= s0 && s0 < static_cast<int64_t>(G) * (excl + local)) {
+    int64_t before = static_cast<int64_t>(G) * excl;
+    int u = ub;
+    for (;; ++u) {
+      const int64_t su = static_cast<int64_t>(G) * ntq_of(u);
+      if (s0 < before + su) break;
+      before += su;
+    }
+    start[0] = u;
+    start[1] = static_cast<int>(s0 - before);
+  }
+  __syncthreads();
 
   const int64_t kvrow = static_cast<int64_t>(b * P.Hkv + g) * S;
   const uint16_t* kvb =
       (pwave ? reinterpret_cast<const uint16_t*>(P.k) : reinterpret_cast<const uint16_t*>(P.v)) + kvrow * D;
   float* dst = (pwave ? P.dv : P.dk) + kvrow * D;
   const float f = pwave ? 1.0f : P.scale;
-  int toff[KG::DB][2];
-  tr_offsets<D>(lane, toff);
+  const LaneOff<D> lo(lane);
 
-  for (int w = slot; w < total; w += nslots) {
-    const int qc = chunk_of(tstart, n_qc, w);
-    const int u0 = (w - tstart[qc]) * KB;
-    const int c0 = qc * QCH;
-    const int c1 = min(c0 + QCH, S);
-    const int n_in = min(ninit, c1);
-    const int n_gl = n_global(c1);
-    __syncthreads();                              // kpos and the tiles of the previous item are consumed
-    for (int u = tid; u < KB; u += KG::NTH) {
-      const int uu = u0 + u;
-      kpos[u] = uu >= n_gl ? -1 : (uu < n_in ? uu : sp[rank_a + (uu - n_in)]);
+  int u = __builtin_amdgcn_readfirstlane(start[0]);   // (LDS values are not known to be uniform)
+  int k0 = __builtin_amdgcn_readfirstlane(start[1]);
+  int64_t rem = s1 - s0;
+  while (rem > 0) {
+    const int qs0 = entry_pos(KB * u) / QB * QB;
+    const int ntq = nqt - qs0 / QB;
+    const int su = G * ntq;
+    const int k1 = static_cast<int>(min(static_cast<int64_t>(su), k0 + rem));
+    __syncthreads();                              // kpos and the tiles of the previous key tile are consumed
+    for (int e = tid; e < KB; e += NTH) {
+      const int ee = KB * u + e;
+      kpos[e] = ee < n_gl ? entry_pos(ee) : -1;
     }
     __syncthreads();
     const int j = kpos[32 * kg + lane % 32];      // this lane's key, -1 past the list
@@ -626,20 +770,10 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
     f32x16 acc[KG::DB];
 #pragma unroll
     for (int db = 0; db < KG::DB; ++db) acc[db] = f32x16{};
-    const int jlo = kpos[0];
-    const int qs0 = max(c0, jlo) / QB * QB;
-    const int ntq = (c1 - qs0 + QB - 1) / QB;
-    const int nt = P.G * ntq;
-    const int lo_j = max(c0, j);                  // rows i of the chunk [c0, c1) with i >= j
-    auto tile = [&](int t, int64_t* hrow, int* qt0) {
-      *hrow = static_cast<int64_t>(b * P.Hq + g * P.G + t / ntq) * S;
-      *qt0 = qs0 + (t % ntq) * QB;
-    };
-    auto vis = [&](int t) {
-      const int qt0 = qs0 + (t % ntq) * QB;
-      return j >= 0 ? row_range(lo_j - qt0, c1 - qt0) : 0u;
-    };
-    pair_loop<D>(P, R, pbuf, nt, tile, pwave, kg, lane, kv, toff, vis, acc);
+    auto hrow_of = [&](int h) { return static_cast<int64_t>(b * P.Hq + g * G + h) * S; };
+    auto vis = [&](int qt0) { return j >= 0 ? row_range(j - qt0, S - qt0) : 0u; };   // rows i >= j, i < S
+    pair_loop<D>(P, R, pbuf, k1 - k0, TileSeq{k0 / ntq, k0 % ntq}, ntq, qs0, hrow_of, pwave, kg, lane, kv, lo,
+                 vis, acc);
     // Add the partials with fp32 atomics, key row by key row through LDS, so
     // that each atomic instruction covers 2 x 32 consecutive floats of two
     // rows (2 cache lines) instead of one float of 32 rows; 64 columns a pass.
@@ -666,6 +800,9 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
       }
       __syncthreads();
     }
+    rem -= k1 - k0;
+    k0 = 0;
+    ++u;
   }
 }
 
@@ -673,21 +810,18 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
 
 hipError_t launch_bf16_kernels(const BwdArgs& A, int D, hipStream_t st) {
   const int n_kt = (A.S + KB - 1) / KB;
-  const int n_qc = (A.S + QCH - 1) / QCH;
   const int BH = A.B * A.Hkv;
-  const int nslots = BH >= 512 ? 1 : 512 / BH;   // twice the resident workgroups on 256 CUs
+  const int nslots = BH >= 256 ? 1 : 256 / BH;   // one workgroup per CU (their LDS allows no more)
   if (D == 128) {
     hipLaunchKernelGGL((dq_bf16_kernel<128>), dim3(A.B * A.Hkv * A.n_hg * A.n_qt), dim3(BT), 0, st, A);
     hipLaunchKernelGGL((dkdv_band_bf16_kernel<128>), dim3(A.B * A.Hkv * n_kt), dim3(KVGeo<128>::NTH), 0, st, A,
                        n_kt);
-    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<128>), dim3(BH * nslots), dim3(KVGeo<128>::NTH), 0, st, A, n_qc,
-                       nslots);
+    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<128>), dim3(BH * nslots), dim3(KVGeo<128>::NTH), 0, st, A, nslots);
   } else {
     hipLaunchKernelGGL((dq_bf16_kernel<64>), dim3(A.B * A.Hkv * A.n_hg * A.n_qt), dim3(BT), 0, st, A);
     hipLaunchKernelGGL((dkdv_band_bf16_kernel<64>), dim3(A.B * A.Hkv * n_kt), dim3(KVGeo<64>::NTH), 0, st, A,
                        n_kt);
-    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<64>), dim3(BH * nslots), dim3(KVGeo<64>::NTH), 0, st, A, n_qc,
-                       nslots);
+    hipLaunchKernelGGL((dkdv_glob_bf16_kernel<64>), dim3(BH * nslots), dim3(KVGeo<64>::NTH), 0, st, A, nslots);
   }
   return hipGetLastError();
 }
