@@ -94,23 +94,83 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// The LDS byte address of a tile, hidden from the compiler's address
+// arithmetic (which otherwise rebuilds every operand address of a tile from
+// the ring's loop-carried pieces): each address below is then one add.
+typedef __attribute__((address_space(3))) const char* lds_cptr;
+__device__ __forceinline__ uint32_t tile_base(const char* p) {
+  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)p));
+  asm volatile("" : "+s"(a));
+  return a;
+}
+__device__ __forceinline__ lds_cptr lds_at(uint32_t a) { return (lds_cptr)static_cast<uintptr_t>(a); }
+
+// Helpers of the LDS-DMA tile loads (global_load_lds: no register results).
+__device__ __forceinline__ void bw_fence() { asm volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void bw_wait_vm() {    // s_waitcnt vmcnt(N) lgkmcnt(0)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+__device__ __forceinline__ uint32_t bw_lds(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Lane l's 16 (or 4) bytes from base + off land at LDS lds_base + 16 l (or
+// 4 l); base and lds_base wave-uniform (taken from the first lane, so that
+// they sit in scalar registers even where the compiler cannot prove them
+// uniform). M0 carries the LDS base; these kernels make no other use of M0.
+__device__ __forceinline__ const void* bw_uniform(const void* p) {
+  const uint64_t v = reinterpret_cast<uintptr_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<const void*>(static_cast<uintptr_t>(lo | (hi << 32)));
+}
+__device__ __forceinline__ void bw_dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(bw_uniform(base)), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void bw_dma4(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(bw_uniform(base)), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+}
+
+// Position of a query tile in a key block's sequence: query tile q of head h
+// of the group, advanced one tile at a time (no divisions in the loop).
+struct TileSeq {
+  int h, q;
+  __device__ void next(int ntq) {
+    if (++q == ntq) {
+      q = 0;
+      ++h;
+    }
+  }
+};
+
 // ---------------------------------------------------------------- dQ (bf16)
-// The forward's work items; the key tiles of 64 stream through LDS with a
-// one-tile register prefetch, their indices two tiles ahead.
+// The forward's work items; the key tiles of 64 (gathered rows: initial and
+// separator keys, then the band) land in a two-stage LDS ring by LDS-DMA one
+// tile ahead, their indices two tiles ahead.
 template <int D>
-__global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
+__global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
   using G = BGeo<D>;
   constexpr int CPR = G::CPR, KS = G::KS, DB = G::DB;
   constexpr int TILEB = KTQ * D * 2;
-  constexpr int LOADS = KTQ * CPR / BT;
-  __shared__ __attribute__((aligned(16))) char kst[TILEB];
-  __shared__ __attribute__((aligned(16))) char vst[TILEB];
+  constexpr int NINS = TILEB / 1024;              // 1 KB DMA ops per tensor and tile
+  constexpr int PERW = NINS / BW;
+  constexpr int OPS = 2 * PERW;
+  static_assert(NINS % BW == 0, "whole DMA ops per wave");
+  __shared__ __attribute__((aligned(1024))) char kring[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char vring[2 * TILEB];
   __shared__ int32_t idxbuf[3][KTQ];
   __shared__ uint64_t sepbits[3];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hsel = lane / 32;
 
   PrefillArgs W;
@@ -166,14 +226,26 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
     idxbuf[t % 3][lane] = key;
     if (lane == 0) sepbits[t % 3] = bits;
   };
-  u32x4 kr[LOADS], vr[LOADS];
-  auto load_rows = [&](int t) {
+  // this lane's row and byte column in each of its DMA ops (the LDS chunk
+  // swizzle goes into the global offsets)
+  int drow[PERW];
+  uint32_t dcol[PERW];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int row = tid / CPR + i * (BT / CPR);
-      const int64_t off = static_cast<int64_t>(idxbuf[t % 3][row]) * D + 8 * (tid % CPR);
-      kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
+  for (int i = 0; i < PERW; ++i) {
+    const int sl = (wave * PERW + i) * kWave + lane;
+    drow[i] = sl / CPR;
+    dcol[i] = 16 * ((sl % CPR) ^ G::swz(drow[i]));
+  }
+  const uint32_t k_lds = tile_base(kring);
+  const uint32_t v_lds = tile_base(vring);
+  auto issue = [&](int t) {                       // the DMA ops of tile t into stage t % 2
+    const uint32_t st = (t & 1) * TILEB;
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) {
+      const uint32_t off = static_cast<uint32_t>(idxbuf[t % 3][drow[i]]) * (D * 2) + dcol[i];
+      const uint32_t dst = st + (wave * PERW + i) * 1024;
+      bw_dma16(kb, off, k_lds + dst);
+      bw_dma16(vb, off, v_lds + dst);
     }
   };
   if (wave == 0) {
@@ -181,7 +253,7 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
     if (ti.ntiles > 1) index_store(1);
   }
   __syncthreads();
-  if (ti.ntiles > 0) load_rows(0);
+  if (ti.ntiles > 0) issue(0);
 
   int toff[DB][2];
   tr_offsets<D>(lane, toff);
@@ -190,17 +262,22 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
   for (int db = 0; db < DB; ++db) dacc[db] = f32x16{};
 
   for (int t = 0; t < ti.ntiles; ++t) {
-    __syncthreads();                              // tile t - 1 consumed
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int row = tid / CPR + i * (BT / CPR);
-      const int sl = G::slot(row, tid % CPR);
-      *reinterpret_cast<u32x4*>(kst + 16 * sl) = kr[i];
-      *reinterpret_cast<u32x4*>(vst + 16 * sl) = vr[i];
-    }
+    bw_fence();
+    __builtin_amdgcn_s_barrier();                 // tile t - 1 consumed: its stage takes tile t + 1
+    bw_fence();
+    // index_store reads global memory and waits for it: before the DMA of
+    // tile t + 1, so that the wait does not cover that DMA
     if (wave == 0 && t + 2 < ti.ntiles) index_store(t + 2);
-    __syncthreads();                              // tile t and index t + 2 published
-    if (t + 1 < ti.ntiles) load_rows(t + 1);      // in flight during tile t
+    if (t + 1 < ti.ntiles) {
+      issue(t + 1);
+      bw_wait_vm<OPS>();                          // this wave's parts of tile t landed
+    } else {
+      bw_wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();                 // tile t and index t + 2 published
+    bw_fence();
+    const char* kst = kring + (t & 1) * TILEB;
+    const char* vst = vring + (t & 1) * TILEB;
 
     const bool band = t >= ti.ntg;
     const int jmin = band ? ti.band_lo + (t - ti.ntg) * KTQ : 0;
@@ -211,12 +288,19 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
         need_mask ? (vis_word(band, qi, jmin, P.n, P.a, sepbits[t % 3], nvalid) >> (4 * hsel)) : ~0ull;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      // the K rows' operands, then the V rows' (in flight during the S chain)
+      bf16x8 ak[KS], av[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ak[ks] = row_operand<D>(kst, 32 * mb + lane % 32, ks, lane);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) av[ks] = row_operand<D>(vst, 32 * mb + lane % 32, ks, lane);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 sc = {}, dp = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sc = mfma32x32x16(row_operand<D>(kst, 32 * mb + lane % 32, ks, lane), qf[ks], sc);
-        dp = mfma32x32x16(row_operand<D>(vst, 32 * mb + lane % 32, ks, lane), of[ks], dp);
-      }
+      for (int ks = 0; ks < KS; ++ks) sc = mfma32x32x16(ak[ks], qf[ks], sc);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(av[ks], of[ks], dp);
+      __builtin_amdgcn_sched_barrier(0);
       const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
       float ds[16];
 #pragma unroll
@@ -225,6 +309,7 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
         const float p = on ? fast_exp2(__builtin_fmaf(sc[r], P.scale_log2, -lse2)) : 0.0f;
         ds[r] = p * (dp[r] - dlt);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kcl = 0; kcl < 2; ++kcl) {
         const bf16x8 bds = pack8(ds + 8 * kcl);
@@ -232,6 +317,13 @@ __global__ void __launch_bounds__(BT, 1) dq_bf16_kernel(BwdArgs P) {
         for (int db = 0; db < DB; ++db)
           dacc[db] = mfma32x32x16(tr_operand<D>(kst, toff[db], 2 * mb + kcl), bds, dacc[db]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (qi < S) {
@@ -276,17 +368,6 @@ struct LaneOff {
     tr_offsets<D>(lane, tr);
   }
 };
-
-// The LDS byte address of a tile, hidden from the compiler's address
-// arithmetic (which otherwise rebuilds every operand address of a tile from
-// the ring's loop-carried pieces): each address below is then one add.
-typedef __attribute__((address_space(3))) const char* lds_cptr;
-__device__ __forceinline__ uint32_t tile_base(const char* p) {
-  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)p));
-  asm volatile("" : "+s"(a));
-  return a;
-}
-__device__ __forceinline__ lds_cptr lds_at(uint32_t a) { return (lds_cptr)static_cast<uintptr_t>(a); }
 
 // The KS products over d of tile rows lane % 32 with the register fragments
 // b (one key per lane): all A operands are read before the first MFMA, so
@@ -400,49 +481,13 @@ __device__ __forceinline__ uint32_t row_range(int lo, int hi) {
 // rows that only wave 0 loads), so one exact vmcnt count per tile says that
 // its own parts of tile t landed; a plain barrier then publishes the tile.
 // Rows are placed with the swizzle of BGeo through the global offsets.
-__device__ __forceinline__ void bw_fence() { asm volatile("" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void bw_wait_vm() {    // s_waitcnt vmcnt(N) lgkmcnt(0)
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-__device__ __forceinline__ uint32_t bw_lds(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-
-// Lane l's 16 (or 4) bytes from base + off land at LDS lds_base + 16 l (or
-// 4 l); base and lds_base wave-uniform. M0 carries the LDS base; these
-// kernels make no other use of M0.
-__device__ __forceinline__ void bw_dma16(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
-}
-__device__ __forceinline__ void bw_dma4(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
-}
-
-// Position of a query tile in a key block's sequence: query tile q of head h
-// of the group, advanced one tile at a time (no divisions in the loop).
-struct TileSeq {
-  int h, q;
-  __device__ void next(int ntq) {
-    if (++q == ntq) {
-      q = 0;
-      ++h;
-    }
-  }
-};
-
 // The LDS byte address of p, computed once (wave-uniform).
 __device__ __forceinline__ uint32_t lds_u32(const char* p) { return tile_base(p); }
 
-// The dS wave reads tile t - 1 while tile t + AHEAD lands: NST = AHEAD + 2.
-// Stages are named by index (0 .. NST - 1); the DMA geometry of this lane is
-// computed once.
+// The dS wave reads tile t - 1 while tile t + AHEAD lands, and a wave may
+// still read tile t - 2 when another issues tile t + AHEAD (one barrier per
+// tile): NST = AHEAD + 3. Stages are named by index (0 .. NST - 1); the DMA
+// geometry of this lane is computed once.
 template <int D, int NW>
 struct QRing {
   static constexpr int CPR = BGeo<D>::CPR;
@@ -451,7 +496,7 @@ struct QRing {
   static constexpr int PERW = NINS >= NW ? NINS / NW : 1;   // per wave (dummies past NINS)
   static constexpr int OPS = 2 * PERW + 2;        // + one dword op each for lse and delta
   static constexpr int AHEAD = 3;
-  static constexpr int NST = AHEAD + 2;
+  static constexpr int NST = AHEAD + 3;
   static constexpr int STAGE = 2 * TB + 2 * 64 * 4;
   static constexpr int BYTES = NST * STAGE;
   static_assert(NINS % NW == 0 || NINS < NW, "whole instructions per wave");
@@ -510,9 +555,13 @@ __device__ __forceinline__ f32x4* p_slot(char* pbuf, int t, int kg, int lane) {
 // from s0 (ntq query tiles per head, the first at row qs0; hrow_of(h) the
 // query row block of head h). Every global load and store of the workgroup
 // issued before the call must be complete or unrelated to vmcnt ordering:
-// the call starts with a full wait. LDS stores of compute(t) are complete
-// before compute(t + 1) starts on any wave (the wait of the tile count
-// includes lgkmcnt(0) and precedes the publishing barrier).
+// the call starts with a full wait.
+// One barrier per tile, after the wait for tile t: every wave that passes
+// it at step t has finished compute(t - 1), and its LDS stores of compute(t
+// - 1) are complete (the wait includes lgkmcnt(0)). So compute(t) may read
+// what compute(t - 1) wrote, and the DMA of tile t + AHEAD, issued after the
+// barrier of step t - 1, only overwrites the stage of tile t - 3, which no
+// wave reads after compute(t - 2).
 template <class RG, class HRow, class Compute>
 __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R, int nt, TileSeq s0, int ntq,
                                                    int qs0, HRow hrow_of, Compute compute) {
@@ -534,8 +583,6 @@ __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R
   for (int t = 0; t < RG::AHEAD; ++t) issue_next();
   int st = 0;
   for (int t = 0; t <= nt; ++t) {
-    bw_fence();
-    __builtin_amdgcn_s_barrier();                 // compute(t - 1) done by every wave
     bw_fence();
     issue_next();
     bw_wait_vm<RG::AHEAD * RG::OPS>();            // this wave's parts of tile t landed
