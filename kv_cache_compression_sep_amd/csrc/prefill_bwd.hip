@@ -520,13 +520,11 @@ template <class T, int D>
 hipError_t launch_bwd(BwdArgs A, hipStream_t st) {
   constexpr bool kBf16 = std::is_same<T, uint16_t>::value;
   const int64_t rows = static_cast<int64_t>(A.B) * A.Hq * A.S;
-  hipLaunchKernelGGL((delta_kernel<T, D>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st, A);
   const int n_kt = (A.S + KB - 1) / KB;
   if constexpr (kBf16) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_bf16_kernels(A, D, st);
+    return launch_bf16_kernels(A, D, st);         // (delta comes from the dQ kernel)
   } else {
+    hipLaunchKernelGGL((delta_kernel<T, D>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st, A);
     hipLaunchKernelGGL((dq_kernel<T, D>), dim3(A.B * A.Hkv * A.n_hg * A.n_qt), dim3(BT), 0, st, A);
     hipLaunchKernelGGL((dkdv_band_kernel<T, D>), dim3(A.B * A.Hkv * n_kt), dim3(BT), 0, st, A, n_kt);
     // twice the resident workgroups (one per CU: register bound) on 256 CUs

@@ -205,7 +205,21 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
     }
   }
   const float lse2 = P.lse[hrow + qc] * kLog2e;
-  const float dlt = P.delta[hrow + qc];
+  // delta of this lane's query row, rowsum(dO o out) in fp32 (the two
+  // halves of d sit in lanes l and l + 32); stored for the dK/dV kernels,
+  // which run after this one
+  float dlt = 0.0f;
+  {
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(P.out) + (hrow + qc) * D + 8 * hsel;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dlt += static_cast<float>(of[ks][e]) * static_cast<float>(ov[e]);
+    }
+    dlt += __shfl_xor(dlt, 32);
+    if (hsel == 0 && qi < S) P.delta[hrow + qi] = dlt;
+  }
 
   const int32_t* rk = P.rank + static_cast<int64_t>(b) * (S + 1);
   const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * S;
@@ -301,14 +315,21 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(av[ks], of[ks], dp);
       __builtin_amdgcn_sched_barrier(0);
-      const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
       float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool on = (word >> (8 * (r / 4) + (r % 4))) & 1u;
-        const float p = on ? fast_exp2(__builtin_fmaf(sc[r], P.scale_log2, -lse2)) : 0.0f;
-        ds[r] = p * (dp[r] - dlt);
+      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(sc[r], P.scale_log2, -lse2));
+      if (need_mask) {                            // hidden pairs: P = +0 (AND with the sign-extended bit)
+        const uint32_t word = static_cast<uint32_t>(vis >> (32 * mb));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t keep = __builtin_amdgcn_sbfe(word, 8 * (r / 4) + (r % 4), 1);
+          uint32_t pb;                            // (the compiler would make the AND a compare and select)
+          asm("v_and_b32 %0, %1, %2" : "=v"(pb) : "v"(__builtin_bit_cast(uint32_t, ds[r])), "v"(keep));
+          ds[r] = __builtin_bit_cast(float, pb);
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] *= dp[r] - dlt;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kcl = 0; kcl < 2; ++kcl) {
