@@ -173,8 +173,8 @@ int sep_attn_prefill(const void* q, const void* k, const void* v, int dtype, int
  *             rounded to bf16 (round to nearest even) before their products.
  *   Each element of dq, dk, dv lies within (e^d - 1 + r + g) * A of the
  *   exact gradient, where A is the same sum taken over absolute values, d
- *   the forward's log-sum-exp error (2.5e-3 bf16, 1e-5 fp32), r = 2^-9 for
- *   bf16 (0 for fp32) and g = m u / (1 - m u) with u = 2^-24 and m = D + G S
+ *   the forward's log-sum-exp error (4e-3 bf16, 1e-5 fp32), r = 2^-8 for
+ *   bf16 (its unit roundoff; 0 for fp32) and g = m u / (1 - m u) with u = 2^-24 and m = D + G S
  *   (G = Hq / Hkv): the bound the parity tests apply.
  * dk and dv of initial and separator keys are summed with fp32 atomics, so
  * their summation order varies between runs.

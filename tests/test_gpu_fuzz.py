@@ -28,7 +28,7 @@ from .gpu_util import check_close, from_dev, guarded_cache, guarded_empty, slots
 
 pytestmark = pytest.mark.gpu
 SEP = list(range(8))
-LSE_TOL = {"bf16": 2.5e-3, "f32": 1e-5}
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}   # the forward's: test_gpu_prefill.py
 
 
 def _prefill_once(ids, q, k, v, a, n, dtype, tq, tk):

@@ -27,11 +27,12 @@ pytestmark = pytest.mark.gpu
 
 
 # Log-sum-exp tolerance. The bf16 path rounds P to bf16 (round to nearest
-# even, relative error <= 2^-9 per term) before both the PV product and the
-# row sum l, so |l_gpu / l - 1| <= 2^-9 and |lse_gpu - lse| <= -ln(1 - 2^-9)
-# ~ 1.96e-3; fp32 scores, fp32 accumulation and the hardware exp2 add a few
-# ulp. The fp32 path keeps P in fp32.
-LSE_TOL = {"bf16": 2.5e-3, "f32": 1e-5}
+# even; 8 significant bits, so relative error <= 2^-8 per term, as u = 2^-24
+# for fp32's 24) before both the PV product and the row sum l, so
+# |l_gpu / l - 1| <= 2^-8 and |lse_gpu - lse| <= -ln(1 - 2^-8) ~ 3.91e-3;
+# fp32 scores, fp32 accumulation and the hardware exp2 add a few ulp. The
+# fp32 path keeps P in fp32.
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}
 
 
 def run_gpu(ids, q, k, v, sep_ids, a, n, dtype, scale):

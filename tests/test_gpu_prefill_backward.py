@@ -11,15 +11,15 @@ where B_g is the same sum taken over absolute values:
     B_dq  = scale aS |K|,  B_dk = scale sum_h aS^T |Q|,  B_dv = sum_h P^T |dO|.
 eps bounds the relative error of the recomputed weights P = exp(s - lse)
 that the forward's lse carries: |lse_gpu - lse| <= delta_lse gives
-|P_gpu / P - 1| <= exp(delta_lse) - 1 (delta_lse = 2.5e-3 for bf16, whose
+|P_gpu / P - 1| <= exp(delta_lse) - 1 (delta_lse = 4e-3 for bf16, whose
 forward sums bf16-rounded weights, and 1e-5 for fp32; both are the
 forward's own log-sum-exp tolerances), plus a few ulp of the hardware exp2.
 gamma = n u / (1 - n u), u = 2^-24, is the worst-case error of an fp32 sum
 of n terms, with n = D + G S the longest chain of fp32 operations (dot
 products of length D, then sums over at most G S query rows). With bf16
 inputs the products run on the bf16 MFMA: P (for dV) and dS (for dQ, dK)
-are rounded to bf16 first, which moves each term by at most 2^-9 of itself
-(round to nearest even, 8 significant bits), so eps gains 2^-9 there; Q, K,
+are rounded to bf16 first, which moves each term by at most 2^-8 of itself
+(round to nearest even, 8 significant bits), so eps gains 2^-8 there; Q, K,
 V and dO enter exactly. A wrong index, a dropped term or a mask error
 shifts an element by a multiple of a single weight's contribution, far
 above (eps + gamma) B at these sizes.
@@ -40,8 +40,8 @@ from .gpu_util import from_dev, guarded_empty, to_dev
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = {"bf16": 2.5e-3, "f32": 1e-5}
-OPERAND_ROUNDING = {"bf16": 2.0 ** -9, "f32": 0.0}   # P and dS rounded for the bf16 MFMA
+LSE_TOL = {"bf16": 4e-3, "f32": 1e-5}   # the forward's: test_gpu_prefill.py
+OPERAND_ROUNDING = {"bf16": 2.0 ** -8, "f32": 0.0}   # P and dS rounded to bf16 (8 significant bits)
 U32 = 2.0 ** -24
 
 

@@ -29,7 +29,7 @@ from .gpu_util import check_close, from_dev, guarded_empty, to_dev
 from .test_gpu_cache_decode import SEP_IDS, Stream, sim_for
 
 pytestmark = pytest.mark.gpu
-LSE_TOL = 2.5e-3
+LSE_TOL = 4e-3   # the forward's bf16 bound: test_gpu_prefill.py
 
 
 def chunk_inputs(st, t0, t1):
