@@ -141,14 +141,31 @@ def write_traffic(name, dirs, alg_bytes):
     hash. alg_bytes: the algorithmic bytes of one launch (one step)."""
     import csv
     import glob
+    import sqlite3
+
+    def rows(d):
+        """(kernel name, counter name, value per dispatch) from a rocprofv3
+        --pmc output folder: its SQLite database (pmc_events), else its
+        counter_collection CSV."""
+        dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+        if dbs:
+            for f in dbs:
+                con = sqlite3.connect(f)
+                q = ("select dispatch_id, name, counter_name, sum(counter_value) from pmc_events "
+                     "group by dispatch_id, counter_name")
+                for _, kname, cname, val in con.execute(q):
+                    yield kname, cname, float(val)
+            return
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                yield r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
 
     def mean(d, kernels, counter):
         per = {}
-        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
-            for r in csv.DictReader(open(f)):
-                for kname in kernels:
-                    if kname in r["Kernel_Name"] and r["Counter_Name"] == counter:
-                        per.setdefault(kname, []).append(float(r["Counter_Value"]))
+        for kname_full, cname, val in rows(d):
+            for kname in kernels:
+                if kname in kname_full and cname == counter:
+                    per.setdefault(kname, []).append(val)
         if set(per) != set(kernels):
             raise SystemExit(f"no {counter} rows for {set(kernels) - set(per)} under {d}")
         return sum(sum(v) / len(v) for v in per.values()), [len(v) for v in per.values()]
