@@ -140,6 +140,11 @@ __device__ __forceinline__ void bw_dma4(const void* base, uint32_t off, uint32_t
 
 // Position of a query tile in a key block's sequence: query tile q of head h
 // of the group, advanced one tile at a time (no divisions in the loop).
+// Loop state that is uniform by construction, pinned to scalar registers:
+// left to itself the compiler may keep it in VGPRs, and then every address
+// derived from it costs VALU work and a readfirstlane per DMA.
+__device__ __forceinline__ int bw_sgpr(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 struct TileSeq {
   int h, q;
   __device__ void next(int ntq) {
@@ -147,6 +152,8 @@ struct TileSeq {
       q = 0;
       ++h;
     }
+    h = bw_sgpr(h);
+    q = bw_sgpr(q);
   }
 };
 
@@ -366,7 +373,9 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
 // (waves 4-7) computes dP = dO V^T and, one query tile later, dS = P (dP -
 // delta) from that P, and accumulates dK^T += Q^T dS over the whole of d. So
 // every product and every element of P and dS is computed once per (key,
-// query row), and each wave holds one of K^T, V^T in registers.
+// query row), and each wave holds one of K^T, V^T in registers (the dS wave
+// V^T negated: its product, started from delta, gives delta - dP at no VALU
+// cost).
 template <int D>
 struct KVGeo {
   static constexpr int KS = D / 16;               // 16-wide k-steps over d
@@ -390,11 +399,12 @@ struct LaneOff {
   }
 };
 
-// The KS products over d of tile rows lane % 32 with the register fragments
-// b (one key per lane): all A operands are read before the first MFMA, so
-// that the LDS latency is paid once per tile.
+// acc plus the KS products over d of tile rows lane % 32 with the register
+// fragments b (one key per lane): all A operands are read before the first
+// MFMA, so that the LDS latency is paid once per tile.
 template <int D>
-__device__ __forceinline__ f32x16 tile_scores(const char* tile, const LaneOff<D>& lo, const bf16x8 (&b)[D / 16]) {
+__device__ __forceinline__ f32x16 tile_scores(const char* tile, const LaneOff<D>& lo, const bf16x8 (&b)[D / 16],
+                                              f32x16 acc = f32x16{}) {
   constexpr int KS = D / 16;
   bf16x8 a[KS];
   const uint32_t base = tile_base(tile);
@@ -404,7 +414,6 @@ __device__ __forceinline__ f32x16 tile_scores(const char* tile, const LaneOff<D>
                                            lds_at(base + lo.row[ks])));
   }
   __builtin_amdgcn_sched_barrier(0);
-  f32x16 acc = {};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[ks], b[ks], acc);
   return acc;
@@ -471,21 +480,34 @@ __device__ __forceinline__ void p_tile(const char* Qs, const char* Os, const flo
   tile_accumulate<D>(Os, lo, w, dv);
 }
 
-// dS wave, the tile whose P the P wave left at pr and whose dP is dp.
+// dS wave, the tile whose P the P wave left at pr; dm = delta - dP of its
+// rows (the dP product run from an accumulator that starts at delta, with
+// V negated), so dS = P (dP - delta) = -(P dm).
 template <int D>
-__device__ __forceinline__ void ds_tile(const char* Qs, const float* dlt, const f32x4* pr, const f32x16& dp,
-                                        const LaneOff<D>& lo, int lane, f32x16 (&dk)[D / 32]) {
-  const int hsel = lane / 32;
+__device__ __forceinline__ void ds_tile(const char* Qs, const f32x4* pr, const f32x16& dm, const LaneOff<D>& lo,
+                                        f32x16 (&dk)[D / 32]) {
   float ds[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const f32x4 pq = pr[i * kWave];
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + 8 * i + 4 * hsel);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ds[4 * i + e] = pq[e] * (dp[4 * i + e] - d4[e]);
+    for (int e = 0; e < 4; ++e) ds[4 * i + e] = -(pq[e] * dm[4 * i + e]);
   }
   const bf16x8 w[2] = {pack8(ds), pack8(ds + 8)};
   tile_accumulate<D>(Qs, lo, w, dk);
+}
+
+// delta of the tile's rows in the accumulator layout (element r: row
+// 8 (r / 4) + 4 (lane / 32) + r % 4)
+__device__ __forceinline__ f32x16 rows_acc(const float* v, int lane) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(v + 8 * i + 4 * (lane / 32));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * i + e] = x[e];
+  }
+  return r;
 }
 
 // Bits [lo, hi) of a 32-row tile, the bounds clamped to the tile.
@@ -597,8 +619,8 @@ __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R
     const bool real = left > 0;
     R.issue(P, real, real ? hrow_of(is.h) : hrow0, qs0 + is.q * QB, ist);
     if (real) is.next(ntq);
-    --left;
-    ist = ist + 1 == RG::NST ? 0 : ist + 1;
+    left = bw_sgpr(left - 1);
+    ist = bw_sgpr(ist + 1 == RG::NST ? 0 : ist + 1);
   };
 #pragma unroll
   for (int t = 0; t < RG::AHEAD; ++t) issue_next();
@@ -610,7 +632,7 @@ __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R
     __builtin_amdgcn_s_barrier();
     bw_fence();
     compute(t, st);
-    st = st + 1 == RG::NST ? 0 : st + 1;
+    st = bw_sgpr(st + 1 == RG::NST ? 0 : st + 1);
   }
   bw_fence();
   __builtin_amdgcn_s_waitcnt(0);                  // no DMA still landing (dummies included)
@@ -648,18 +670,22 @@ __device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char*
                 p_slot(pbuf, t, kg, lane), acc);
     });
   } else {
-    f32x16 dp = {};
+    bf16x8 nv[D / 16];                            // -V^T: a sign flip per bf16
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      nv[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, kv[ks]) ^ 0x80008000u);
+    f32x16 dm = {};                               // delta - dP of tile t - 1
     bool prev = false;                            // tile t - 1 seen by the group
     stream_query_tiles(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
       if (prev) {
         const int sp = st == 0 ? Ring::NST - 1 : st - 1;
-        ds_tile<D>(R.q(sp), R.d(sp), p_slot(pbuf, t - 1, kg, lane), dp, lo, lane, acc);
+        ds_tile<D>(R.q(sp), p_slot(pbuf, t - 1, kg, lane), dm, lo, acc);
       }
       prev = false;
       if (t < nt) {
         prev = ballot(vis(qs0 + cs.q * QB) != 0u) != 0;
         cs.next(ntq);
-        if (prev) dp = tile_scores<D>(R.o(st), lo, kv);
+        if (prev) dm = tile_scores<D>(R.o(st), lo, nv, rows_acc(R.d(st), lane));
       }
     });
   }
