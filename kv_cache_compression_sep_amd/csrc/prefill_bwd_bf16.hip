@@ -170,6 +170,7 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
   constexpr int PERW = NINS / BW;
   constexpr int OPS = 2 * PERW;
   static_assert(NINS % BW == 0, "whole DMA ops per wave");
+  static_assert(kWave % CPR == 0, "a wave's 16-byte slots span whole rows");
   __shared__ __attribute__((aligned(1024))) char kring[2 * TILEB];
   __shared__ __attribute__((aligned(1024))) char vring[2 * TILEB];
   __shared__ int32_t idxbuf[3][KTQ];
@@ -235,43 +236,51 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(P.k) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(P.v) + static_cast<int64_t>(b * P.Hkv + g) * S * D;
 
-  auto index_store = [&](int t) {                // wave 0: key rows and separator bits of tile t
-    bool band;
-    const int key = tile_key<KTQ>(ti, sp, S, t, lane, &band);
+  // wave 0: the key rows and separator flags of tile t (the entries of
+  // tile_key), in two steps: index_load issues one load per lane from a
+  // clamped, always valid address (no per-lane branch, so nothing waits for
+  // it), index_write selects from what it returned and fills the index ring
+  auto index_load = [&](int t) -> int {
+    if (t < ti.ntg) return sp[min(max(ti.rank_a + t * KTQ + lane - ti.n_init, 0), S - 1)];
+    return fl[min(ti.band_lo + (t - ti.ntg) * KTQ + lane, S - 1)];
+  };
+  auto index_write = [&](int t, int raw) {
+    int key;
     bool f = false;
-    if (band) {
+    if (t < ti.ntg) {                             // gathered: initial keys, then separators
+      const int gu = t * KTQ + lane;
+      key = gu >= ti.n_glob ? 0 : (gu < ti.n_init ? gu : raw);
+    } else {                                      // band: consecutive keys and their flags
       const int j = ti.band_lo + (t - ti.ntg) * KTQ + lane;
-      f = (j < S) && (fl[j] != 0);
+      key = min(j, S - 1);
+      f = j < S && raw != 0;
     }
     const uint64_t bits = ballot(f);
     idxbuf[t % 3][lane] = key;
     if (lane == 0) sepbits[t % 3] = bits;
   };
-  // this lane's row and byte column in each of its DMA ops (the LDS chunk
-  // swizzle goes into the global offsets)
-  int drow[PERW];
-  uint32_t dcol[PERW];
-#pragma unroll
-  for (int i = 0; i < PERW; ++i) {
-    const int sl = (wave * PERW + i) * kWave + lane;
-    drow[i] = sl / CPR;
-    dcol[i] = 16 * ((sl % CPR) ^ G::swz(drow[i]));
-  }
   const uint32_t k_lds = tile_base(kring);
   const uint32_t v_lds = tile_base(vring);
   auto issue = [&](int t) {                       // the DMA ops of tile t into stage t % 2
     const uint32_t st = (t & 1) * TILEB;
+    // this lane's row and byte column in each op (the LDS chunk swizzle goes
+    // into the global offsets), recomputed from an opaque copy of the lane
+    // index each tile rather than held in registers through the loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
-      const uint32_t off = static_cast<uint32_t>(idxbuf[t % 3][drow[i]]) * (D * 2) + dcol[i];
+      const int r = (wave * PERW + i) * (kWave / CPR) + l / CPR;
+      const uint32_t col = 16 * ((l % CPR) ^ G::swz(r));
+      const uint32_t off = static_cast<uint32_t>(idxbuf[t % 3][r]) * (D * 2) + col;
       const uint32_t dst = st + (wave * PERW + i) * 1024;
       bw_dma16(kb, off, k_lds + dst);
       bw_dma16(vb, off, v_lds + dst);
     }
   };
   if (wave == 0) {
-    if (ti.ntiles > 0) index_store(0);
-    if (ti.ntiles > 1) index_store(1);
+    if (ti.ntiles > 0) index_write(0, index_load(0));
+    if (ti.ntiles > 1) index_write(1, index_load(1));
   }
   __syncthreads();
   if (ti.ntiles > 0) issue(0);
@@ -282,45 +291,41 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dacc[db] = f32x16{};
 
-  for (int t = 0; t < ti.ntiles; ++t) {
-    bw_fence();
-    __builtin_amdgcn_s_barrier();                 // tile t - 1 consumed: its stage takes tile t + 1
-    bw_fence();
-    // index_store reads global memory and waits for it: before the DMA of
-    // tile t + 1, so that the wait does not cover that DMA
-    if (wave == 0 && t + 2 < ti.ntiles) index_store(t + 2);
-    if (t + 1 < ti.ntiles) {
-      issue(t + 1);
-      bw_wait_vm<OPS>();                          // this wave's parts of tile t landed
-    } else {
-      bw_wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();                 // tile t and index t + 2 published
-    bw_fence();
+  // the products of tile t (band tiles no row of the wave sees are skipped)
+  auto tile_products = [&](int t) {
     const char* kst = kring + (t & 1) * TILEB;
     const char* vst = vring + (t & 1) * TILEB;
-
     const bool band = t >= ti.ntg;
     const int jmin = band ? ti.band_lo + (t - ti.ntg) * KTQ : 0;
     const int nvalid = band ? KTQ : min(KTQ, ti.n_glob - t * KTQ);
-    if (band && (jmin > qmax || qw0 >= S)) continue;
+    if (band && (jmin > qmax || qw0 >= S)) return;
     const bool need_mask = band ? !(jmin + KTQ - 1 <= qw0 && jmin >= qmax - P.n + 1) : nvalid < KTQ;
     const uint64_t vis =
         need_mask ? (vis_word(band, qi, jmin, P.n, P.a, sepbits[t % 3], nvalid) >> (4 * hsel)) : ~0ull;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      // the K rows' operands, then the V rows' (in flight during the S chain)
-      bf16x8 ak[KS], av[KS];
+      // the K rows' operands; each V row operand is read into the registers
+      // of the K operand that the S chain has just consumed, so that the V
+      // reads are in flight during the S chain without a second set of
+      // operand registers
+      bf16x8 a[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ak[ks] = row_operand<D>(kst, 32 * mb + lane % 32, ks, lane);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) av[ks] = row_operand<D>(vst, 32 * mb + lane % 32, ks, lane);
+      for (int ks = 0; ks < KS; ++ks) a[ks] = row_operand<D>(kst, 32 * mb + lane % 32, ks, lane);
       __builtin_amdgcn_sched_barrier(0);
       f32x16 sc = {}, dp = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sc = mfma32x32x16(ak[ks], qf[ks], sc);
+      for (int ks = 0; ks < KS; ++ks) {
+        sc = mfma32x32x16(a[ks], qf[ks], sc);
+        a[ks] = row_operand<D>(vst, 32 * mb + lane % 32, ks, lane);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(av[ks], of[ks], dp);
+      for (int ks = 0; ks < KS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32x32x16(a[ks], of[ks], dp);
       __builtin_amdgcn_sched_barrier(0);
       float ds[16];
 #pragma unroll
@@ -353,6 +358,30 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  for (int t = 0; t < ti.ntiles; ++t) {
+    bw_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): wave 0's index writes are complete
+    __builtin_amdgcn_s_barrier();                 // tile t - 1 consumed: its stage takes tile t + 1
+    bw_fence();
+    if (t + 1 < ti.ntiles) {
+      issue(t + 1);
+      bw_wait_vm<OPS>();                          // this wave's parts of tile t landed
+    } else {
+      bw_wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();                 // tile t published
+    bw_fence();
+    // wave 0 reads the indices of tile t + 2 now and writes them after this
+    // tile's products, so that their global-memory latency is hidden behind
+    // the MFMAs (the write waits for every load of the wave, the DMA of tile
+    // t + 1 included, which has long landed by then)
+    const bool nidx = wave == 0 && t + 2 < ti.ntiles;
+    int nx;                                       // (read only where nidx holds: no default that
+    if (nidx) nx = index_load(t + 2);             // would overwrite a load in flight)
+    tile_products(t);
+    if (nidx) index_write(t + 2, nx);
   }
   if (qi < S) {
     float* dst = P.dq + (hrow + qi) * D;
