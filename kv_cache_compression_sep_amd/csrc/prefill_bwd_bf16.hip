@@ -548,10 +548,11 @@ __device__ __forceinline__ uint32_t row_range(int lo, int hi) {
 
 // Query tiles of 32 rows (Q, dO, lse, delta) stream into a ring of NST LDS
 // stages by LDS-DMA (global_load_lds: no register results), AHEAD tiles
-// ahead of the one being computed. Every wave issues exactly OPS DMA ops per
-// tile (dummies into its junk row past the last tile, or for the lse/delta
-// rows that only wave 0 loads), so one exact vmcnt count per tile says that
-// its own parts of tile t landed; a plain barrier then publishes the tile.
+// ahead of the one being computed. The NW issuing waves (waves 0 .. NW - 1)
+// each issue exactly OPS DMA ops per tile (dummies into their junk row past
+// the last tile, or for the lse/delta rows that only wave 0 loads), so one
+// exact vmcnt count per tile says that a wave's own parts of tile t landed;
+// a plain barrier then publishes the tile to every wave.
 // Rows are placed with the swizzle of BGeo through the global offsets.
 // The LDS byte address of p, computed once (wave-uniform).
 __device__ __forceinline__ uint32_t lds_u32(const char* p) { return tile_base(p); }
@@ -633,8 +634,9 @@ __device__ __forceinline__ f32x4* p_slot(char* pbuf, int t, int kg, int lane) {
 // - 1) are complete (the wait includes lgkmcnt(0)). So compute(t) may read
 // what compute(t - 1) wrote, and the DMA of tile t + AHEAD, issued after the
 // barrier of step t - 1, only overwrites the stage of tile t - 3, which no
-// wave reads after compute(t - 2).
-template <class RG, class HRow, class Compute>
+// wave reads after compute(t - 2). ISSUE: this wave is one of the ring's
+// issuing waves (the others only wait at the barriers).
+template <bool ISSUE, class RG, class HRow, class Compute>
 __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R, int nt, TileSeq s0, int ntq,
                                                    int qs0, HRow hrow_of, Compute compute) {
   bw_fence();
@@ -651,13 +653,19 @@ __device__ __forceinline__ void stream_query_tiles(const BwdArgs& P, const RG& R
     left = bw_sgpr(left - 1);
     ist = bw_sgpr(ist + 1 == RG::NST ? 0 : ist + 1);
   };
+  if (ISSUE) {
 #pragma unroll
-  for (int t = 0; t < RG::AHEAD; ++t) issue_next();
+    for (int t = 0; t < RG::AHEAD; ++t) issue_next();
+  }
   int st = 0;
   for (int t = 0; t <= nt; ++t) {
     bw_fence();
-    issue_next();
-    bw_wait_vm<RG::AHEAD * RG::OPS>();            // this wave's parts of tile t landed
+    if (ISSUE) {
+      issue_next();
+      bw_wait_vm<RG::AHEAD * RG::OPS>();          // this wave's parts of tile t landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): its LDS accesses of compute(t - 1) done
+    }
     __builtin_amdgcn_s_barrier();
     bw_fence();
     compute(t, st);
@@ -682,7 +690,8 @@ __device__ __forceinline__ void load_key_bf16(const uint16_t* base, int j, int l
 // visibility mask of the tile at row qt0 for this lane's key; a tile that
 // no lane of the group sees is skipped by both waves alike. The two roles
 // run separate loops (with the same barriers), so that each is
-// register-allocated alone.
+// register-allocated alone. The P waves issue the query-tile DMA: the dS
+// waves' steps are the longer ones, so they only wait at the barriers.
 template <int D, class Ring, class HRow, class Vis>
 __device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char* pbuf, int nt, TileSeq s0, int ntq,
                                           int qs0, HRow hrow_of, bool pwave, int kg, int lane,
@@ -690,7 +699,7 @@ __device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char*
                                           f32x16 (&acc)[D / 32]) {
   TileSeq cs = s0;                                // tile t
   if (pwave) {
-    stream_query_tiles(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
+    stream_query_tiles<true>(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
       if (t == nt) return;
       const uint32_t vm = vis(qs0 + cs.q * QB);
       cs.next(ntq);
@@ -705,7 +714,7 @@ __device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char*
       nv[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, kv[ks]) ^ 0x80008000u);
     f32x16 dm = {};                               // delta - dP of tile t - 1
     bool prev = false;                            // tile t - 1 seen by the group
-    stream_query_tiles(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
+    stream_query_tiles<false>(P, R, nt, s0, ntq, qs0, hrow_of, [&](int t, int st) {
       if (prev) {
         const int sp = st == 0 ? Ring::NST - 1 : st - 1;
         ds_tile<D>(R.q(sp), p_slot(pbuf, t - 1, kg, lane), dm, lo, acc);
@@ -723,7 +732,7 @@ __device__ __forceinline__ void pair_loop(const BwdArgs& P, const Ring& R, char*
 template <int D>
 __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArgs P, int n_kt) {
   using KG = KVGeo<D>;
-  using Ring = QRing<D, KG::NWAVE>;
+  using Ring = QRing<D, 4>;                 // the P waves issue the query-tile DMA
   __shared__ __attribute__((aligned(1024))) char ringmem[Ring::BYTES];
   __shared__ __attribute__((aligned(1024))) char junkmem[KG::NWAVE * 1024];
   __shared__ __attribute__((aligned(16))) char pbuf[kPBytes];
@@ -790,7 +799,7 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_band_bf16_kernel(BwdArg
 template <int D>
 __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArgs P, int nslots) {
   using KG = KVGeo<D>;
-  using Ring = QRing<D, KG::NWAVE>;
+  using Ring = QRing<D, 4>;                 // the P waves issue the query-tile DMA
   constexpr int NTH = KG::NTH;
   constexpr int RED = KG::NWAVE * 32 * 64 * 4;    // one 64-column pass of every wave's partial
   constexpr int SM = Ring::BYTES + kPBytes;
