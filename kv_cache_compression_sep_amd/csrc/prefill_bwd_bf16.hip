@@ -160,7 +160,8 @@ struct TileSeq {
 // ---------------------------------------------------------------- dQ (bf16)
 // The forward's work items; the key tiles of 64 (gathered rows: initial and
 // separator keys, then the band) land in a two-stage LDS ring by LDS-DMA one
-// tile ahead, their indices two tiles ahead.
+// tile ahead (issued while the tile before is computed), their indices two
+// tiles ahead.
 template <int D>
 __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
   using G = BGeo<D>;
@@ -168,7 +169,6 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
   constexpr int TILEB = KTQ * D * 2;
   constexpr int NINS = TILEB / 1024;              // 1 KB DMA ops per tensor and tile
   constexpr int PERW = NINS / BW;
-  constexpr int OPS = 2 * PERW;
   static_assert(NINS % BW == 0, "whole DMA ops per wave");
   static_assert(kWave % CPR == 0, "a wave's 16-byte slots span whole rows");
   __shared__ __attribute__((aligned(1024))) char kring[2 * TILEB];
@@ -200,34 +200,6 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
   const int64_t hrow = static_cast<int64_t>(b * P.Hq + h) * S;
   const int qi = qw0 + lane % 32;
   const int qc = min(qi, S - 1);
-
-  // Q^T and dO^T fragments of this lane's query: d = 16 ks + 8 (lane / 32) + i
-  bf16x8 qf[KS], of[KS];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(P.q) + (hrow + qc) * D + 8 * hsel;
-    const uint16_t* op = reinterpret_cast<const uint16_t*>(P.dout) + (hrow + qc) * D + 8 * hsel;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
-      of[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
-    }
-  }
-  const float lse2 = P.lse[hrow + qc] * kLog2e;
-  // delta of this lane's query row, rowsum(dO o out) in fp32 (the two
-  // halves of d sit in lanes l and l + 32); stored for the dK/dV kernels,
-  // which run after this one
-  float dlt = 0.0f;
-  {
-    const uint16_t* op = reinterpret_cast<const uint16_t*>(P.out) + (hrow + qc) * D + 8 * hsel;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dlt += static_cast<float>(of[ks][e]) * static_cast<float>(ov[e]);
-    }
-    dlt += __shfl_xor(dlt, 32);
-    if (hsel == 0 && qi < S) P.delta[hrow + qi] = dlt;
-  }
 
   const int32_t* rk = P.rank + static_cast<int64_t>(b) * (S + 1);
   const int32_t* sp = P.sep_pos + static_cast<int64_t>(b) * S;
@@ -268,22 +240,61 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
     // index each tile rather than held in registers through the loop
     int l = lane;
     asm volatile("" : "+v"(l));
+    // the index reads first: a DMA (an opaque memory access) would keep a
+    // later LDS read behind it, one round trip per op
+    int key[PERW];
+#pragma unroll
+    for (int i = 0; i < PERW; ++i) key[i] = idxbuf[t % 3][(wave * PERW + i) * (kWave / CPR) + l / CPR];
 #pragma unroll
     for (int i = 0; i < PERW; ++i) {
       const int r = (wave * PERW + i) * (kWave / CPR) + l / CPR;
       const uint32_t col = 16 * ((l % CPR) ^ G::swz(r));
-      const uint32_t off = static_cast<uint32_t>(idxbuf[t % 3][r]) * (D * 2) + col;
+      const uint32_t off = static_cast<uint32_t>(key[i]) * (D * 2) + col;
       const uint32_t dst = st + (wave * PERW + i) * 1024;
       bw_dma16(kb, off, k_lds + dst);
       bw_dma16(vb, off, v_lds + dst);
     }
   };
+  // Wave 0's index loads of tiles 0 and 1 go out before the row loads of
+  // Q, dO and out, so that its wait for them (which the compiler counts
+  // exactly) does not include those, and tile 0's DMA is issued while the
+  // rows are still landing.
+  int ix0, ix1;                                   // (read only where loaded)
   if (wave == 0) {
-    if (ti.ntiles > 0) index_write(0, index_load(0));
-    if (ti.ntiles > 1) index_write(1, index_load(1));
+    if (ti.ntiles > 0) ix0 = index_load(0);
+    if (ti.ntiles > 1) ix1 = index_load(1);
+  }
+  // Q^T and dO^T fragments of this lane's query: d = 16 ks + 8 (lane / 32) + i,
+  // and its out row for delta
+  bf16x8 qf[KS], of[KS], ov[KS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(P.q) + (hrow + qc) * D + 8 * hsel;
+    const uint16_t* dp = reinterpret_cast<const uint16_t*>(P.dout) + (hrow + qc) * D + 8 * hsel;
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(P.out) + (hrow + qc) * D + 8 * hsel;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+      of[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dp + 16 * ks));
+      ov[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
+    }
+  }
+  const float lse2 = P.lse[hrow + qc] * kLog2e;
+  if (wave == 0) {
+    if (ti.ntiles > 0) index_write(0, ix0);
+    if (ti.ntiles > 1) index_write(1, ix1);
   }
   __syncthreads();
   if (ti.ntiles > 0) issue(0);
+  // delta of this lane's query row, rowsum(dO o out) in fp32 (the two
+  // halves of d sit in lanes l and l + 32); stored for the dK/dV kernels,
+  // which run after this one
+  float dlt = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dlt += static_cast<float>(of[ks][e]) * static_cast<float>(ov[ks][e]);
+  dlt += __shfl_xor(dlt, 32);
+  if (hsel == 0 && qi < S) P.delta[hrow + qi] = dlt;
 
   int toff[DB][2];
   tr_offsets<D>(lane, toff);
@@ -360,19 +371,17 @@ __global__ void __launch_bounds__(BT, 2) dq_bf16_kernel(BwdArgs P) {
     }
   };
 
+  // One barrier per tile. Before it each wave waits for all of its loads:
+  // its parts of tile t (issued during tile t - 1) and, on wave 0, the index
+  // loads (its index writes complete too: lgkmcnt(0)). Past it, tile t is
+  // published, and every wave is done with tile t - 1, whose stage then takes
+  // tile t + 1 and whose index slot the indices of tile t + 2.
   for (int t = 0; t < ti.ntiles; ++t) {
     bw_fence();
-    __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): wave 0's index writes are complete
-    __builtin_amdgcn_s_barrier();                 // tile t - 1 consumed: its stage takes tile t + 1
+    bw_wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
     bw_fence();
-    if (t + 1 < ti.ntiles) {
-      issue(t + 1);
-      bw_wait_vm<OPS>();                          // this wave's parts of tile t landed
-    } else {
-      bw_wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();                 // tile t published
-    bw_fence();
+    if (t + 1 < ti.ntiles) issue(t + 1);
     // wave 0 reads the indices of tile t + 2 now and writes them after this
     // tile's products, so that their global-memory latency is hidden behind
     // the MFMAs (the write waits for every load of the wave, the DMA of tile
