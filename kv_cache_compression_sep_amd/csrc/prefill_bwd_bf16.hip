@@ -108,6 +108,16 @@ __device__ __forceinline__ lds_cptr lds_at(uint32_t a) { return (lds_cptr)static
 // Helpers of the LDS-DMA tile loads (global_load_lds: no register results).
 __device__ __forceinline__ void bw_fence() { asm volatile("" ::: "memory"); }
 
+// A workgroup barrier for LDS hand-offs only: it waits for this wave's LDS
+// accesses (lgkmcnt(0)) but not for its global stores and atomics, which
+// may complete in the background.
+__device__ __forceinline__ void lds_barrier() {
+  bw_fence();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  bw_fence();
+}
+
 template <int N>
 __device__ __forceinline__ void bw_wait_vm() {    // s_waitcnt vmcnt(N) lgkmcnt(0)
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -899,12 +909,12 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
     const int ntq = nqt - qs0 / QB;
     const int su = G * ntq;
     const int k1 = static_cast<int>(min(static_cast<int64_t>(su), k0 + rem));
-    __syncthreads();                              // kpos and the tiles of the previous key tile are consumed
+    lds_barrier();                                // kpos and the tiles of the previous key tile are consumed
     for (int e = tid; e < KB; e += NTH) {
       const int ee = KB * u + e;
       kpos[e] = ee < n_gl ? entry_pos(ee) : -1;
     }
-    __syncthreads();
+    lds_barrier();
     const int j = kpos[32 * kg + lane % 32];      // this lane's key, -1 past the list
     bf16x8 kv[KG::KS];
     load_key_bf16<D>(kvb, j < 0 ? 0 : j, lane, kv);
@@ -918,6 +928,9 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
     // Add the partials with fp32 atomics, key row by key row through LDS, so
     // that each atomic instruction covers 2 x 32 consecutive floats of two
     // rows (2 cache lines) instead of one float of 32 rows; 64 columns a pass.
+    // The barriers here order the LDS staging only: nothing waits for the
+    // atomics until the next key tile's query stream (which starts with a
+    // full wait) or the end of the kernel.
 #pragma unroll
     for (int h = 0; h < D / 64; ++h) {
 #pragma unroll
@@ -927,7 +940,7 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
           const int dl = 32 * db + 8 * (r / 4) + 4 * hsel + (r % 4);       // column within the pass
           red[(wave * 32 + lane % 32) * 64 + (dl ^ (lane % 32))] = acc[2 * h + db][r] * f;
         }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll 4
       for (int pass = 0; pass < 16; ++pass) {
         const int row = 2 * pass + lane / 32;
@@ -939,7 +952,7 @@ __global__ void __launch_bounds__(KVGeo<D>::NTH, 1) dkdv_glob_bf16_kernel(BwdArg
                       red[(wave * 32 + row) * 64 + ((32 * e + lane % 32) ^ row)]);
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     rem -= k1 - k0;
     k0 = 0;
