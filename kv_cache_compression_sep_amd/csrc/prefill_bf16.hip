@@ -331,10 +331,16 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     voff[db] = 16 * G::slot_v(R, dcol / 8) + 2 * (dcol % 8);
   }
 
-  // ---- top of iteration t: wait for K(t) and V(t - 1), issue the loads
-  //      of later tiles (none in the last, PV-only iteration)
-  auto advance = [&](int t) {
-    tile_barrier<G::OPS>(t);
+  // ---- top of iteration t: wait for K(t) and V(t - 1)
+  auto advance = [&](int t) { tile_barrier<G::OPS>(t); };
+  // ---- the loads of iteration t (none in the last, PV-only one): issued
+  //      inside the wave's VALU phase, which reads no LDS and leaves issue
+  //      slots free while its exponentials run. The early waves' VALU phase
+  //      falls in the second half of an iteration, the late waves' in the
+  //      first, so the two halves of the workgroup do not issue at once.
+  //      Every op of iteration t still precedes the barrier of t + 1, in the
+  //      order index slice, K(t + 3), V(t + 2): the wait counts hold.
+  auto issue_loads = [&](int t) {
     if (t < ti.ntiles) {
       issue_index(t + IAHEAD);
       int knext[PW];
@@ -422,7 +428,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   //      band tile whose keys all lie in the future of this wave's rows gets
   //      an all-zero visibility word, so its P is zero), then the online
   //      softmax into pk, m, l
-  auto valu_phase = [&](int t, f32x16 (&sh)[2], uint64_t sepbits) {
+  auto valu_phase = [&](int t, f32x16 (&sh)[2], uint64_t sepbits, int t_issue) {
     __builtin_amdgcn_sched_barrier(0);
     const bool band = t >= ti.ntg;
     const int jmin = band ? ti.band_lo + (t - ti.ntg) * KT : 0;
@@ -450,6 +456,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     m_run = m_new;
     resc = resc || grow;
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+    issue_loads(t_issue);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int o = 8 * (kc % 2);
@@ -479,13 +486,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     advance(0);
     mfma_phase(0, sh, flag<true>{}, flag<false>{});
     sepb = sep_bits(0);
-    valu_phase(0, sh, sepb);
+    valu_phase(0, sh, sepb, 0);
     for (int t = 1; t < ti.ntiles; ++t) {
       advance(t);
       rescale();
       mfma_phase(t, sh, flag<true>{}, flag<true>{});
       sepb = sep_bits(t);
-      valu_phase(t, sh, sepb);
+      valu_phase(t, sh, sepb, t);
     }
     advance(ti.ntiles);
     rescale();
@@ -494,15 +501,16 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     advance(0);
     mfma_phase(0, sh, flag<true>{}, flag<false>{});
     sepb = sep_bits(0);
+    issue_loads(0);                                    // (no VALU phase in iteration 0)
     for (int t = 1; t < ti.ntiles; ++t) {
       advance(t);
-      valu_phase(t - 1, sh, sepb);
+      valu_phase(t - 1, sh, sepb, t);
       rescale();
       mfma_phase(t, sh, flag<true>{}, flag<true>{});
       sepb = sep_bits(t);
     }
     advance(ti.ntiles);
-    valu_phase(ti.ntiles - 1, sh, sepb);
+    valu_phase(ti.ntiles - 1, sh, sepb, ti.ntiles);
     rescale();
     mfma_phase(ti.ntiles, sh, flag<false>{}, flag<true>{});
   }
