@@ -335,17 +335,22 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   auto advance = [&](int t) { tile_barrier<G::OPS>(t); };
   // ---- the loads of iteration t (none in the last, PV-only one): issued
   //      inside the wave's VALU phase, which reads no LDS and leaves issue
-  //      slots free while its exponentials run. The early waves' VALU phase
-  //      falls in the second half of an iteration, the late waves' in the
-  //      first, so the two halves of the workgroup do not issue at once.
-  //      Every op of iteration t still precedes the barrier of t + 1, in the
-  //      order index slice, K(t + 3), V(t + 2): the wait counts hold.
-  auto issue_loads = [&](int t) {
+  //      slots free while its exponentials run (the index slice and K(t + 3)
+  //      before them, V(t + 2) after). The early waves' VALU phase falls in
+  //      the second half of an iteration, the late waves' in the first, so
+  //      the two halves of the workgroup do not issue at once. Every op of
+  //      iteration t still precedes the barrier of t + 1, in the order index
+  //      slice, K(t + 3), V(t + 2): the wait counts hold.
+  int knext[PW];
+  auto issue_k = [&](int t) {
     if (t < ti.ntiles) {
       issue_index(t + IAHEAD);
-      int knext[PW];
       rows_from(t + KAHEAD, graw, knext);
       issue_rows(kb, kring_lds, t + KAHEAD, knext, flag<false>{});
+    }
+  };
+  auto issue_v = [&](int t) {
+    if (t < ti.ntiles) {
       issue_rows(vb, vring_lds, t + VAHEAD, vrows, flag<true>{});
 #pragma unroll
       for (int i = 0; i < PW; ++i) vrows[i] = knext[i];
@@ -456,7 +461,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     m_run = m_new;
     resc = resc || grow;
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    issue_loads(t_issue);
+    issue_k(t_issue);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int o = 8 * (kc % 2);
@@ -472,6 +477,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       pk[kc] = w;
     }
+    issue_v(t_issue);
   };
 
   // The two waves that share a SIMD (waves w and w + 4) alternate between an
@@ -501,7 +507,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     advance(0);
     mfma_phase(0, sh, flag<true>{}, flag<false>{});
     sepb = sep_bits(0);
-    issue_loads(0);                                    // (no VALU phase in iteration 0)
+    issue_k(0);                                        // (no VALU phase in iteration 0)
+    issue_v(0);
     for (int t = 1; t < ti.ntiles; ++t) {
       advance(t);
       valu_phase(t - 1, sh, sepb, t);
