@@ -59,6 +59,7 @@ constexpr int IAHEAD = 7;              // index slices loaded this many tiles ah
 constexpr int IDXR = 8;                // index ring depth (> IAHEAD)
 static_assert(IDXR > IAHEAD && IAHEAD >= KAHEAD + 4, "index ring too shallow");
 constexpr float kLazy = 8.0f;
+constexpr int kOpsEnd = 1 << 16;       // the end of a wave's op range [lo, hi): past its last op
 // V of tiles t - 1 .. t + VAHEAD and K of tiles t .. t + KAHEAD are live in
 // iteration t
 static_assert(KAHEAD < KSTAGES && VAHEAD + 2 <= VSTAGES, "ring too shallow for the pipeline");
@@ -258,10 +259,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     rows_from(t, g, rows);
   };
   // ---- LDS-DMA of the K (or V) rows of tile t into its ring stage
-  auto issue_rows = [&](const char* base, uint32_t stage0, int t, const int (&rows)[PW], auto is_v) {
+  auto issue_rows = [&](const char* base, uint32_t stage0, int t, const int (&rows)[PW], auto is_v, int lo = 0, int hi = kOpsEnd) {
     const uint32_t st = stage0 + (t % (decltype(is_v)::value ? VSTAGES : KSTAGES)) * TB;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
+      if (i < lo || i >= (hi < PW ? hi : PW)) continue;
       const int ins = wave * PW + i;                   // 1 KB block of the tile
       const int sl = ins * kWave + lane;               // 16-byte slot this lane fills
       const int r = sl / CPR;
@@ -335,26 +337,31 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
   auto advance = [&](int t) { tile_barrier<G::OPS>(t); };
   // ---- the loads of iteration t (none in the last, PV-only one): issued
   //      inside the wave's VALU phase, which reads no LDS and leaves issue
-  //      slots free while its exponentials run (the index slice and K(t + 3)
-  //      before them, V(t + 2) after). The early waves' VALU phase falls in
-  //      the second half of an iteration, the late waves' in the first, so
-  //      the two halves of the workgroup do not issue at once. Every op of
-  //      iteration t still precedes the barrier of t + 1, in the order index
-  //      slice, K(t + 3), V(t + 2): the wait counts hold.
+  //      slots free while its exponentials run; one op before the first
+  //      16-key chunk of exponentials and one after each of the next ones
+  //      (ops [lo, hi) of a tensor per call). The early waves' VALU phase
+  //      falls in the second half of an iteration, the late waves' in the
+  //      first, so the two halves of the workgroup do not issue at once. Every
+  //      op of iteration t still precedes the barrier of t + 1, in the order
+  //      index slice, K(t + 3), V(t + 2): the wait counts hold.
   int knext[PW];
-  auto issue_k = [&](int t) {
+  auto issue_k = [&](int t, int lo = 0, int hi = kOpsEnd) {
     if (t < ti.ntiles) {
-      issue_index(t + IAHEAD);
-      rows_from(t + KAHEAD, graw, knext);
-      issue_rows(kb, kring_lds, t + KAHEAD, knext, flag<false>{});
+      if (lo == 0) {
+        issue_index(t + IAHEAD);
+        rows_from(t + KAHEAD, graw, knext);
+      }
+      issue_rows(kb, kring_lds, t + KAHEAD, knext, flag<false>{}, lo, hi);
     }
   };
-  auto issue_v = [&](int t) {
+  auto issue_v = [&](int t, int lo = 0, int hi = kOpsEnd) {
     if (t < ti.ntiles) {
-      issue_rows(vb, vring_lds, t + VAHEAD, vrows, flag<true>{});
+      issue_rows(vb, vring_lds, t + VAHEAD, vrows, flag<true>{}, lo, hi);
+      if (hi >= PW) {
 #pragma unroll
-      for (int i = 0; i < PW; ++i) vrows[i] = knext[i];
-      read_gather(t + KAHEAD + 1, graw);               // used in the next iteration
+        for (int i = 0; i < PW; ++i) vrows[i] = knext[i];
+        read_gather(t + KAHEAD + 1, graw);               // used in the next iteration
+      }
     }
   };
   // ---- the running max moved in the previous softmax: O to the new scale
@@ -461,7 +468,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
     m_run = m_new;
     resc = resc || grow;
     const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-    issue_k(t_issue);
+    issue_k(t_issue, 0, PW > 1 ? 1 : PW);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int o = 8 * (kc % 2);
@@ -476,8 +483,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_bf16_kernel(PrefillArgs P) {
       // that consumes it
       asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
       pk[kc] = w;
+      if (PW > 1 && kc == 0) issue_k(t_issue, 1, PW);
+      if (PW > 1 && kc == 1) issue_v(t_issue, 0, 1);
+      if (kc == 2) issue_v(t_issue, PW > 1 ? 1 : 0, PW);
     }
-    issue_v(t_issue);
   };
 
   // The two waves that share a SIMD (waves w and w + 4) alternate between an
