@@ -8,7 +8,8 @@
 //
 // Staging: K and V tiles go straight from global memory into LDS with
 // 16-byte LDS-DMA loads (no registers), each into a ring of four stages.
-// K of tile t + 3 and V of tile t + 2 are issued in iteration t. Rows are
+// K of tile t + 3 and V of tile t + 2 are issued in iteration t, inside the
+// wave's VALU phase (below), spread over its exponentials. Rows are
 // stored row-major with the 16-byte chunk index XOR-swizzled by the row, one
 // swizzle for K (the QK reads take one chunk of 32 rows) and one for V (a
 // transposed read takes 64 bytes of 4 rows per half wave), so that both hit
