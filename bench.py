@@ -31,7 +31,8 @@ under "secondary":
   * prefill backward on the prefill workload (sep_attn_prefill_backward,
     bf16 MFMA with fp32 accumulation): useful TFLOP/s = 10 * D * visible
     pairs per query head (S = QK^T recomputed, dP = dO V^T, dQ, dK, dV) over
-    its launch time, against the bf16 peak.
+    the mean time of a call (K calls back to back between one event pair),
+    against the bf16 peak.
 
 Prints one JSON line. ``--gpus N`` with N > 1 exits: the path runs on one
 GPU only.
@@ -323,15 +324,9 @@ def bench_backward(args, torch, sa, res):
     for _ in range(args.warmup):
         call()
     st = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        ev[i][0].record(st)
-        call()
-        ev[i][1].record(st)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # K calls back to back between one event pair (the call's three launches
+    # run one after another on the stream; no events between calls)
+    ms = time_back_to_back(torch, st, call, args.steps)
     useful = 2.5 * res["useful"]
     tflops = useful / (ms * 1e-3) / 1e12
     # bf16 inputs run on the bf16 MFMA (fp32 accumulation): its peak applies
