@@ -873,14 +873,15 @@ __global__ void __launch_bounds__(kUpdThreads) decode_update_kernel(DecodeArgs A
   update_body<UPD_FUSED, DYN>(U);
 }
 
-// Split decode's second launch, grid (Hkv + 1, B): workgroup g < Hkv merges
-// the partials of kv head g of sequence b (blockIdx.y); workgroup Hkv then
-// runs the single-token update of sequence b. The first launch (the ranges)
-// has finished reading the cache, so the update may rewrite it.
+// Split decode's second launch, grid (Hkv + 1, B): workgroup 0 runs the
+// single-token update of sequence b (blockIdx.y), the longest chain of the
+// launch, so it is dispatched first; workgroup 1 + g merges the partials of
+// kv head g. The first launch (the ranges) has finished reading the cache,
+// so the update may rewrite it.
 template <int D, bool DYN>
 __global__ void __launch_bounds__(kUpdThreads) merge_update_kernel(DecodeArgs A, CacheArgs U) {
-  if (static_cast<int>(blockIdx.x) < U.Hkv) {
-    merge_body<D>(A, blockIdx.x, blockIdx.y, kUpdThreads);
+  if (blockIdx.x > 0) {
+    merge_body<D>(A, blockIdx.x - 1, blockIdx.y, kUpdThreads);
     return;
   }
   update_body<UPD_FUSED, DYN>(U);
