@@ -22,11 +22,12 @@ inline int cache_slots(const sep_cache& c) { return c.a + c.s + cache_ring(c); }
 // Decode geometry. Few (sequence, kv head) pairs: wider workgroups (8
 // waves), so that each pair's list is read by more waves at once; and, when
 // the cache carries a large enough work buffer, each list split over several
-// workgroups: ranges of whole 128-entry units (one 32-entry slice for each of
-// 4 waves), at most kMaxSplits ranges per list (longer lists take longer
+// workgroups: ranges of whole 32-entry slices, one wave per workgroup, so
+// that each CU takes in as little of the list as possible (16 KB of K and V
+// at D = 128); at most kMaxSplits ranges per list (longer lists take longer
 // ranges). A list holds at most slots + 1 entries.
 inline bool decode_uses_wide(const sep_cache& c) { return c.B * c.Hkv < 256; }
-constexpr int kSplitChunk = 128;
+constexpr int kSplitChunk = 32;
 constexpr int kMaxSplits = 32;
 inline void decode_split_shape(const sep_cache& c, int* ns, int* span) {
   const int nch = (cache_slots(c) + 1 + kSplitChunk - 1) / kSplitChunk;
