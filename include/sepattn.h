@@ -239,7 +239,7 @@ int sep_attn_prefill_backward(const void* q, const void* k, const void* v, const
  *          The ring's entries, oldest first, are the slots
  *          a + (sep_head - sep_count + i) mod s, i = 0 .. sep_count-1.
  *   work   device work buffer of work_bytes bytes (256-byte aligned), or
- *          NULL. With few (sequence, kv head) pairs (B * Hkv < 256) and
+ *          NULL. With few (sequence, kv head) pairs (B * Hkv <= 64) and
  *          work_bytes >= sep_decode_work_bytes(cache, Hq), the decode calls
  *          (sep_attn_decode, sep_attn_decode_rope, sep_decode_update) split
  *          each list over several workgroups and keep their partial results
@@ -269,7 +269,7 @@ typedef struct {
 /*
  * sep_decode_work_bytes - the work buffer (sep_cache.work) the decode calls
  * need to split their lists for Hq query heads: 0 when they never split
- * (B * Hkv >= 256) or the cache is invalid. Split decode [P2 §1.3, only the
+ * (B * Hkv > 64) or the cache is invalid. Split decode [P2 §1.3, only the
  * retained KV are read: more workgroups read each list at once].
  */
 size_t sep_decode_work_bytes(const sep_cache* cache, int Hq);

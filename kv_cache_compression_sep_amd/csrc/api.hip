@@ -202,7 +202,7 @@ int sep_attn_decode(const void* q, const void* k_new, const void* v_new, const s
 
 size_t sep_decode_work_bytes(const sep_cache* cache, int Hq) {
   if (check_cache(cache) != SEP_OK || Hq <= 0 || Hq % cache->Hkv != 0 || Hq / cache->Hkv > 16) return 0;
-  if (!sep::decode_uses_wide(*cache)) return 0;
+  if (!sep::decode_may_split(*cache)) return 0;
   return sep::decode_split_bytes(*cache, Hq);
 }
 

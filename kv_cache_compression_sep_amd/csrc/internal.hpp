@@ -25,8 +25,12 @@ inline int cache_slots(const sep_cache& c) { return c.a + c.s + cache_ring(c); }
 // workgroups: ranges of whole 32-entry slices, one wave per workgroup, so
 // that each CU takes in as little of the list as possible (16 KB of K and V
 // at D = 128); at most kMaxSplits ranges per list (longer lists take longer
-// ranges). A list holds at most slots + 1 entries.
+// ranges). A list holds at most slots + 1 entries. The split (two launches
+// and the partials' round trip) pays only while the lists are too few to
+// spread over the CUs whole: up to kSplitMaxPairs (sequence, kv head) pairs.
 inline bool decode_uses_wide(const sep_cache& c) { return c.B * c.Hkv < 256; }
+constexpr int kSplitMaxPairs = 64;
+inline bool decode_may_split(const sep_cache& c) { return c.B * c.Hkv <= kSplitMaxPairs; }
 constexpr int kSplitChunk = 32;
 constexpr int kMaxSplits = 32;
 inline void decode_split_shape(const sep_cache& c, int* ns, int* span) {
@@ -42,7 +46,7 @@ inline size_t decode_split_bytes(const sep_cache& c, int Hq) {
   return static_cast<size_t>(c.B) * Hq * ns * kSplitWaves * static_cast<size_t>(c.D + 4) * sizeof(float);
 }
 inline bool decode_uses_split(const sep_cache& c, int Hq) {
-  return decode_uses_wide(c) && c.work != nullptr && c.work_bytes >= decode_split_bytes(c, Hq);
+  return decode_may_split(c) && c.work != nullptr && c.work_bytes >= decode_split_bytes(c, Hq);
 }
 
 hipError_t launch_is_sep(const int32_t* ids, int64_t N, const int32_t* sep_ids, int n_sep,

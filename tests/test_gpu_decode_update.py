@@ -7,7 +7,8 @@ and state words) bit for bit as those calls do; state word 7, the arrival
 count of the fused launch, must read 0 between calls. The cache is also
 checked against the list-based simulation and the decode outputs against
 fp64 attention over the retained keys plus the current token (bf16
-tolerance), every few steps. Cases cover the fused launch (B * Hkv < 256)
+tolerance), every few steps. Cases cover the split lists (B * Hkv <= 64
+with a work buffer), the fused whole-list launch (B * Hkv < 256 otherwise)
 across cache policies, StreamingLLM mode, D = 64 / 128, GQA 1..8, with and
 without RoPE position shifting, compressions at many steps, and the
 two-launch fallback (B * Hkv >= 256).
@@ -39,6 +40,7 @@ CASES = [
     (1, 12, 3, 64, 0, 5, 3, 7, 0, 50, SEP_POLICY_NO_ACCUM, True),
     (2, 8, 1, 128, 1, 4, 6, 5, 10, 50, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM, False),
     (1, 4, 2, 128, 4, 0, 0, 12, 5, 40, 0, False),            # StreamingLLM mode
+    (12, 16, 8, 64, 4, 6, 5, 9, 30, 30, 0, False),           # B * Hkv = 96: whole lists even with a work buffer
     (40, 16, 8, 64, 4, 6, 5, 9, 30, 30, 0, False),           # B * Hkv = 320: the two launches
 ]
 
@@ -52,7 +54,7 @@ def test_fused_step_equals_two_calls_and_oracle(case, split):
     d_sep = to_dev(np.asarray(SEP_IDS, np.int32))
     fused = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy, split=split)
     plain = guarded_cache(B, Hkv, D, a, s, p, w, policy=policy, split=split)
-    assert (fused.work is not None) == (split and B * Hkv < 256)
+    assert (fused.work is not None) == (split and B * Hkv <= 64)
     sims = [sim_for((a, s, p, w), policy) for _ in range(B)]
     if T0 > 0:
         st.push_gpu(fused, 0, T0, d_sep)
