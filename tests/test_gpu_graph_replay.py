@@ -1,7 +1,9 @@
-"""Graph capture: the prefill step (sep_mask_compact, then sep_attn_prefill)
-and the prefill backward, each captured once as a HIP graph and replayed, on
-the 8192-token Llama-3 layer workload. Their entry points allocate nothing
-and issue no memset, so a caller (a serving loop) may capture them.
+"""Graph capture: the prefill step (sep_mask_compact, then sep_attn_prefill),
+the prefill backward, and the same prompt streamed into a cache in chunks
+(sep_cache_reset, then per chunk sep_attn_prefill_chunk and
+sep_cache_update), each captured once as a HIP graph and replayed, on the
+8192-token Llama-3 layer workload. Their entry points allocate nothing and
+issue no memset, so a caller (a serving loop) may capture them.
 
 Every replay writes into outputs that eager work overwrote first, and must
 equal the eager launches: bit for bit, except dk and dv, whose initial and
@@ -17,9 +19,10 @@ import pytest
 import torch
 
 from inputs import configs, gen
-from kv_cache_compression_sep_amd import sep_attn_prefill, sep_attn_prefill_backward, sep_mask_compact
+from kv_cache_compression_sep_amd import (chunk_workspace_bytes, sep_attn_prefill, sep_attn_prefill_backward,
+                                          sep_attn_prefill_chunk, sep_cache_update, sep_mask_compact)
 
-from .gpu_util import guarded_empty, to_dev
+from .gpu_util import guarded_cache, guarded_empty, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +126,58 @@ def test_prefill_backward_graph_replays_match_eager(layer):
     refs = [o.clone() for o in outs]
     g = capture(call)
     replay_and_compare(g, outs, refs, [True, True, False, False], "prefill backward")
+
+
+@pytest.mark.timeout(600)
+def test_chunked_prompt_graph_replays_match_eager(layer):
+    """The prompt in 4 chunks of 2048 into the streaming cache (4/64/64/256),
+    window 256: every chunk's output and the whole cache (K/V rows, pos,
+    tok, state) after a replay equal the eager calls'. Before each replay
+    the outputs are poisoned, K/V zeroed and pos/tok/state set to garbage,
+    so the replay itself must write them (its reset restores pos/tok/state)."""
+    t = layer
+    cfg = t["cfg"]
+    sc = configs.STREAM_DECODE
+    B, Hq, Hkv, S, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.D
+    C, n = 2048, cfg.n
+    scale = 1.0 / math.sqrt(D)
+    spans = [(c0, c0 + C) for c0 in range(0, S, C)]
+    qc = [t["q"][:, :, c0:c1].contiguous() for c0, c1 in spans]
+    kc = [t["k"][:, :, c0:c1].contiguous() for c0, c1 in spans]
+    vc = [t["v"][:, :, c0:c1].contiguous() for c0, c1 in spans]
+    ic = [t["ids"][:, c0:c1].contiguous() for c0, c1 in spans]
+    cache = guarded_cache(B, Hkv, D, sc.a, sc.s, sc.p, sc.w)
+    ws = guarded_empty((chunk_workspace_bytes(cache, C),), torch.uint8)
+    outs = [guarded_empty((B, Hq, C, D), torch.bfloat16) for _ in spans]
+
+    def prompt():
+        cache.reset()
+        for j in range(len(spans)):
+            sep_attn_prefill_chunk(qc[j], kc[j], vc[j], ic[j], cache, t["sep"], n, scale, workspace=ws, out=outs[j])
+            sep_cache_update(cache, kc[j], vc[j], ic[j], t["sep"])
+
+    def scrub():
+        cache.k.zero_()
+        cache.v.zero_()
+        for m in (cache.pos, cache.tok, cache.state):
+            m.fill_(7)
+
+    scrub()
+    prompt()
+    torch.cuda.synchronize()
+    state = [cache.k, cache.v, cache.pos, cache.tok, cache.state]
+    refs_o = [o.clone() for o in outs]
+    refs_c = [m.clone() for m in state]
+    g = capture(prompt)
+    for i in range(REPLAYS):
+        scrub()
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (o, r) in enumerate(zip(outs, refs_o)):
+            assert torch.equal(o, r), f"chunked prompt: replay {i}, chunk {j} output differs"
+        for name, m, r in zip(("k", "v", "pos", "tok", "state"), state, refs_c):
+            assert torch.equal(m, r), f"chunked prompt: replay {i}, cache {name} differs"
+        print(f"[chunked prompt] replay {i} matches the eager calls", flush=True)
