@@ -683,6 +683,35 @@ def bench_batched(args, torch, sa, configs, gen):
     torch.cuda.synchronize()
     ms_steps = e0.elapsed_time(e1)
     assert int(cache.state[0, 0]) == H + cfg.steps
+    # the same 1024 steps replayed from HIP graphs of 256 steps, captured once
+    # on the cache the history leaves (re-ingested first): the step without
+    # the host's launch cost between steps. The final output and cache must
+    # equal the eager steps' bit for bit.
+    final = [out.clone()] + [m.clone() for m in (cache.k, cache.v, cache.pos, cache.tok, cache.state)]
+    cache.reset()
+    sa.sep_cache_update(cache, hk, hv, hist_ids, sep)
+    torch.cuda.synchronize()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(st)
+    graphs = []
+    with torch.cuda.stream(s_cap):
+        for g0 in range(0, cfg.steps, 256):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s_cap):
+                for j in range(g0, min(g0 + 256, cfg.steps)):
+                    sa.sep_decode_update(pq[j], pk[j], pv[j], step_ids[j], cache, sep, scale, out=out)
+            graphs.append(gr)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for gr in graphs:
+        gr.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_steps_graph = e0.elapsed_time(e1)
+    got = [out] + [cache.k, cache.v, cache.pos, cache.tok, cache.state]
+    assert all(torch.equal(a, b) for a, b in zip(got, final)), "batched steps: graph replay differs from eager"
+    del final, graphs
     # RoPE with position shifting (sep_attn_decode_rope) against the plain
     # decode, 32 steps each on the same final cache
     table = sa.sep_rope_table(500000.0, D, cache.slots + 1)
@@ -747,6 +776,7 @@ def bench_batched(args, torch, sa, configs, gen):
         del pc
     step_bytes = total_bytes / cfg.steps
     step_us = ms_steps * 1e3 / cfg.steps
+    step_graph_us = ms_steps_graph * 1e3 / cfg.steps
     dec_us = rope["plain"]["decode_us"]
     res = dict(
         entry="sep_decode_update",
@@ -757,12 +787,18 @@ def bench_batched(args, torch, sa, configs, gen):
         ingest_bytes=ingest_bytes,
         steps=cfg.steps, step_us=step_us, step_bytes=step_bytes,
         kv_GBps=step_bytes / (step_us * 1e-6) / 1e9,
+        step_graph_us=step_graph_us, kv_graph_GBps=step_bytes / (step_graph_us * 1e-6) / 1e9,
         decode_kernel_us=dec_us, decode_kernel_GBps=rope["plain"]["decode_GBps"], decode_bytes_per_launch=dec_f,
         roofline={
             "decode_update_step": roofline("sep_decode_update", "hbm", step_bytes / (step_us * 1e-6) / 1e9,
                                            PEAK_HBM_GBPS, "GB/s", step_us, traffic=None,
                                            algorithmic_bytes_per_launch=int(step_bytes),
                                            note="one step; the cache (~210 MB) fits the 256 MB MALL"),
+            "decode_update_step_graph": roofline("sep_decode_update", "hbm",
+                                                 step_bytes / (step_graph_us * 1e-6) / 1e9, PEAK_HBM_GBPS, "GB/s",
+                                                 step_graph_us, traffic=None,
+                                                 algorithmic_bytes_per_launch=int(step_bytes),
+                                                 note="the same steps replayed from graphs of 256 steps"),
             "decode": roofline("sep_attn_decode", "hbm", rope["plain"]["decode_GBps"], PEAK_HBM_GBPS, "GB/s",
                                dec_us, traffic=measured_traffic("sep_attn_decode_batched"),
                                algorithmic_bytes_per_launch=dec_f, note="back to back on the final cache"),
@@ -777,7 +813,8 @@ def bench_batched(args, torch, sa, configs, gen):
         })
     log(f"batched decode: ingest {ms_ingest:.3f} ms with the MALL flushed ({res['ingest_GBps']:.0f} GB/s; "
         f"{ms_ingest_warm:.3f} ms, {res['ingest_warm_GBps']:.0f} GB/s warm), "
-        f"step {step_us:.1f} us, KV {res['kv_GBps']:.0f} GB/s, decode kernel "
+        f"step {step_us:.1f} us, KV {res['kv_GBps']:.0f} GB/s ({step_graph_us:.1f} us, "
+        f"{res['kv_graph_GBps']:.0f} GB/s from graphs), decode kernel "
         f"{dec_us:.1f} us ({res['decode_kernel_GBps']:.0f} GB/s)")
     return res
 
