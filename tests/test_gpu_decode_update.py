@@ -40,6 +40,7 @@ CASES = [
     (1, 12, 3, 64, 0, 5, 3, 7, 0, 50, SEP_POLICY_NO_ACCUM, True),
     (2, 8, 1, 128, 1, 4, 6, 5, 10, 50, SEP_POLICY_DYNAMIC | SEP_POLICY_NO_ACCUM, False),
     (1, 4, 2, 128, 4, 0, 0, 12, 5, 40, 0, False),            # StreamingLLM mode
+    (8, 16, 8, 64, 4, 6, 5, 9, 30, 30, 0, False),            # B * Hkv = 64: the largest split
     (12, 16, 8, 64, 4, 6, 5, 9, 30, 30, 0, False),           # B * Hkv = 96: whole lists even with a work buffer
     (40, 16, 8, 64, 4, 6, 5, 9, 30, 30, 0, False),           # B * Hkv = 320: the two launches
 ]
