@@ -63,6 +63,7 @@ struct CacheArgs {
   int T;                     // tokens of this call
   int tstride;               // tokens per (sequence, head) row of k_new / ids_new
   int dynamic, accumulate;
+  int csplit;                // data_kernel: workgroups per (sequence, kv head), each a column range
 };
 
 struct PlanHead {
@@ -419,18 +420,25 @@ __device__ void plan(const CacheArgs& A, int b, const Set& S, PlanHead& ph, int3
 // runs once per 16 bytes but the column split is done once. kCopyUnroll
 // loads are in flight per thread before their stores. The functor maps
 // (row, head, k-or-v) to (src, dst) row pointers; no destination of one call
-// is a source of the same call.
+// is a source of the same call. With parts > 1 the call copies only column
+// range `part` of `parts` equal ones: workgroups that split a head's columns
+// between them never touch the same bytes.
 constexpr int kCopyUnroll = 8;
 
 template <class RowFn>
-__device__ __forceinline__ void copy_rows(int nrows, int g0, int g1, int row_bytes, RowFn fn) {
+__device__ __forceinline__ void copy_rows(int nrows, int g0, int g1, int row_bytes, RowFn fn, int part = 0,
+                                          int parts = 1) {
   const int cpr = row_bytes / 16;
-  const int W = (g1 - g0) * 2 * cpr;
+  const int Wall = (g1 - g0) * 2 * cpr;
+  const int clo = Wall * part / parts;
+  const int chi = Wall * (part + 1) / parts;
+  const int W = chi - clo;
   const int t = threadIdx.x;
+  if (W <= 0) return;
   const int R = W <= kUpdThreads ? kUpdThreads / W : 1;
   const int rbeg = W <= kUpdThreads ? t / W : 0;
   if (rbeg >= R) return;
-  for (int col = W <= kUpdThreads ? t % W : t; col < W; col += kUpdThreads) {
+  for (int col = clo + (W <= kUpdThreads ? t % W : t); col < chi; col += kUpdThreads) {
     const int chunk = col % cpr;
     const int kvg = col / cpr;
     const int kv = kvg & 1;
@@ -460,7 +468,7 @@ __device__ __forceinline__ void copy_rows(int nrows, int g0, int g1, int row_byt
 // recent-ring slots for positions >= cend1 (those below cend1 were compacted
 // away, and the ring holds at most rw positions).
 __device__ __forceinline__ void copy_new_rows(const CacheArgs& A, int b, int g0, int g1, int64_t t0,
-                                              int64_t t1, int64_t cend1) {
+                                              int64_t t1, int64_t cend1, int part = 0, int parts = 1) {
   const int rw = A.rw;
   const int row_bytes = A.D * A.esize;
   const int64_t cache_seq = static_cast<int64_t>(b) * A.Hkv;
@@ -477,7 +485,7 @@ __device__ __forceinline__ void copy_new_rows(const CacheArgs& A, int b, int g0,
     char* base_c = kv ? A.v : A.k;
     *src = base_new + ((cache_seq + g) * A.tstride + (y - t0)) * row_bytes;
     *dst = base_c + ((cache_seq + g) * A.c + dslot) * row_bytes;
-  });
+  }, part, parts);
 }
 
 enum { UPD_META = 1, UPD_FUSED = 2 };
@@ -696,7 +704,10 @@ __global__ void __launch_bounds__(kUpdThreads) update_kernel(CacheArgs A) {
   update_body<MODE, DYN>(A);
 }
 
-// K/V rows of a call with T > 1, grid (Hkv, B), one head per block; runs
+// K/V rows of a call with T > 1, grid (Hkv * csplit, B): block x copies
+// column range x % csplit of head x / csplit, in both steps below (the rows
+// step (2) overwrites are read by step (1) in the same columns only, so the
+// block's own barrier orders them); runs
 // after update_kernel<UPD_META> of the same call and plans nothing itself.
 // From the state META left it takes t1 (t0 = t1 - T), cend1 and cend0 (state
 // words 1 and 4). A separator-ring slot whose pos[] is >= cend0 was written
@@ -713,7 +724,9 @@ __global__ void __launch_bounds__(kUpdThreads) data_kernel(CacheArgs A) {
   const int lane = tid % kWave;
   const int wv = tid / kWave;
   const int b = blockIdx.y;
-  const int g = blockIdx.x;
+  const int parts = A.csplit;
+  const int g = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
   const int rw = A.rw;
   const int row_bytes = A.D * A.esize;
   const int64_t cache_seq = static_cast<int64_t>(b) * A.Hkv;
@@ -754,11 +767,11 @@ __global__ void __launch_bounds__(kUpdThreads) data_kernel(CacheArgs A) {
         *src = base_new + ((cache_seq + gg) * A.tstride + (x - t0)) * row_bytes;
       }
       *dst = base_c + (crow + A.a + j) * row_bytes;
-    });
+    }, part, parts);
     __syncthreads();
   }
   // (2) new tokens that stay
-  copy_new_rows(A, b, g, g + 1, t0, t1, cend1);
+  copy_new_rows(A, b, g, g + 1, t0, t1, cend1, part, parts);
 }
 
 __global__ void __launch_bounds__(kUpdThreads) reset_kernel(int32_t* pos, int32_t* tok, int64_t* state,
@@ -787,7 +800,13 @@ static hipError_t launch_update_chunk(const sep_cache& c, const CacheArgs& A, si
   hipLaunchKernelGGL((update_kernel<UPD_META, DYN>), dim3(1, c.B), dim3(kUpdThreads), dyn, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(data_kernel, dim3(c.Hkv, c.B), dim3(kUpdThreads), dyn, st, A);
+  // few (sequence, kv head) pairs: split each head's columns over several
+  // workgroups, so that each takes in less (up to 8 parts, 256 blocks)
+  CacheArgs D = A;
+  const int wall = 2 * (A.D * A.esize / 16);
+  D.csplit = 1;
+  while (c.B * c.Hkv * D.csplit < 256 && D.csplit < 8 && wall % (2 * D.csplit) == 0) D.csplit *= 2;
+  hipLaunchKernelGGL(data_kernel, dim3(c.Hkv * D.csplit, c.B), dim3(kUpdThreads), dyn, st, D);
   return hipGetLastError();
 }
 
@@ -812,6 +831,7 @@ static CacheArgs cache_args(const sep_cache& c, const int32_t* sep_ids, int n_se
   A.tstride = T;
   A.dynamic = (c.policy & SEP_POLICY_DYNAMIC) ? 1 : 0;
   A.accumulate = (c.policy & SEP_POLICY_NO_ACCUM) ? 0 : 1;
+  A.csplit = 1;
   return A;
 }
 
