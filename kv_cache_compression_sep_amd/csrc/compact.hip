@@ -73,9 +73,12 @@ __global__ void __launch_bounds__(kCompactThreads)
 }
 
 // sep_mask_compact: the flags of sep_mask_build and the compaction above in
-// one launch. Same walk as compact_kernel; each thread reads its 4 ids (one
-// 16-byte load when the rows allow it), tests them against the separator
-// set in LDS, writes the 4 flags and then their ranks as one 16-byte store.
+// one launch. The same walk with 8 ids per thread (chunks of 8192 ids, so
+// an 8192-token row is one chunk: one barrier): each thread reads its ids
+// with two 16-byte loads when the rows allow it, tests them against the
+// separator set in LDS, writes the 8 flags, then their ranks with 16-byte
+// stores; the per-thread counts (0..8) take four ballot bit planes.
+constexpr int kMcPer = 8;
 __global__ void __launch_bounds__(kCompactThreads)
     mask_compact_kernel(const int32_t* __restrict__ ids, int S, const int32_t* __restrict__ sep_ids, int n_sep,
                         uint8_t* __restrict__ is_sep, int32_t* __restrict__ rank,
@@ -89,40 +92,54 @@ __global__ void __launch_bounds__(kCompactThreads)
   uint8_t* f = is_sep + static_cast<int64_t>(b) * S;
   int32_t* rk = rank + static_cast<int64_t>(b) * (S + 1);
   int32_t* sp = sep_pos + static_cast<int64_t>(b) * S;
-  const bool vec = (S % 4) == 0;                  // rows of whole 16-byte groups (ids, rank)
+  const bool vec = (S % 4) == 0;                  // rows of whole 16-byte groups (ids) and 4-byte flag groups
+  const bool rvec = vec && ((static_cast<int64_t>(b) * (S + 1)) % 4) == 0;   // 16-byte aligned rank row
+  constexpr int kChunk = kMcPer * kCompactThreads;
   // the ids of each chunk are loaded one chunk ahead (the first ones while
   // the separator set is staged), so a load's latency overlaps the previous
   // chunk's work
   auto load4 = [&](int j0) -> int4 {
     return (vec && j0 + 4 <= S) ? *reinterpret_cast<const int4*>(id + j0) : make_int4(0, 0, 0, 0);
   };
-  int4 next = load4(4 * tid);
+  int4 nx0 = load4(kMcPer * tid), nx1 = load4(kMcPer * tid + 4);
   for (int i = tid; i < n_sep; i += kCompactThreads) set[i] = sep_ids[i];
   __syncthreads();
   int carry = 0;
   int parity = 0;
-  for (int base = 0; base < S; base += 4 * kCompactThreads, parity ^= 1) {
-    const int j0 = base + 4 * tid;
-    const int4 v = next;
-    if (base + 4 * kCompactThreads < S) next = load4(j0 + 4 * kCompactThreads);
-    int fl[4];
-    if (vec && j0 + 4 <= S) {
-      fl[0] = in_set(v.x, set, n_sep);
-      fl[1] = in_set(v.y, set, n_sep);
-      fl[2] = in_set(v.z, set, n_sep);
-      fl[3] = in_set(v.w, set, n_sep);
-      *reinterpret_cast<uchar4*>(f + j0) = make_uchar4(fl[0], fl[1], fl[2], fl[3]);
-    } else {
+  for (int base = 0; base < S; base += kChunk, parity ^= 1) {
+    const int j0 = base + kMcPer * tid;
+    const int4 v0 = nx0, v1 = nx1;
+    if (base + kChunk < S) {
+      nx0 = load4(j0 + kChunk);
+      nx1 = load4(j0 + kChunk + 4);
+    }
+    int fl[kMcPer];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fl[e] = (j0 + e < S) ? in_set(id[j0 + e], set, n_sep) : 0;
-        if (j0 + e < S) f[j0 + e] = static_cast<uint8_t>(fl[e]);
+    for (int h = 0; h < 2; ++h) {
+      const int4 v = h ? v1 : v0;
+      const int jh = j0 + 4 * h;
+      if (vec && jh + 4 <= S) {
+        fl[4 * h + 0] = in_set(v.x, set, n_sep);
+        fl[4 * h + 1] = in_set(v.y, set, n_sep);
+        fl[4 * h + 2] = in_set(v.z, set, n_sep);
+        fl[4 * h + 3] = in_set(v.w, set, n_sep);
+        *reinterpret_cast<uchar4*>(f + jh) =
+            make_uchar4(fl[4 * h], fl[4 * h + 1], fl[4 * h + 2], fl[4 * h + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = jh + e;
+          fl[4 * h + e] = (j < S) ? in_set(id[j], set, n_sep) : 0;
+          if (j < S) f[j] = static_cast<uint8_t>(fl[4 * h + e]);
+        }
       }
     }
-    const int c = fl[0] + fl[1] + fl[2] + fl[3];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kMcPer; ++e) c += fl[e];
     int pre = 0, tot = 0;
 #pragma unroll
-    for (int bit = 0; bit < 3; ++bit) {
+    for (int bit = 0; bit < 4; ++bit) {              // c <= 8: four bit planes
       const uint64_t m = ballot((c >> bit) & 1);
       pre += static_cast<int>(mbcnt(m)) << bit;
       tot += __popcll(m) << bit;
@@ -136,24 +153,27 @@ __global__ void __launch_bounds__(kCompactThreads)
       before += (w < wid) ? t : 0;
       chunk += t;
     }
-    const int r = carry + before + pre;
-    int rr[4];
-    rr[0] = r;
-    rr[1] = r + fl[0];
-    rr[2] = rr[1] + fl[1];
-    rr[3] = rr[2] + fl[2];
-    // rank rows start at b (S + 1): 16-byte aligned only when b (S + 1) % 4 == 0
-    if (vec && j0 + 4 <= S && ((static_cast<int64_t>(b) * (S + 1)) % 4) == 0) {
-      *reinterpret_cast<int4*>(rk + j0) = make_int4(rr[0], rr[1], rr[2], rr[3]);
-    } else {
+    int rr[kMcPer];
+    rr[0] = carry + before + pre;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j0 + e < S) rk[j0 + e] = rr[e];
+    for (int e = 1; e < kMcPer; ++e) rr[e] = rr[e - 1] + fl[e - 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jh = j0 + 4 * h;
+      if (rvec && jh + 4 <= S) {
+        *reinterpret_cast<int4*>(rk + jh) = make_int4(rr[4 * h], rr[4 * h + 1], rr[4 * h + 2], rr[4 * h + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (jh + e < S) rk[jh + e] = rr[4 * h + e];
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < kMcPer; ++e)
       if (j0 + e < S && fl[e]) sp[rr[e]] = j0 + e;
     carry += chunk;
+    // wave_tot is double-buffered by chunk parity, so the next chunk's
+    // writes cannot race with this chunk's reads.
   }
   for (int j = carry + tid; j < S; j += kCompactThreads) sp[j] = -1;
   if (tid == 0) {
